@@ -1,0 +1,212 @@
+"""Float64 CPU oracle of the Video Delta Attention (VDA) linear branch.
+
+TEST INFRASTRUCTURE.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import or run this module.  It shares
+no code with the HIP path (``frame_wise_delta_amd``) and imports nothing from
+it: it receives plain float64 arrays and returns plain float64 arrays.
+
+Source.  All formulas come from the summary page of the paper
+"Video DeltaNet: A Video-Native Hybrid Attention for Livestream Video
+Generation" (paper.rainbus.top, paper 2609.20744), cited below as [VDN] with
+the section heading of that page:
+
+* [VDN 前置知识, "Delta 规则"]      token delta rule with decayed state
+  S_bar_t = S_{t-1} Diag(alpha_t); state S in R^{d_v x d_k}, read as S q
+  ([VDN 前置知识, "线性注意力与递归记忆"]).
+* [VDN 核心方法 ¶2]                 frame-level joint objective
+  argmin_S 1/2 ||S - S_bar_t||_F^2 + sum_u beta_{t,u}/2 ||S k_{t,u} - v_{t,u}||^2
+  with closed form S_t = (S_bar_t + B_t)(I + A_t)^{-1}.
+* [VDN 方法步骤详情 step (3)]        A_t = K_t^T Diag(beta_t) K_t,
+  B_t = V_t^T Diag(beta_t) K_t.
+* [VDN 核心方法 ¶1]                 bidirectional 15-frame window aligned to
+  5-frame VAE chunks, first/last anchor frames, forward and reverse linear
+  scans summarise the history on each side of the window, the two readouts are
+  summed so nothing is counted twice; the text state S^T initialises both
+  scans.
+* [VDN 方法步骤详情 step (2)]        the linear branch drops the anchor rows.
+* [VDN 方法步骤详情 step (4)]        S^T initialises the two scans "by halves".
+* [VDN 方法步骤详情 step (5)]        window-boundary states are carried to the
+  query through the decay bridge prod(alpha_r).
+
+Readings of points the page leaves open (listed in the design doc as well):
+
+* S^T is one joint write of all text tokens into a zero state with no decay.
+* "By halves": each scan starts from ``text_init_scale * S^T`` (default 1/2)
+  so that the summed forward and reverse reads count the text once.
+* The bridge runs from the window edge to the query frame, inclusive:
+  forward b_f = prod_{r=ws}^{t} alpha_r, reverse b_r = prod_{r=t}^{we} alpha_r.
+* In the reverse scan alpha_t travels with frame t.
+* The window is clipped at the sequence ends; anchors are neither written nor
+  read by the linear branch (their output rows are zero).
+* With ``window = -1`` (no exclusion) the readout of frame t is S^f_t q where
+  S^f_t includes frame t's own write.
+
+Everything is float64; matrix products and linear solves are NumPy/LAPACK
+calls used as single steps.  No blocking, chunk composition or reordering.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+# ------------------------------------------------------------------ maps --
+
+def index_maps(frames: int, chunk: int, window: int, anchors: int):
+    """Chunk and window index maps, by brute-force set enumeration
+    [VDN 核心方法 ¶1; 前置知识 "VAE 潜空间帧与时间 chunk"].
+
+    Returns ``(rows, frame_chunk)``:
+      rows        int32 [C, 7]: (c, lo, hi, ws, we, F, R) where lo..hi are the
+                  window chunks of query chunk c (own chunk +- ``window``,
+                  clipped), ws..we the first/last window frame, F the number
+                  of chunks wholly before ws (index of the forward state the
+                  readout uses) and R the number of chunks wholly after we
+                  (index of the reverse state).
+      frame_chunk int32 [T]: chunk of each frame, -1 for anchors.
+    ``window < 0`` (no exclusion) gives the rows of ``window = 0``.
+    """
+    a = 1 if anchors else 0
+    scanned = list(range(a, frames - a))
+    groups = [scanned[i:i + chunk] for i in range(0, len(scanned), chunk)]
+    C = len(groups)
+    w = max(window, 0)
+    frame_chunk = np.full(frames, -1, dtype=np.int32)
+    for c, g in enumerate(groups):
+        for f in g:
+            frame_chunk[f] = c
+    rows = np.zeros((C, 7), dtype=np.int32)
+    for c in range(C):
+        wchunks = [x for x in range(C) if abs(x - c) <= w]
+        wframes = set()
+        for x in wchunks:
+            wframes.update(groups[x])
+        ws, we = min(wframes), max(wframes)
+        F = sum(1 for g in groups if all(f < ws for f in g))
+        R = sum(1 for g in groups if all(f > we for f in g))
+        rows[c] = (c, min(wchunks), max(wchunks), ws, we, F, R)
+    return rows, frame_chunk
+
+
+# -------------------------------------------------------- frame update ----
+
+def frame_stats(K: np.ndarray, V: np.ndarray, beta: np.ndarray):
+    """A = K^T Diag(beta) K (d_k x d_k), B = V^T Diag(beta) K (d_v x d_k)
+    [VDN 方法步骤详情 step (3)].  K [U, d_k], V [U, d_v], beta [U]."""
+    BK = beta[:, None] * K
+    return K.T @ BK, V.T @ BK
+
+
+def frame_update(S_prev: np.ndarray, K: np.ndarray, V: np.ndarray,
+                 beta: np.ndarray, alpha: np.ndarray) -> np.ndarray:
+    """One frame write: S_bar = S_prev Diag(alpha) [VDN 前置知识 "Delta 规则"],
+    S = (S_bar + B)(I + A)^{-1} [VDN 核心方法 ¶2], computed as the solution of
+    S (I + A) = S_bar + B (I + A is symmetric, so S^T = (I+A)^{-1}(S_bar+B)^T)."""
+    A, B = frame_stats(K, V, beta)
+    S_bar = S_prev * alpha[None, :]
+    G = np.eye(A.shape[0]) + A
+    return np.linalg.solve(G, (S_bar + B).T).T
+
+
+def text_state(Kt: np.ndarray, Vt: np.ndarray, bt: np.ndarray, d_v: int, d_k: int) -> np.ndarray:
+    """S^T: all text tokens written jointly into a zero state with no decay
+    (reading of [VDN 核心方法 ¶1] "文本状态 S^T")."""
+    if Kt.shape[0] == 0:
+        return np.zeros((d_v, d_k))
+    return frame_update(np.zeros((d_v, d_k)), Kt, Vt, bt, np.ones(d_k))
+
+
+# ---------------------------------------------------------------- scans --
+
+def scan(order, K, V, beta, alpha, S0, record_every: int):
+    """Apply ``frame_update`` over the frames in ``order`` starting from S0;
+    return the states after 0, r, 2r, ... frames (r = ``record_every``) and
+    after the last frame.  [VDN 核心方法 ¶1, 方法步骤详情 step (4)]"""
+    S = S0.copy()
+    states = [S.copy()]
+    for i, t in enumerate(order):
+        S = frame_update(S, K[t], V[t], beta[t], alpha[t])
+        if (i + 1) % record_every == 0 or i + 1 == len(order):
+            states.append(S.copy())
+    return np.stack(states)
+
+
+def scanned_frames(frames: int, anchors: int):
+    a = 1 if anchors else 0
+    return list(range(a, frames - a))
+
+
+# -------------------------------------------------------------- readout --
+
+def readout_windowed(Q, alpha, states_f, states_r, rows, frame_chunk, bridge=True):
+    """Window-excluding bidirectional readout [VDN 核心方法 ¶1, 方法步骤详情
+    step (5)]: for a scanned frame t of chunk c, token u,
+        o = S^f_{F(c)} (b_f * q) + S^r_{R(c)} (b_r * q),
+    b_f = prod_{r=ws}^{t} alpha_r, b_r = prod_{r=t}^{we} alpha_r (ones when
+    ``bridge`` is False).  Anchor rows are zero."""
+    T, U, d_k = Q.shape
+    d_v = states_f.shape[1]
+    O = np.zeros((T, U, d_v))
+    for t in range(T):
+        c = frame_chunk[t]
+        if c < 0:
+            continue
+        _, lo, hi, ws, we, F, R = rows[c]
+        if bridge:
+            bf = np.prod(alpha[ws:t + 1], axis=0)
+            br = np.prod(alpha[t:we + 1], axis=0)
+        else:
+            bf = np.ones(d_k)
+            br = np.ones(d_k)
+        O[t] = (Q[t] * bf[None, :]) @ states_f[F].T + (Q[t] * br[None, :]) @ states_r[R].T
+    return O
+
+
+def readout_full(Q, states_f, frame_chunk, anchors):
+    """No window exclusion: o_t = S^f_t q with S^f_t after frame t's write."""
+    T, U, d_k = Q.shape
+    d_v = states_f.shape[1]
+    O = np.zeros((T, U, d_v))
+    a = 1 if anchors else 0
+    for t in range(T):
+        if frame_chunk[t] < 0:
+            continue
+        O[t] = Q[t] @ states_f[t - a + 1].T
+    return O
+
+
+# ------------------------------------------------------------------ run --
+
+def run_head(frames, chunk, window, anchors, q, k, v, beta, alpha,
+             kt=None, vt=None, bt=None, text_init_scale=0.5, bridge=True,
+             with_output=True):
+    """Whole linear branch for one head.  Arrays are float64:
+    q, k, v [T, U, d]; beta [T, U]; alpha [T, d]; kt, vt [N_text, d]; bt
+    [N_text].  Returns a dict with the maps, S^T, forward/reverse recorded
+    states and the output O [T, U, d_v]."""
+    T, U, d = k.shape
+    rows, frame_chunk = index_maps(frames, chunk, window, anchors)
+    order = scanned_frames(frames, anchors)
+    if kt is None or len(kt) == 0:
+        ST = np.zeros((d, d))
+    else:
+        ST = text_state(kt, vt, bt, d, d)
+    S0 = text_init_scale * ST
+    every = chunk if window >= 0 else 1
+    states_f = scan(order, k, v, beta, alpha, S0, every)
+    states_r = scan(order[::-1], k, v, beta, alpha, S0, every)
+    out = dict(rows=rows, frame_chunk=frame_chunk, S_text=ST,
+               states_f=states_f, states_r=states_r)
+    if with_output:
+        if window >= 0:
+            out["O"] = readout_windowed(q, alpha, states_f, states_r, rows, frame_chunk, bridge)
+        else:
+            out["O"] = readout_full(q, states_f, frame_chunk, anchors)
+    return out
+
+
+def rel_l2(x, ref) -> float:
+    """||x - ref||_2 / ||ref||_2 in float64."""
+    x = np.asarray(x, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    den = np.linalg.norm(ref.ravel())
+    return float(np.linalg.norm((x - ref).ravel()) / (den if den > 0 else 1.0))

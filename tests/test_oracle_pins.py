@@ -1,0 +1,363 @@
+"""Pins of the float64 oracle against facts fixed by the Video DeltaNet summary
+page and by the mathematics, independent of the oracle's own formulas.
+
+Each pin is chosen so that a plausible slip in the oracle (a dropped term,
+decay on the wrong side, a transposed cross term, a wrong bridge range, a
+window off by one chunk) fails at least one of them.  CPU only.
+"""
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+from oracle import vda_oracle as orc
+from frame_wise_delta_amd import inputs as inp
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _unit(g, shape):
+    x = g.standard_normal(shape)
+    return x / np.linalg.norm(x, axis=-1, keepdims=True)
+
+
+def _frame(g, U, d):
+    K = _unit(g, (U, d))
+    V = g.standard_normal((U, d))
+    beta = 1 / (1 + np.exp(-g.standard_normal(U)))
+    alpha = 0.9 + 0.1 * g.random(d)
+    S_prev = g.standard_normal((d, d))
+    return S_prev, K, V, beta, alpha
+
+
+def _objective_grad(S, S_bar, K, V, beta):
+    """Gradient of 1/2||S - S_bar||^2 + sum_u beta_u/2 ||S k_u - v_u||^2,
+    written token by token from the joint objective (核心方法 para 2)."""
+    g = S - S_bar
+    for u in range(K.shape[0]):
+        g = g + beta[u] * np.outer(S @ K[u] - V[u], K[u])
+    return g
+
+
+# ------------------------------------------------ frame update (a1 + a2) --
+
+@pytest.mark.parametrize("U,d", [(1, 4), (7, 5), (40, 16), (300, 64)])
+def test_closed_form_is_stationary_point_of_objective(U, d):
+    """The oracle's S_t zeroes the gradient of the joint objective, i.e. it
+    satisfies the normal equations S_t(I + A_t) = S_bar_t + B_t."""
+    g = np.random.default_rng([1, U, d])
+    S_prev, K, V, beta, alpha = _frame(g, U, d)
+    S = orc.frame_update(S_prev, K, V, beta, alpha)
+    S_bar = S_prev * alpha[None, :]
+    grad = _objective_grad(S, S_bar, K, V, beta)
+    assert np.abs(grad).max() <= 1e-12 * max(1.0, np.abs(S).max())
+
+
+def test_gradient_descent_reaches_the_same_minimiser():
+    """Brute-force minimisation of the joint objective on tiny inputs."""
+    for seed in range(5):
+        g = np.random.default_rng([2, seed])
+        d, U = 3 + seed, 5 + 3 * seed
+        S_prev, K, V, beta, alpha = _frame(g, U, d)
+        S_bar = S_prev * alpha[None, :]
+        # step 1/L with L >= lambda_max of the Hessian (trace bound)
+        step = 1.0 / (1.0 + float(np.sum(beta * np.sum(K * K, axis=1))))
+        S = S_bar.copy()
+        for _ in range(200000):
+            grad = _objective_grad(S, S_bar, K, V, beta)
+            if np.abs(grad).max() < 1e-13:
+                break
+            S = S - step * grad
+        ref = orc.frame_update(S_prev, K, V, beta, alpha)
+        assert np.abs(S - ref).max() <= 1e-10
+
+
+def test_single_token_equals_implicit_delta_step():
+    """U = 1: the frame write is the implicit token delta step
+    S_bar + beta (v - S_bar k) k^T / (1 + beta ||k||^2)  (Delta 规则)."""
+    g = np.random.default_rng(3)
+    for d in (2, 8, 64):
+        S_prev = g.standard_normal((d, d))
+        k = g.standard_normal(d)          # not normalised on purpose
+        v = g.standard_normal(d)
+        beta = float(g.random()) * 3
+        alpha = 0.5 + 0.5 * g.random(d)
+        S_bar = S_prev * alpha[None, :]
+        expect = S_bar + beta * np.outer(v - S_bar @ k, k) / (1 + beta * k @ k)
+        got = orc.frame_update(S_prev, k[None], v[None], np.array([beta]), alpha)
+        assert np.abs(got - expect).max() <= 1e-13 * max(1, np.abs(expect).max())
+
+
+def test_correlation_awareness_saturation():
+    """Repeated key U times -> read weight U beta/(1 + U beta); orthonormal
+    keys -> beta/(1 + beta) each (技术新颖性, appendix A.2 summary)."""
+    g = np.random.default_rng(4)
+    d, U, beta = 16, 9, 0.37
+    k = _unit(g, (d,))
+    v = g.standard_normal(d)
+    K = np.tile(k, (U, 1))
+    V = np.tile(v, (U, 1))
+    S = orc.frame_update(np.zeros((d, d)), K, V, np.full(U, beta), np.ones(d))
+    assert np.abs(S @ k - U * beta / (1 + U * beta) * v).max() <= 1e-14
+    # with a non-zero decayed state: S k = (S_bar k + U beta v)/(1 + U beta)
+    S_prev = g.standard_normal((d, d))
+    alpha = 0.9 + 0.1 * g.random(d)
+    S = orc.frame_update(S_prev, K, V, np.full(U, beta), alpha)
+    S_bar = S_prev * alpha[None, :]
+    assert np.abs(S @ k - (S_bar @ k + U * beta * v) / (1 + U * beta)).max() <= 1e-13
+    # orthonormal keys
+    Qm, _ = np.linalg.qr(g.standard_normal((d, d)))
+    Ko = Qm.T[:6]
+    Vo = g.standard_normal((6, d))
+    S = orc.frame_update(np.zeros((d, d)), Ko, Vo, np.full(6, beta), np.ones(d))
+    for u in range(6):
+        assert np.abs(S @ Ko[u] - beta / (1 + beta) * Vo[u]).max() <= 1e-14
+
+
+def test_exact_rational_two_by_two():
+    """d = 2, U = 2 with rational data, solved exactly (Cramer's rule on the
+    normal equations in exact fractions) against the float64 oracle."""
+    F = Fraction
+    K = [[F(1, 2), F(1, 3)], [F(-1, 4), F(2, 3)]]
+    V = [[F(3, 2), F(-1)], [F(1, 5), F(2)]]
+    beta = [F(1, 2), F(3, 4)]
+    alpha = [F(9, 10), F(4, 5)]
+    S_prev = [[F(1), F(-2)], [F(1, 2), F(3)]]
+    S_bar = [[S_prev[i][j] * alpha[j] for j in range(2)] for i in range(2)]
+    G = [[(1 if i == j else 0) + sum(beta[u] * K[u][i] * K[u][j] for u in range(2))
+          for j in range(2)] for i in range(2)]
+    Y = [[S_bar[i][j] + sum(beta[u] * V[u][i] * K[u][j] for u in range(2))
+          for j in range(2)] for i in range(2)]
+    det = G[0][0] * G[1][1] - G[0][1] * G[1][0]
+    Ginv = [[G[1][1] / det, -G[0][1] / det], [-G[1][0] / det, G[0][0] / det]]
+    S_exact = [[sum(Y[i][m] * Ginv[m][j] for m in range(2)) for j in range(2)] for i in range(2)]
+    f = lambda M: np.array([[float(x) for x in r] for r in M])
+    got = orc.frame_update(f(S_prev), f(K), f(V), np.array([float(b) for b in beta]),
+                           np.array([float(a) for a in alpha]))
+    assert np.abs(got - f(S_exact)).max() <= 2e-15
+
+
+def test_transition_is_non_expansive():
+    """Proposition 1: ||S_bar (I + A)^{-1}||_2 <= ||S_bar||_2 and
+    ||Diag(alpha)(I + A)^{-1}||_2 <= 1 without commutation (核心方法 para 2,
+    技术新颖性).  Counter-check: the batched additive transition I - A of
+    SANA-WM expands when lambda_max(A) > 2 (核心方法 para 2)."""
+    g = np.random.default_rng(5)
+    for trial in range(40):
+        d, U = (16, 16) if trial < 20 else (8, 64)
+        S_prev, K, V, beta, alpha = _frame(g, U, d)
+        S_bar = S_prev * alpha[None, :]
+        # V = 0 isolates the inherited-state transition S_bar -> S_bar N
+        S = orc.frame_update(S_prev, K, np.zeros_like(V), beta, alpha)
+        assert np.linalg.norm(S, 2) <= np.linalg.norm(S_bar, 2) * (1 + 1e-12)
+        # M = Diag(alpha) N is the image of S_prev = I
+        M = orc.frame_update(np.eye(d), K, np.zeros_like(V), beta, alpha)
+        assert np.linalg.norm(M, 2) <= 1 + 1e-12
+    # SANA-WM comparator: many aligned tokens make lambda_max(A) > 2
+    k = _unit(g, (8,))
+    K = np.tile(k, (10, 1))
+    A = K.T @ (0.5 * K)
+    assert np.linalg.eigvalsh(A).max() > 2
+    assert np.linalg.norm(np.eye(8) - A, 2) > 1
+    M = orc.frame_update(np.eye(8), K, np.zeros_like(K), np.full(10, 0.5), np.ones(8))
+    assert np.linalg.norm(M, 2) <= 1 + 1e-12
+
+
+# ----------------------------------------------------------------- scans --
+
+def _small_cfg_inputs(seed=6, T=17, U=12, d=8, anchors=1, nt=5):
+    g = np.random.default_rng(seed)
+    q = _unit(g, (T, U, d))
+    k = _unit(g, (T, U, d))
+    v = g.standard_normal((T, U, d))
+    beta = 1 / (1 + np.exp(-g.standard_normal((T, U))))
+    alpha = 0.9 + 0.1 * g.random((T, d))
+    kt = _unit(g, (nt, d))
+    vt = g.standard_normal((nt, d))
+    bt = 1 / (1 + np.exp(-g.standard_normal(nt)))
+    return q, k, v, beta, alpha, kt, vt, bt
+
+
+def test_reverse_scan_equals_forward_scan_on_reversed_time():
+    q, k, v, beta, alpha, kt, vt, bt = _small_cfg_inputs()
+    T = k.shape[0]
+    r = orc.run_head(T, 5, 1, 1, q, k, v, beta, alpha, kt, vt, bt)
+    rr = orc.run_head(T, 5, 1, 1, q[::-1], k[::-1], v[::-1], beta[::-1], alpha[::-1], kt, vt, bt)
+    assert np.array_equal(r["states_r"], rr["states_f"])
+    assert np.array_equal(r["states_f"], rr["states_r"])
+
+
+def test_no_writes_gives_pure_decay():
+    """beta = 0: S = S_0 Diag(prod alpha); alpha = 1 too: S = S_0."""
+    g = np.random.default_rng(7)
+    T, U, d = 12, 6, 5
+    k = _unit(g, (T, U, d))
+    v = g.standard_normal((T, U, d))
+    alpha = 0.8 + 0.2 * g.random((T, d))
+    S0 = g.standard_normal((d, d))
+    order = list(range(1, T - 1))
+    st = orc.scan(order, k, v, np.zeros((T, U)), alpha, S0, 1)
+    for i in range(len(order) + 1):
+        decay = np.ones(d)
+        for t in order[:i]:
+            decay = decay * alpha[t]
+        assert np.abs(st[i] - S0 * decay[None, :]).max() <= 1e-14
+    st = orc.scan(order, k, v, np.zeros((T, U)), np.ones((T, d)), S0, 1)
+    assert np.array_equal(st[-1], S0)
+
+
+def test_scan_records_every_chunk_boundary():
+    q, k, v, beta, alpha, *_ = _small_cfg_inputs(T=22)
+    order = list(range(1, 21))
+    per_frame = orc.scan(order, k, v, beta, alpha, np.zeros((8, 8)), 1)
+    per_chunk = orc.scan(order, k, v, beta, alpha, np.zeros((8, 8)), 5)
+    assert np.array_equal(per_chunk, per_frame[::5])
+
+
+# ---------------------------------------------------------------- maps ----
+
+def _closed_form_rows(T, P, w, anchors):
+    a = 1 if anchors else 0
+    n = T - 2 * a
+    C = -(-n // P)
+    w = max(w, 0)
+    rows = []
+    for c in range(C):
+        lo, hi = max(0, c - w), min(C - 1, c + w)
+        ws = a + P * lo
+        we = min(a + P * (hi + 1) - 1, a + n - 1)
+        rows.append((c, lo, hi, ws, we, lo, C - 1 - hi))
+    return np.array(rows, dtype=np.int32)
+
+
+def test_maps_match_hand_derived_tiny_table():
+    rows, fc = orc.index_maps(22, 5, 1, 1)
+    table, fcg = [], None
+    with open(os.path.join(GOLDEN, "tiny_maps.txt")) as f:
+        for line in f:
+            if line.startswith("#") or not line.strip():
+                continue
+            if line.startswith("frame_chunk"):
+                fcg = np.array([int(x) for x in line.split()[1:]], dtype=np.int32)
+            else:
+                table.append([int(x) for x in line.split()])
+    assert np.array_equal(rows, np.array(table, dtype=np.int32))
+    assert np.array_equal(fc, fcg)
+
+
+@pytest.mark.parametrize("cfg", inp.CONFIGS, ids=lambda c: c.name)
+def test_maps_closed_form_and_partition(cfg):
+    _check_maps(cfg.frames, cfg.chunk, cfg.window, cfg.anchors)
+
+
+def test_maps_random_shapes():
+    g = np.random.default_rng(8)
+    for _ in range(200):
+        P = int(g.integers(1, 8))
+        n = int(g.integers(1, 12)) * P
+        anchors = int(g.integers(0, 2))
+        w = int(g.integers(0, 4))
+        _check_maps(n + 2 * anchors, P, w, anchors)
+
+
+def _check_maps(T, P, w, anchors):
+    rows, fc = orc.index_maps(T, P, w, anchors)
+    assert np.array_equal(rows, _closed_form_rows(T, P, w, anchors))
+    a = 1 if anchors else 0
+    scanned = set(range(a, T - a))
+    C = len(rows)
+    for c, lo, hi, ws, we, F, R in rows:
+        fwd = {f for f in scanned if fc[f] < F}
+        win = set(range(ws, we + 1))
+        rev = {f for f in scanned if fc[f] >= C - R}
+        # forward frames, window and reverse frames partition the scanned frames
+        assert fwd | win | rev == scanned
+        assert not (fwd & win) and not (win & rev) and not (fwd & rev)
+        # the query chunk lies inside its window and the window spans 2w+1
+        # chunks unless clipped at an end
+        own = {f for f in scanned if fc[f] == c}
+        assert own <= win
+        if w >= 0 and P * (2 * w + 1) <= len(scanned):
+            assert len(win) == P * (hi - lo + 1)
+
+
+def test_h3_maps_sample_rows():
+    rows, _ = orc.index_maps(102, 5, 1, 1)
+    assert tuple(rows[0][3:]) == (1, 10, 0, 18)
+    assert tuple(rows[10][3:]) == (46, 60, 9, 8)
+    assert tuple(rows[19][3:]) == (91, 100, 18, 0)
+    # 15-frame window for interior chunks (核心方法 para 1)
+    assert all(r[4] - r[3] + 1 == 15 for r in rows[1:-1])
+
+
+# ------------------------------------------------------------- readout ----
+
+def test_text_is_counted_once_when_video_writes_nothing():
+    """beta = 0, alpha = 1 in the video: both reads see 1/2 S^T, so the output
+    is exactly S^T q (nothing counted twice, 核心方法 para 1)."""
+    q, k, v, beta, alpha, kt, vt, bt = _small_cfg_inputs(T=22)
+    r = orc.run_head(22, 5, 1, 1, q, k, v, np.zeros_like(beta), np.ones_like(alpha), kt, vt, bt)
+    ST = r["S_text"]
+    for t in range(1, 21):
+        assert np.abs(r["O"][t] - q[t] @ ST.T).max() <= 1e-14
+    assert not r["O"][0].any() and not r["O"][21].any()
+
+
+def test_bridge_continues_the_decay_through_the_window():
+    """With beta = 0 everywhere in the video the scans only decay.  The bridged
+    windowed read of frame t must then equal the read of the decay-only
+    states carried all the way to t from both ends (bridge inclusive of t)."""
+    q, k, v, beta, alpha, kt, vt, bt = _small_cfg_inputs(T=22, seed=9)
+    r = orc.run_head(22, 5, 1, 1, q, k, v, np.zeros_like(beta), alpha, kt, vt, bt)
+    S0 = 0.5 * r["S_text"]
+    for t in range(1, 21):
+        df = np.prod(alpha[1:t + 1], axis=0)
+        dr = np.prod(alpha[t:21], axis=0)
+        expect = q[t] @ (S0 * df[None, :]).T + q[t] @ (S0 * dr[None, :]).T
+        assert np.abs(r["O"][t] - expect).max() <= 1e-14
+
+
+def test_text_state_satisfies_its_normal_equations():
+    q, k, v, beta, alpha, kt, vt, bt = _small_cfg_inputs(nt=30)
+    ST = orc.text_state(kt, vt, bt, 8, 8)
+    grad = _objective_grad(ST, np.zeros((8, 8)), kt, vt, bt)
+    assert np.abs(grad).max() <= 1e-12
+
+
+def test_full_forward_readout_uses_state_after_own_write():
+    q, k, v, beta, alpha, *_ = _small_cfg_inputs(T=9, anchors=0)
+    r = orc.run_head(9, 5, -1, 0, q, k, v, beta, alpha)
+    S = np.zeros((8, 8))
+    for t in range(9):
+        S = orc.frame_update(S, k[t], v[t], beta[t], alpha[t])
+        assert np.abs(r["O"][t] - q[t] @ S.T).max() <= 1e-14
+
+
+def test_readout_is_linear_in_q():
+    q, k, v, beta, alpha, kt, vt, bt = _small_cfg_inputs(T=22, seed=10)
+    q2 = np.random.default_rng(11).standard_normal(q.shape)
+    o1 = orc.run_head(22, 5, 1, 1, q, k, v, beta, alpha, kt, vt, bt)["O"]
+    o2 = orc.run_head(22, 5, 1, 1, q2, k, v, beta, alpha, kt, vt, bt)["O"]
+    o3 = orc.run_head(22, 5, 1, 1, q + 2 * q2, k, v, beta, alpha, kt, vt, bt)["O"]
+    assert np.abs(o3 - (o1 + 2 * o2)).max() <= 1e-12
+
+
+# -------------------------------------------------------------- inputs ----
+
+def test_bf16_rounding_is_nearest_even():
+    x = np.array([1.0, 1.0 + 2**-8, 1.0 + 3 * 2**-8, -2.5, 1e-3, 3.0e5], dtype=np.float32)
+    b = inp.bf16_bits_to_f32(inp.f32_to_bf16_bits(x))
+    assert b[0] == 1.0 and b[1] == 1.0 and b[2] == 1.0 + 4 * 2**-8 and b[3] == -2.5
+    assert abs(b[4] - 1e-3) <= 1e-3 * 2**-8
+    assert abs(b[5] - 3.0e5) <= 3.0e5 * 2**-8
+
+
+def test_inputs_are_deterministic_per_head():
+    cfg = inp.CONFIG_BY_NAME["tiny"]
+    a = inp.head_inputs(cfg, 0)
+    b = inp.head_inputs(cfg, 0)
+    assert np.array_equal(a.k, b.k) and np.array_equal(a.alpha, b.alpha)
+    k = a.f64("k")
+    assert np.allclose(np.linalg.norm(k, axis=-1), 1.0, atol=1e-6)
+    assert ((a.alpha >= 0.9) & (a.alpha < 1.0)).all()
