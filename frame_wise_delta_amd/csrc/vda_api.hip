@@ -1,0 +1,308 @@
+// libvda C ABI: argument validation, index maps, workspace sizing and
+// kernel launches.  All validation happens on the host before anything is
+// enqueued, so it is testable without a GPU.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <mutex>
+
+#include "vda.h"
+#include "vda_common.h"
+#include "vda_kernels.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_last_error[0] = '\0';
+  return VDA_OK;
+}
+
+struct Shape {
+  int H, T, U, d, P, a, n, C, w, Nt, n_eff, count;
+};
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Host-side validation of a descriptor; fills the derived sizes.
+int check_desc(const vda_desc* desc, Shape* s) {
+  if (!desc) return fail(VDA_ERR_NULL, "desc is NULL");
+  const vda_desc& q = *desc;
+  if (q.heads < 0) return fail(VDA_ERR_SHAPE, "heads = %d < 0", q.heads);
+  if (q.tokens < 0) return fail(VDA_ERR_SHAPE, "tokens = %d < 0", q.tokens);
+  if (q.d_k != q.d_v) return fail(VDA_ERR_SHAPE, "d_k (%d) != d_v (%d)", q.d_k, q.d_v);
+  if (q.d_k != 16 && q.d_k != 32 && q.d_k != 64 && q.d_k != 128)
+    return fail(VDA_ERR_SHAPE, "d = %d is not one of 16, 32, 64, 128", q.d_k);
+  if (q.chunk < 1) return fail(VDA_ERR_SHAPE, "chunk = %d < 1", q.chunk);
+  if (q.anchors != 0 && q.anchors != 1) return fail(VDA_ERR_SHAPE, "anchors = %d (0 or 1)", q.anchors);
+  if (q.frames < 2 * q.anchors || q.frames < 0)
+    return fail(VDA_ERR_SHAPE, "frames = %d < 2 * anchors", q.frames);
+  if (q.window < -1) return fail(VDA_ERR_SHAPE, "window = %d < -1", q.window);
+  if (q.text_tokens < 0) return fail(VDA_ERR_SHAPE, "text_tokens = %d < 0", q.text_tokens);
+  if (q.in_dtype != VDA_F32 && q.in_dtype != VDA_BF16)
+    return fail(VDA_ERR_DTYPE, "in_dtype = %d (VDA_F32 or VDA_BF16)", q.in_dtype);
+  if (q.out_dtype != VDA_F32 && q.out_dtype != VDA_BF16 && q.out_dtype != VDA_F16)
+    return fail(VDA_ERR_DTYPE, "out_dtype = %d (VDA_F32, VDA_BF16 or VDA_F16)", q.out_dtype);
+  if (!(q.text_init_scale == q.text_init_scale)) return fail(VDA_ERR_SHAPE, "text_init_scale is NaN");
+  if (q.flags & ~(uint32_t)VDA_NO_BRIDGE) return fail(VDA_ERR_SHAPE, "unknown flags 0x%x", q.flags);
+  s->H = q.heads;
+  s->T = q.frames;
+  s->U = q.tokens;
+  s->d = q.d_k;
+  s->P = q.chunk;
+  s->a = q.anchors;
+  s->n = q.frames - 2 * q.anchors;
+  s->C = (s->n + s->P - 1) / s->P;
+  s->w = q.window;
+  s->Nt = q.text_tokens;
+  s->n_eff = s->n + (s->Nt > 0 ? 1 : 0);
+  if (s->w >= 0 && s->n % s->P != 0)
+    return fail(VDA_ERR_SHAPE, "windowed readout needs n %% chunk == 0 (n = %d, chunk = %d)", s->n, s->P);
+  s->count = (s->w >= 0 ? s->C : s->n) + 1;
+  // 64-bit sizes must not overflow and grids must fit
+  const double elems = (double)s->H * s->T * (double)s->U * s->d;
+  if (elems > 9.0e15) return fail(VDA_ERR_SHAPE, "tensor too large");
+  if ((double)s->H * s->n_eff > 2.0e9 || (double)s->H * s->T > 2.0e9) return fail(VDA_ERR_SHAPE, "grid too large");
+  return VDA_OK;
+}
+
+size_t ws_bytes(const Shape& s) {
+  return vda::kWsHeader + (size_t)s.H * s.n_eff * vda::ws_slot_floats(s.d) * sizeof(float);
+}
+
+// One-time check per device that it is a gfx950 GPU.
+int check_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(VDA_ERR_DEVICE, "no HIP device available");
+  static std::mutex mu;
+  static int known[64];  // 0 unknown, 1 ok, -1 bad
+  if (dev < 0 || dev >= 64) return fail(VDA_ERR_DEVICE, "device index %d out of range", dev);
+  std::lock_guard<std::mutex> lock(mu);
+  if (known[dev] == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return fail(VDA_ERR_DEVICE, "hipGetDeviceProperties failed");
+    known[dev] = (strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : -1;
+    if (known[dev] < 0) return fail(VDA_ERR_DEVICE, "device %d is %s, libvda needs gfx950", dev, prop.gcnArchName);
+  }
+  if (known[dev] < 0) return fail(VDA_ERR_DEVICE, "device %d is not gfx950", dev);
+  return VDA_OK;
+}
+
+int launch_status() {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(VDA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* vda_status_string(int code) {
+  switch (code) {
+    case VDA_OK: return "ok";
+    case VDA_ERR_NULL: return "null pointer";
+    case VDA_ERR_SHAPE: return "invalid shape";
+    case VDA_ERR_DTYPE: return "unsupported dtype";
+    case VDA_ERR_ALIGN: return "misaligned pointer";
+    case VDA_ERR_WORKSPACE: return "workspace too small";
+    case VDA_ERR_HIP: return "HIP error";
+    case VDA_ERR_DEVICE: return "no usable gfx950 device";
+    default: return "unknown status";
+  }
+}
+
+const char* vda_last_error(void) { return g_last_error; }
+
+int vda_workspace_bytes(const vda_desc* desc, size_t* bytes) {
+  Shape s;
+  int rc = check_desc(desc, &s);
+  if (rc) return rc;
+  if (!bytes) return fail(VDA_ERR_NULL, "bytes is NULL");
+  *bytes = ws_bytes(s);
+  return ok();
+}
+
+int vda_state_count(const vda_desc* desc, int32_t* count) {
+  Shape s;
+  int rc = check_desc(desc, &s);
+  if (rc) return rc;
+  if (!count) return fail(VDA_ERR_NULL, "count is NULL");
+  *count = s.count;
+  return ok();
+}
+
+int vda_index_map(const vda_desc* desc, int32_t* chunk_rows, int32_t* frame_chunk) {
+  Shape s;
+  int rc = check_desc(desc, &s);
+  if (rc) return rc;
+  const int w = s.w < 0 ? 0 : s.w;
+  if (chunk_rows) {
+    for (int c = 0; c < s.C; ++c) {
+      const int lo = c - w > 0 ? c - w : 0;
+      const int hi = c + w < s.C - 1 ? c + w : s.C - 1;
+      int we = s.a + s.P * (hi + 1) - 1;
+      if (we > s.a + s.n - 1) we = s.a + s.n - 1;  // ragged last chunk
+      int32_t* r = chunk_rows + 7 * (size_t)c;
+      r[0] = c;
+      r[1] = lo;
+      r[2] = hi;
+      r[3] = s.a + s.P * lo;
+      r[4] = we;
+      r[5] = lo;
+      r[6] = s.C - 1 - hi;
+    }
+  }
+  if (frame_chunk) {
+    for (int t = 0; t < s.T; ++t) {
+      const int f = t - s.a;
+      frame_chunk[t] = (f >= 0 && f < s.n) ? f / s.P : -1;
+    }
+  }
+  return ok();
+}
+
+int vda_prepare_frames(const vda_desc* desc, const void* k, const void* v, const float* beta,
+                       const void* k_text, const void* v_text, const float* beta_text, void* ws,
+                       size_t ws_size, void* stream) {
+  Shape s;
+  int rc = check_desc(desc, &s);
+  if (rc) return rc;
+  const bool need_video = (size_t)s.H * s.n * s.U > 0;
+  if (need_video && (!k || !v || !beta)) return fail(VDA_ERR_NULL, "k, v or beta is NULL");
+  if (s.Nt > 0 && s.H > 0 && (!k_text || !v_text || !beta_text))
+    return fail(VDA_ERR_NULL, "k_text, v_text or beta_text is NULL with text_tokens = %d", s.Nt);
+  if (!ws) return fail(VDA_ERR_NULL, "ws is NULL");
+  if (ws_size < ws_bytes(s)) return fail(VDA_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_size, ws_bytes(s));
+  if (!aligned16(k) || !aligned16(v) || !aligned16(beta) || !aligned16(k_text) || !aligned16(v_text) ||
+      !aligned16(beta_text) || ((uintptr_t)ws & 255u))
+    return fail(VDA_ERR_ALIGN, "k, v, beta, k_text, v_text, beta_text need 16-byte and ws 256-byte alignment");
+  rc = check_device();
+  if (rc) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  vda::PrepArgs a;
+  a.k = k;
+  a.v = v;
+  a.beta = beta;
+  a.kt = k_text;
+  a.vt = v_text;
+  a.bt = beta_text;
+  a.status = static_cast<int*>(ws);
+  a.frames = reinterpret_cast<float*>(static_cast<char*>(ws) + vda::kWsHeader);
+  a.H = s.H;
+  a.T = s.T;
+  a.U = s.U;
+  a.a = s.a;
+  a.n = s.n;
+  a.n_eff = s.n_eff;
+  a.Nt = s.Nt;
+  vda::launch_clear_status(a.status, st);
+  vda::launch_prepare(a, s.d, desc->in_dtype == VDA_F32, st);
+  return launch_status();
+}
+
+static int scan_common(const vda_desc* desc, const void* ws, const float* alpha, const float* s_init,
+                       float* states, void* stream, int reverse) {
+  Shape s;
+  int rc = check_desc(desc, &s);
+  if (rc) return rc;
+  if (!ws) return fail(VDA_ERR_NULL, "ws is NULL");
+  if (!states) return fail(VDA_ERR_NULL, "states is NULL");
+  if (s.H * (size_t)s.n > 0 && !alpha) return fail(VDA_ERR_NULL, "alpha is NULL");
+  if (!aligned16(alpha) || !aligned16(s_init) || !aligned16(states) || ((uintptr_t)ws & 255u))
+    return fail(VDA_ERR_ALIGN, "alpha, s_init, states need 16-byte and ws 256-byte alignment");
+  rc = check_device();
+  if (rc) return rc;
+  vda::ScanArgs a;
+  a.frames = reinterpret_cast<const float*>(static_cast<const char*>(ws) + vda::kWsHeader);
+  a.alpha = alpha;
+  a.s_init = s_init;
+  a.states = states;
+  a.H = s.H;
+  a.T = s.T;
+  a.a = s.a;
+  a.n = s.n;
+  a.n_eff = s.n_eff;
+  a.count = s.count;
+  a.every = s.w >= 0 ? s.P : 1;
+  a.reverse = reverse;
+  a.use_text = s.Nt > 0;
+  a.scale = desc->text_init_scale;
+  vda::launch_scan(a, s.d, static_cast<hipStream_t>(stream));
+  return launch_status();
+}
+
+int vda_scan_fwd(const vda_desc* desc, const void* ws, const float* alpha, const float* s_init, float* states,
+                 void* stream) {
+  return scan_common(desc, ws, alpha, s_init, states, stream, 0);
+}
+
+int vda_scan_rev(const vda_desc* desc, const void* ws, const float* alpha, const float* s_init, float* states,
+                 void* stream) {
+  return scan_common(desc, ws, alpha, s_init, states, stream, 1);
+}
+
+int vda_readout(const vda_desc* desc, const void* q, const float* alpha, const float* states_fwd,
+                const float* states_rev, void* out, void* stream) {
+  Shape s;
+  int rc = check_desc(desc, &s);
+  if (rc) return rc;
+  const bool any = (size_t)s.H * s.T * s.U > 0;
+  if (any && !out) return fail(VDA_ERR_NULL, "out is NULL");
+  if (any && s.n > 0) {
+    if (!q || !states_fwd) return fail(VDA_ERR_NULL, "q or states_fwd is NULL");
+    if (!alpha && s.w >= 0) return fail(VDA_ERR_NULL, "alpha is NULL");
+    if (s.w >= 0 && !states_rev) return fail(VDA_ERR_NULL, "states_rev is NULL with window >= 0");
+  }
+  if (!aligned16(q) || !aligned16(alpha) || !aligned16(states_fwd) || !aligned16(states_rev) || !aligned16(out))
+    return fail(VDA_ERR_ALIGN, "q, alpha, states, out need 16-byte alignment");
+  rc = check_device();
+  if (rc) return rc;
+  if (!any) return ok();
+  vda::ReadArgs a;
+  a.q = q;
+  a.alpha = alpha;
+  a.sf = states_fwd;
+  a.sr = states_rev;
+  a.out = out;
+  a.H = s.H;
+  a.T = s.T;
+  a.U = s.U;
+  a.a = s.a;
+  a.n = s.n;
+  a.P = s.P;
+  a.C = s.C;
+  a.w = s.w;
+  a.count = s.count;
+  a.bridge = (desc->flags & VDA_NO_BRIDGE) ? 0 : 1;
+  vda::launch_readout(a, s.d, desc->in_dtype, desc->out_dtype, static_cast<hipStream_t>(stream));
+  return launch_status();
+}
+
+int vda_device_status(const vda_desc* desc, const void* ws, void* stream, int32_t* flags) {
+  Shape s;
+  int rc = check_desc(desc, &s);
+  if (rc) return rc;
+  if (!ws || !flags) return fail(VDA_ERR_NULL, "ws or flags is NULL");
+  rc = check_device();
+  if (rc) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (hipStreamSynchronize(st) != hipSuccess) return fail(VDA_ERR_HIP, "hipStreamSynchronize failed");
+  int32_t v = 0;
+  if (hipMemcpy(&v, ws, sizeof(v), hipMemcpyDeviceToHost) != hipSuccess)
+    return fail(VDA_ERR_HIP, "reading the status word failed");
+  *flags = v;
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,47 @@
+// Kernel argument blocks and launchers (internal to libvda).
+#pragma once
+
+#include "vda_common.h"
+
+namespace vda {
+
+struct PrepArgs {
+  const void* k;
+  const void* v;
+  const float* beta;
+  const void* kt;
+  const void* vt;
+  const float* bt;
+  float* frames;  // workspace after the header: [H][n_eff][N | B]
+  int* status;
+  int H, T, U, a, n, n_eff, Nt;
+};
+
+struct ScanArgs {
+  const float* frames;  // workspace frames: [H][n_eff][N | B]
+  const float* alpha;   // [H][T][d]
+  const float* s_init;  // [H][d][d] or nullptr
+  float* states;        // [H][count][d][d]
+  int H, T, a, n, n_eff, count;
+  int every;            // record the state after every `every` frames
+  int reverse;
+  int use_text;         // S_init = S^T from the text slot (slot n) when s_init == nullptr
+  float scale;
+};
+
+struct ReadArgs {
+  const void* q;          // [H][T][U][d]
+  const float* alpha;     // [H][T][d]
+  const float* sf;        // [H][count][d][d]
+  const float* sr;        // [H][count][d][d] or nullptr (full mode)
+  void* out;              // [H][T][U][d]
+  int H, T, U, a, n, P, C, w, count;
+  int bridge;
+};
+
+int launch_prepare(const PrepArgs& a, int d, bool in_f32, hipStream_t stream);
+void launch_clear_status(int* status, hipStream_t stream);
+int launch_scan(const ScanArgs& a, int d, hipStream_t stream);
+int launch_readout(const ReadArgs& a, int d, int in_dtype, int out_dtype, hipStream_t stream);
+
+}  // namespace vda

@@ -1,0 +1,237 @@
+// Window-excluding bidirectional readout.
+//
+// For a scanned frame t of chunk c ("Video DeltaNet: A Video-Native Hybrid
+// Attention for Livestream Video Generation", core-method section,
+// paragraph 1, and method-steps section, step (5)):
+//
+//   O_t = Q_t W_t^T,   W_t = S^f_{F(c)} Diag(b_f) + S^r_{R(c)} Diag(b_r),
+//   b_f = prod_{r=ws}^{t} alpha_r,   b_r = prod_{r=t}^{we} alpha_r,
+//
+// i.e. the forward state that ends before the softmax window and the reverse
+// state that starts after it, each carried to frame t through the decay of
+// the excluded frames.  The two reads are merged into one d x d operand W_t
+// per frame, so the token GEMM runs once.  With no window exclusion the
+// readout is O_t = Q_t (S^f_t)^T.  Anchor frames get zero rows.
+//
+// One workgroup per (head, frame).  Wavefront w owns value-channel tiles
+// w, w+4, ... and keeps its rows of W_t in registers as bf16 hi/lo pairs;
+// 64-token tiles of Q are staged in LDS with one coalesced pass and each
+// wavefront computes O^T = W Q^T on MFMA (2 products per tile for bf16 Q,
+// 3 for float32 Q split hi/lo), accumulating in float32.
+#include "vda_common.h"
+#include "vda_kernels.h"
+
+namespace vda {
+
+namespace {
+
+constexpr int kQT = 64;  // tokens per LDS tile
+
+template <int OUT>
+struct OutT;
+template <>
+struct OutT<VDA_F32> {
+  static __device__ __forceinline__ void store4(void* base, size_t idx, f32x4 v) {
+    *reinterpret_cast<float4*>(static_cast<float*>(base) + idx) = make_float4(v[0], v[1], v[2], v[3]);
+  }
+  static constexpr int bytes = 4;
+};
+template <>
+struct OutT<VDA_BF16> {
+  static __device__ __forceinline__ void store4(void* base, size_t idx, f32x4 v) {
+    uint2 p;
+    p.x = f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16);
+    p.y = f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16);
+    *reinterpret_cast<uint2*>(static_cast<u16*>(base) + idx) = p;
+  }
+  static constexpr int bytes = 2;
+};
+template <>
+struct OutT<VDA_F16> {
+  static __device__ __forceinline__ void store4(void* base, size_t idx, f32x4 v) {
+    typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+    h4 p = {(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
+    *reinterpret_cast<h4*>(static_cast<_Float16*>(base) + idx) = p;
+  }
+  static constexpr int bytes = 2;
+};
+
+// Q operand (eight consecutive channels of one token) from the LDS tile.
+template <class TIN>
+struct QFrag;
+template <>
+struct QFrag<InBF16> {
+  bf16x8 hi;
+  __device__ __forceinline__ void load(const char* row, int k0, bool in) {
+    if (in) {
+      hi = *reinterpret_cast<const bf16x8*>(row + 2 * k0);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) hi[e] = bits_to_bf16(0);
+    }
+  }
+};
+template <>
+struct QFrag<InF32> {
+  bf16x8 hi, lo;
+  __device__ __forceinline__ void load(const char* row, int k0, bool in) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float x = in ? reinterpret_cast<const float*>(row)[k0 + e] : 0.f;
+      __bf16 h, l;
+      split_bf16(x, h, l);
+      hi[e] = h;
+      lo[e] = l;
+    }
+  }
+};
+
+}  // namespace
+
+template <int D, class TIN, int OUT>
+__global__ __launch_bounds__(kThreads, 2) void readout_kernel(ReadArgs a) {
+  using T = typename TIN::T;
+  constexpr int VT = D / 16;                         // value-channel tiles
+  constexpr int NVT = (VT + 3) / 4;                  // tiles per wavefront
+  constexpr int KS = D / 32 > 0 ? D / 32 : 1;        // MFMA k-steps
+  constexpr int PITCH = D * TIN::bytes + 16;         // LDS bytes per token row
+  __shared__ __attribute__((aligned(16))) char sQ[kQT * PITCH];
+  __shared__ float sBf[D], sBr[D];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lr = lane & 15, lg = lane >> 4;
+  const int h = blockIdx.x / a.T;
+  const int t = blockIdx.x - h * a.T;
+  const size_t frame_off = ((size_t)h * a.T + t) * (size_t)a.U * D;
+
+  if (t < a.a || t >= a.T - a.a) {  // anchor frame: zero rows
+    constexpr int per16 = 16 / OutT<OUT>::bytes;
+    const size_t n16 = (size_t)a.U * D / per16;
+    uint4* o = reinterpret_cast<uint4*>(static_cast<char*>(a.out) + frame_off * OutT<OUT>::bytes);
+    for (size_t i = tid; i < n16; i += kThreads) o[i] = make_uint4(0, 0, 0, 0);
+    return;
+  }
+
+  // ---- states and bridges for this frame
+  const int f = t - a.a;
+  const float* sf;
+  const float* sr = nullptr;
+  const float* alpha_h = a.alpha + (size_t)h * a.T * D;
+  if (a.w >= 0) {
+    const int c = f / a.P;
+    const int lo = c - a.w > 0 ? c - a.w : 0;
+    const int hi = c + a.w < a.C - 1 ? c + a.w : a.C - 1;
+    const int ws = a.a + a.P * lo;
+    const int we = a.a + a.P * (hi + 1) - 1;
+    sf = a.sf + ((size_t)h * a.count + lo) * D * D;
+    sr = a.sr + ((size_t)h * a.count + (a.C - 1 - hi)) * D * D;
+    for (int k = tid; k < D; k += kThreads) {
+      float bf = 1.f, br = 1.f;
+      if (a.bridge) {
+        for (int r = ws; r <= t; ++r) bf *= alpha_h[(size_t)r * D + k];
+        for (int r = t; r <= we; ++r) br *= alpha_h[(size_t)r * D + k];
+      }
+      sBf[k] = bf;
+      sBr[k] = br;
+    }
+  } else {
+    sf = a.sf + ((size_t)h * a.count + f + 1) * D * D;
+    for (int k = tid; k < D; k += kThreads) {
+      sBf[k] = 1.f;
+      sBr[k] = 0.f;
+    }
+  }
+  __syncthreads();
+
+  // ---- W rows of this wavefront's value tiles, bf16 hi/lo, A-operand layout
+  bf16x8 wh[NVT][KS], wl[NVT][KS];
+#pragma unroll
+  for (int i = 0; i < NVT; ++i) {
+    const int vt = wave + 4 * i;
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+      const int k0 = 32 * kk + 8 * lg;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float x = 0.f;
+        if (vt < VT && k0 + e < D) {
+          const size_t idx = (size_t)(16 * vt + lr) * D + k0 + e;
+          x = sf[idx] * sBf[k0 + e];
+          if (sr) x = fmaf(sr[idx], sBr[k0 + e], x);
+        }
+        __bf16 hh, ll;
+        split_bf16(x, hh, ll);
+        wh[i][kk][e] = hh;
+        wl[i][kk][e] = ll;
+      }
+    }
+  }
+
+  // ---- token tiles
+  const T* qh = static_cast<const T*>(a.q) + frame_off;
+  constexpr int CH = D * TIN::bytes / 16;  // 16-byte chunks per token row
+  for (int u0 = 0; u0 < a.U; u0 += kQT) {
+    for (int i = tid; i < kQT * CH; i += kThreads) {
+      const int r = i / CH, ch = i - r * CH;
+      uint4 val = make_uint4(0, 0, 0, 0);
+      if (u0 + r < a.U)
+        val = reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(qh + (size_t)(u0 + r) * D))[ch];
+      *reinterpret_cast<uint4*>(sQ + r * PITCH + 16 * ch) = val;
+    }
+    __syncthreads();
+    if (wave < VT) {
+#pragma unroll
+      for (int st = 0; st < kQT / 16; ++st) {
+        const int ul = 16 * st + lr;  // token of this lane's operand column
+        f32x4 acc[NVT];
+#pragma unroll
+        for (int i = 0; i < NVT; ++i) acc[i] = f32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) {
+          const int k0 = 32 * kk + 8 * lg;
+          QFrag<TIN> qf;
+          qf.load(sQ + ul * PITCH, k0, k0 < D);
+#pragma unroll
+          for (int i = 0; i < NVT; ++i) {
+            if (wave + 4 * i < VT) {
+              acc[i] = mfma_bf16(wh[i][kk], qf.hi, acc[i]);
+              acc[i] = mfma_bf16(wl[i][kk], qf.hi, acc[i]);
+              if constexpr (TIN::bytes == 4) acc[i] = mfma_bf16(wh[i][kk], qf.lo, acc[i]);
+            }
+          }
+        }
+        const int u = u0 + ul;
+        if (u < a.U) {
+#pragma unroll
+          for (int i = 0; i < NVT; ++i) {
+            const int vt = wave + 4 * i;
+            if (vt < VT) OutT<OUT>::store4(a.out, frame_off + (size_t)u * D + 16 * vt + 4 * lg, acc[i]);
+          }
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
+int launch_readout(const ReadArgs& a, int d, int in_dtype, int out_dtype, hipStream_t stream) {
+  if (a.H == 0 || a.T == 0) return 0;
+  dim3 grid((unsigned)(a.H * a.T)), block(kThreads);
+#define VDA_RD3(DD, TI, OO) \
+  if (out_dtype == OO) { hipLaunchKernelGGL((readout_kernel<DD, TI, OO>), grid, block, 0, stream, a); return 0; }
+#define VDA_RD(DD)                                                                 \
+  if (d == DD) {                                                                   \
+    if (in_dtype == VDA_F32) {                                                     \
+      VDA_RD3(DD, InF32, VDA_F32) VDA_RD3(DD, InF32, VDA_BF16) VDA_RD3(DD, InF32, VDA_F16) \
+    } else {                                                                       \
+      VDA_RD3(DD, InBF16, VDA_F32) VDA_RD3(DD, InBF16, VDA_BF16) VDA_RD3(DD, InBF16, VDA_F16) \
+    }                                                                              \
+    return -1;                                                                     \
+  }
+  VDA_RD(16) VDA_RD(32) VDA_RD(64) VDA_RD(128)
+#undef VDA_RD
+#undef VDA_RD3
+  return -1;
+}
+
+}  // namespace vda

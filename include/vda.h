@@ -1,0 +1,172 @@
+/*
+ * libvda — Video Delta Attention (VDA) linear branch on AMD MI355X (gfx950).
+ *
+ * The operation is defined on the summary page of the paper "Video DeltaNet:
+ * A Video-Native Hybrid Attention for Livestream Video Generation"
+ * (paper.rainbus.top, paper 2609.20744), cited as [VDN <section>]:
+ *
+ *   frame statistics   A_t = K_t^T Diag(beta_t) K_t,  B_t = V_t^T Diag(beta_t) K_t
+ *                      [VDN 方法步骤详情 step (3)]
+ *   frame write        S_t = (S_{t-1} Diag(alpha_t) + B_t)(I + A_t)^{-1}
+ *                      [VDN 核心方法 para 2; 前置知识 "Delta 规则"]
+ *   bidirectional scan forward and reverse over the non-anchor frames, both
+ *                      started from text_init_scale * S^T
+ *                      [VDN 核心方法 para 1; 方法步骤详情 step (4)]
+ *   readout            o = S^f_{F(c)} (b_f * q) + S^r_{R(c)} (b_r * q), which
+ *                      excludes the chunk-aligned softmax window and carries
+ *                      each state to the query frame through the decay bridge
+ *                      prod alpha_r [VDN 核心方法 para 1; 方法步骤详情 step (5)]
+ *
+ * Notation: H heads, T frames (anchors included), U tokens per frame,
+ * d = d_k = d_v, P frames per chunk, n = T - 2*anchors scanned frames,
+ * C = ceil(n / P) chunks.  The state S is d_v x d_k (row = value channel,
+ * column = key channel) and is read as S q.
+ *
+ * Conventions (all entry points):
+ *  - Layouts are dense row-major: q/k/v/out [H][T][U][d], beta [H][T][U]
+ *    float32, alpha [H][T][d] float32, k_text/v_text [H][N_text][d],
+ *    beta_text [H][N_text] float32, states [H][count][d][d] float32.
+ *  - Every array pointer is a device pointer (hipMalloc'd or equivalent),
+ *    16-byte aligned.  The caller owns every buffer; the library allocates no
+ *    device memory and keeps no pointer after a call returns.
+ *  - Calls that take `stream` only enqueue work on that hipStream_t (NULL =
+ *    the null stream) and return without synchronising.  Buffers must stay
+ *    alive until the caller synchronises the stream.
+ *  - Every argument is validated on the host before anything is enqueued; a
+ *    failed validation returns a negative code, launches nothing and leaves
+ *    the message in vda_last_error() (thread-local).  No exception or abort
+ *    crosses the ABI.
+ *  - Numerical faults found on the device (a non-finite statistic or a
+ *    non-positive pivot in the factorisation) set bits in a status word in
+ *    the workspace; vda_device_status() reads it.
+ */
+#ifndef VDA_H
+#define VDA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* return codes */
+enum {
+  VDA_OK = 0,
+  VDA_ERR_NULL = -1,      /* a required pointer is NULL */
+  VDA_ERR_SHAPE = -2,     /* inconsistent or unsupported sizes */
+  VDA_ERR_DTYPE = -3,     /* unsupported element type */
+  VDA_ERR_ALIGN = -4,     /* a pointer is not 16-byte aligned */
+  VDA_ERR_WORKSPACE = -5, /* workspace too small */
+  VDA_ERR_HIP = -6,       /* a HIP runtime call or kernel launch failed */
+  VDA_ERR_DEVICE = -7     /* no usable gfx950 device */
+};
+
+/* element types */
+enum { VDA_F32 = 0, VDA_BF16 = 1, VDA_F16 = 2 };
+
+/* vda_desc.flags */
+enum {
+  VDA_NO_BRIDGE = 1u << 0 /* readout without the decay bridge (b_f = b_r = 1) */
+};
+
+/* bits of the device status word */
+enum {
+  VDA_DEV_NONFINITE = 1, /* a frame statistic or factor was NaN/Inf */
+  VDA_DEV_PIVOT = 2      /* I + A_t had a pivot <= 0 (not positive definite) */
+};
+
+typedef struct vda_desc {
+  int32_t heads;       /* H >= 0 */
+  int32_t frames;      /* T >= 2*anchors */
+  int32_t tokens;      /* U >= 0 tokens per frame */
+  int32_t d_k, d_v;    /* d_k == d_v, one of 16, 32, 64, 128 */
+  int32_t chunk;       /* P >= 1 frames per chunk (5 for the VAE chunks) */
+  int32_t anchors;     /* 1: frames 0 and T-1 are anchors; 0: none */
+  int32_t window;      /* w >= 0: the softmax window of query chunk c is chunks
+                          c-w..c+w clipped to [0, C-1] and n % P must be 0;
+                          -1: no exclusion, the readout of frame t is S^f_t q
+                          with S^f_t the forward state after frame t */
+  int32_t text_tokens; /* N_text >= 0 text tokens forming S^T (0: S^T = 0) */
+  int32_t in_dtype;    /* q, k, v, k_text, v_text: VDA_F32 or VDA_BF16 */
+  int32_t out_dtype;   /* out: VDA_F32, VDA_BF16 or VDA_F16 */
+  float text_init_scale; /* both scans start from text_init_scale * S^T;
+                            1/2 reads the page's "initialised by halves" */
+  uint32_t flags;      /* VDA_NO_BRIDGE */
+} vda_desc;
+
+/* Bytes of device workspace vda_prepare_frames needs for `desc` (host only,
+ * enqueues nothing).  The workspace carries, per head, the factor
+ * (I + A_t)^{-1} and B_t of every scanned frame and of the text "frame", plus
+ * the device status word, from vda_prepare_frames to the scans. */
+int vda_workspace_bytes(const vda_desc* desc, size_t* bytes);
+
+/* Number of states each scan records per head (host only):
+ * C + 1 when window >= 0 (the state after 0, 1, ..., C chunks),
+ * n + 1 when window == -1 (the state after 0, 1, ..., n frames). */
+int vda_state_count(const vda_desc* desc, int32_t* count);
+
+/* Integer index maps (host only, host pointers) [VDN 核心方法 para 1]:
+ *  chunk_rows [C][7] int32: (c, lo, hi, ws, we, F, R) — window chunks lo..hi
+ *    = c-w..c+w clipped (w = 0 when window == -1), first/last window frame
+ *    ws/we, F = lo (forward state index: chunks wholly before the window),
+ *    R = C-1-hi (reverse state index: chunks wholly after the window);
+ *  frame_chunk [T] int32: chunk of each frame, -1 for anchors.
+ * Either pointer may be NULL to skip that output. */
+int vda_index_map(const vda_desc* desc, int32_t* chunk_rows, int32_t* frame_chunk);
+
+/* Frame statistics and factorisation [VDN 方法步骤详情 step (3)]: for every
+ * head and every scanned frame t (and the text tokens when text_tokens > 0)
+ * computes A_t and B_t over the frame's U tokens, factorises I + A_t and
+ * stores N_t = (I + A_t)^{-1} and B_t in `ws`.  Also clears the device status
+ * word.
+ *  k, v        [H][T][U][d] in_dtype (anchor frames are not read)
+ *  beta        [H][T][U] float32
+ *  k_text, v_text [H][N_text][d] in_dtype; beta_text [H][N_text] float32
+ *              (all three may be NULL when text_tokens == 0)
+ *  ws          device workspace of ws_bytes >= vda_workspace_bytes(desc). */
+int vda_prepare_frames(const vda_desc* desc, const void* k, const void* v, const float* beta,
+                       const void* k_text, const void* v_text, const float* beta_text,
+                       void* ws, size_t ws_bytes, void* stream);
+
+/* Forward scan [VDN 核心方法 para 1; 方法步骤详情 step (4)]: starting from
+ * S_0 = text_init_scale * S_init, applies S_t = (S_{t-1} Diag(alpha_t) + B_t) N_t
+ * over the scanned frames in increasing order and records vda_state_count()
+ * states per head into `states` [H][count][d][d] float32 (states[h][0] = S_0).
+ *  S_init = s_init [H][d][d] float32 when s_init != NULL, else S^T built from
+ *  the text tokens in ws (zero when text_tokens == 0).
+ *  ws must hold the output of vda_prepare_frames for the same desc. */
+int vda_scan_fwd(const vda_desc* desc, const void* ws, const float* alpha, const float* s_init,
+                 float* states, void* stream);
+
+/* Reverse scan: the same recurrence over the scanned frames in decreasing
+ * order, each frame with its own alpha_t; states[h][j] is the state after the
+ * last j chunks (or frames when window == -1). */
+int vda_scan_rev(const vda_desc* desc, const void* ws, const float* alpha, const float* s_init,
+                 float* states, void* stream);
+
+/* Readout [VDN 核心方法 para 1; 方法步骤详情 step (5)].  window >= 0: for a
+ * scanned frame t of chunk c and each token,
+ *   o = states_fwd[F(c)] (b_f * q) + states_rev[R(c)] (b_r * q),
+ *   b_f = prod_{r=ws}^{t} alpha_r,  b_r = prod_{r=t}^{we} alpha_r
+ * (b = 1 with VDA_NO_BRIDGE).  window == -1: o = states_fwd[t-anchors+1] q and
+ * states_rev may be NULL.  Anchor frames get zero rows.
+ *  q [H][T][U][d] in_dtype; out [H][T][U][d] out_dtype (every element written). */
+int vda_readout(const vda_desc* desc, const void* q, const float* alpha, const float* states_fwd,
+                const float* states_rev, void* out, void* stream);
+
+/* Synchronises `stream`, then copies the device status word of `ws` into
+ * *flags (VDA_DEV_* bits; 0 = no fault).  For tests and diagnostics. */
+int vda_device_status(const vda_desc* desc, const void* ws, void* stream, int32_t* flags);
+
+/* Static description of a return code. */
+const char* vda_status_string(int code);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char* vda_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VDA_H */

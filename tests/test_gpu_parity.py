@@ -1,0 +1,207 @@
+"""GPU parity of the libvda HIP path against the float64 oracle, at sizes the
+oracle finishes in seconds (several MFMA tiles, ragged token tails, every
+supported head size), plus the path's edge cases.  All calls go through the
+C ABI."""
+import numpy as np
+import pytest
+
+from frame_wise_delta_amd import inputs as inp
+from frame_wise_delta_amd import runner, vda
+from oracle import vda_oracle as orc
+
+pytestmark = pytest.mark.gpu
+
+TOL_O = 2e-3       # output, relative L2 (bf16 inputs, float32 state)
+TOL_STATE = 1e-3   # recorded states and workspace factors, relative L2
+
+
+def _oracle(cfg, h_in, bridge=True, scale=0.5):
+    f = h_in.f64
+    text = cfg.text_tokens > 0
+    return orc.run_head(cfg.frames, cfg.chunk, cfg.window, cfg.anchors, f("q"), f("k"), f("v"),
+                        f("beta"), f("alpha"), f("kt") if text else None, f("vt") if text else None,
+                        f("bt") if text else None, text_init_scale=scale, bridge=bridge)
+
+
+def _scanned_rel(O, ref, cfg):
+    a = cfg.anchors
+    sl = slice(a, cfg.frames - a)
+    return orc.rel_l2(O[sl], ref[sl])
+
+
+def _check(cfg, heads=None, tol_o=TOL_O, bridge=True, **over):
+    print(f"[parity] {cfg.name} H={cfg.heads} T={cfg.frames} U={cfg.tokens} d={cfg.d} {over}", flush=True)
+    heads_in = inp.all_heads(cfg)
+    desc, dev, bufs = runner.run(cfg, heads_in, bridge=bridge, **over)
+    O = runner.out_f64(bufs)
+    sf = bufs.states_f.cpu().numpy()
+    sr = bufs.states_r.cpu().numpy()
+    assert vda.vda_device_status(desc, bufs.ws) == 0
+    worst = 0.0
+    for h in (range(cfg.heads) if heads is None else heads):
+        ref = _oracle(cfg, heads_in[h], bridge=bridge)
+        r_o = _scanned_rel(O[h], ref["O"], cfg)
+        r_f = orc.rel_l2(sf[h], ref["states_f"])
+        r_r = orc.rel_l2(sr[h], ref["states_r"])
+        print(f"  head {h}: O {r_o:.3e}  states_f {r_f:.3e}  states_r {r_r:.3e}", flush=True)
+        assert r_o <= tol_o
+        assert r_f <= TOL_STATE and r_r <= TOL_STATE
+        # anchors are exactly zero
+        if cfg.anchors:
+            assert not O[h, 0].any() and not O[h, -1].any()
+        worst = max(worst, r_o)
+    return desc, bufs, heads_in, worst
+
+
+def _ws_frames(bufs, desc):
+    d = desc.d_k
+    n = desc.frames - 2 * desc.anchors
+    n_eff = n + (1 if desc.text_tokens else 0)
+    raw = bufs.ws.cpu().numpy()[256:256 + desc.heads * n_eff * 2 * d * d * 4]
+    return raw.view(np.float32).reshape(desc.heads, n_eff, 2, d, d).astype(np.float64)
+
+
+def test_tiny_config():
+    cfg = inp.CONFIG_BY_NAME["tiny"]
+    desc, bufs, heads_in, _ = _check(cfg)
+    # stage check: N_t = (I + A_t)^-1 and B_t in the workspace
+    fr = _ws_frames(bufs, desc)
+    h = heads_in[0]
+    for f in range(cfg.scanned):
+        t = cfg.anchors + f
+        A, B = orc.frame_stats(h.f64("k")[t], h.f64("v")[t], h.f64("beta")[t])
+        N = np.linalg.inv(np.eye(cfg.d) + A)
+        assert orc.rel_l2(fr[0, f, 0], N) <= 1e-4
+        assert orc.rel_l2(fr[0, f, 1], B) <= 1e-3
+
+
+def test_scan_only_config():
+    _check(inp.CONFIG_BY_NAME["scan_only"])
+
+
+def test_h3_shape_reduced_frames():
+    """H3 frame shape (U = 1008, d = 128, 512 text tokens), 2 heads, 4 chunks."""
+    cfg = inp.scaled(inp.CONFIG_BY_NAME["h3"], heads=2, frames=22)
+    desc, bufs, heads_in, _ = _check(cfg)
+    fr = _ws_frames(bufs, desc)
+    h = heads_in[1]
+    for f in (0, 7, 19):
+        t = cfg.anchors + f
+        A, B = orc.frame_stats(h.f64("k")[t], h.f64("v")[t], h.f64("beta")[t])
+        assert orc.rel_l2(fr[1, f, 0], np.linalg.inv(np.eye(cfg.d) + A)) <= 1e-4
+        assert orc.rel_l2(fr[1, f, 1], B) <= 1e-3
+    # text slot
+    A, B = orc.frame_stats(h.f64("kt"), h.f64("vt"), h.f64("bt"))
+    assert orc.rel_l2(fr[1, cfg.scanned, 0], np.linalg.inv(np.eye(cfg.d) + A)) <= 1e-4
+
+
+@pytest.mark.parametrize("d,U", [(16, 5), (32, 70), (64, 100), (128, 37), (128, 1000)])
+def test_head_sizes_and_ragged_tokens(d, U):
+    cfg = inp.scaled(inp.CONFIG_BY_NAME["h3"], heads=3, frames=17, tokens=U, d=d, text_tokens=13)
+    _check(cfg)
+
+
+@pytest.mark.parametrize("out_dtype", ["f32", "f16"])
+def test_output_dtypes(out_dtype):
+    cfg = inp.scaled(inp.CONFIG_BY_NAME["h3"], heads=1, frames=12, tokens=200, out_dtype=out_dtype)
+    _, _, _, worst = _check(cfg)
+    assert worst <= 5e-4  # no bf16 rounding of the output
+
+
+def test_float32_inputs_d128():
+    cfg = inp.scaled(inp.CONFIG_BY_NAME["h3"], heads=1, frames=12, tokens=100, in_dtype="f32",
+                     out_dtype="f32")
+    _, _, _, worst = _check(cfg)
+    assert worst <= 5e-4
+
+
+def test_without_bridge():
+    cfg = inp.scaled(inp.CONFIG_BY_NAME["h3"], heads=1, frames=27, tokens=64, d=64)
+    _check(cfg, bridge=False)
+
+
+def test_wide_window_and_unit_chunks():
+    cfg = inp.scaled(inp.CONFIG_BY_NAME["h3"], heads=1, frames=14, tokens=48, d=32, chunk=3, window=2,
+                     text_tokens=0)
+    _check(cfg)
+    cfg = inp.scaled(inp.CONFIG_BY_NAME["h3"], heads=1, frames=9, tokens=48, d=32, chunk=1, window=1,
+                     anchors=0)
+    _check(cfg)
+
+
+def test_reverse_scan_is_forward_scan_on_reversed_time():
+    """Same kernels, same frame data in the opposite order: bitwise equal."""
+    import torch
+    cfg = inp.scaled(inp.CONFIG_BY_NAME["h3"], heads=2, frames=22, tokens=300)
+    heads_in = inp.all_heads(cfg)
+    desc, dev, bufs = runner.run(cfg, heads_in)
+    rev = []
+    for h in heads_in:
+        r = inp.HeadInputs(**{**h.__dict__})
+        for name in ("q", "k", "v", "beta", "alpha"):
+            setattr(r, name, np.ascontiguousarray(getattr(h, name)[::-1]))
+        rev.append(r)
+    _, _, bufs2 = runner.run(cfg, rev)
+    assert torch.equal(bufs.states_r, bufs2.states_f)
+    assert torch.equal(bufs.states_f, bufs2.states_r)
+
+
+def test_no_scanned_frames():
+    cfg = inp.scaled(inp.CONFIG_BY_NAME["h3"], heads=2, frames=2, tokens=40, d=64)
+    heads_in = inp.all_heads(cfg)
+    desc, dev, bufs = runner.run(cfg, heads_in)
+    assert not bufs.out.float().cpu().numpy().any()
+    sf = bufs.states_f.cpu().numpy()
+    for h in range(2):
+        ref = _oracle(cfg, heads_in[h])
+        assert orc.rel_l2(sf[h, 0], ref["states_f"][0]) <= TOL_STATE
+
+
+def test_zero_tokens_is_pure_decay():
+    cfg = inp.scaled(inp.CONFIG_BY_NAME["h3"], heads=1, frames=12, tokens=0, d=64, text_tokens=20)
+    heads_in = inp.all_heads(cfg)
+    desc, dev, bufs = runner.run(cfg, heads_in)
+    ref = _oracle(cfg, heads_in[0])
+    assert orc.rel_l2(bufs.states_f.cpu().numpy()[0], ref["states_f"]) <= TOL_STATE
+    assert orc.rel_l2(bufs.states_r.cpu().numpy()[0], ref["states_r"]) <= TOL_STATE
+
+
+def test_explicit_initial_state():
+    import torch
+    cfg = inp.scaled(inp.CONFIG_BY_NAME["h3"], heads=2, frames=12, tokens=64, d=64, text_tokens=0)
+    heads_in = inp.all_heads(cfg)
+    S0 = np.random.default_rng(5).standard_normal((2, 64, 64)).astype(np.float32)
+    s_init = torch.from_numpy(S0).cuda()
+    desc, dev, bufs = runner.run(cfg, heads_in, s_init=s_init)
+    O = runner.out_f64(bufs)
+    for h in range(2):
+        f = heads_in[h].f64
+        rows, fc = orc.index_maps(cfg.frames, cfg.chunk, cfg.window, cfg.anchors)
+        order = orc.scanned_frames(cfg.frames, cfg.anchors)
+        S_0 = 0.5 * S0[h].astype(np.float64)
+        st_f = orc.scan(order, f("k"), f("v"), f("beta"), f("alpha"), S_0, cfg.chunk)
+        st_r = orc.scan(order[::-1], f("k"), f("v"), f("beta"), f("alpha"), S_0, cfg.chunk)
+        ref = orc.readout_windowed(f("q"), f("alpha"), st_f, st_r, rows, fc)
+        assert orc.rel_l2(bufs.states_f.cpu().numpy()[h], st_f) <= TOL_STATE
+        assert _scanned_rel(O[h], ref, cfg) <= TOL_O
+
+
+def test_device_status_flags_bad_data():
+    """Non-positive-definite I + A (negative write gates) and NaN keys are
+    reported through the status word; the kernels still run to completion."""
+    import torch
+    cfg = inp.scaled(inp.CONFIG_BY_NAME["h3"], heads=1, frames=7, tokens=64, d=32, text_tokens=0)
+    heads_in = inp.all_heads(cfg)
+    h = heads_in[0]
+    h.beta = (-50.0 * np.ones_like(h.beta)).astype(np.float32)
+    desc, dev, bufs = runner.run(cfg, heads_in)
+    assert vda.vda_device_status(desc, bufs.ws) & vda.VDA_DEV_PIVOT
+    heads_in = inp.all_heads(cfg)
+    k = inp.bf16_bits_to_f32(heads_in[0].k).copy()
+    k[3, 5, 7] = np.nan
+    heads_in[0].k = inp.f32_to_bf16_bits(k)
+    desc, dev, bufs = runner.run(cfg, heads_in)
+    assert vda.vda_device_status(desc, bufs.ws) & vda.VDA_DEV_NONFINITE
+    # a clean run clears the word again
+    desc, dev, bufs = runner.run(cfg, inp.all_heads(cfg))
+    assert vda.vda_device_status(desc, bufs.ws) == 0
