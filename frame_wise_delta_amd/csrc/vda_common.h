@@ -28,26 +28,29 @@ __device__ __forceinline__ f32x4 mfma_f16(f16x8 a, f16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
+// Workgroup barrier that orders LDS traffic only: outstanding global loads
+// and stores stay in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // ---------------------------------------------------------- conversions --
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
   return __uint_as_float(bits16 << 16);
 }
-// float -> bf16 bits, round to nearest even (finite inputs; NaN stays NaN).
+// float -> bf16, round to nearest even (gfx950 converts in hardware).
 __device__ __forceinline__ uint32_t f32_to_bf16_bits(float x) {
-  uint32_t u = __float_as_uint(x);
-  if ((u & 0x7f800000u) == 0x7f800000u) return (u >> 16) | ((u & 0xffffu) ? 0x40u : 0u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
+  return __builtin_bit_cast(uint16_t, (__bf16)x);
 }
 __device__ __forceinline__ __bf16 bits_to_bf16(uint32_t b) {
   return __builtin_bit_cast(__bf16, (uint16_t)b);
 }
 // x = hi + lo with hi, lo bfloat16: |x - hi - lo| <= 2^-17 |x| (about).
 __device__ __forceinline__ void split_bf16(float x, __bf16& hi, __bf16& lo) {
-  uint32_t h = f32_to_bf16_bits(x);
-  float hf = bf16_bits_to_f32(h);
-  hi = bits_to_bf16(h);
-  lo = bits_to_bf16(f32_to_bf16_bits(x - hf));
+  hi = (__bf16)x;
+  lo = (__bf16)(x - (float)hi);
 }
 
 // Element type tags for the input / output tensors.
@@ -57,9 +60,22 @@ struct InBF16 { typedef u16 T; static constexpr int bytes = 2; };
 // ------------------------------------------------------------ workspace --
 // [0, 256): device status word (int32) + padding.
 // then, per head h and frame slot f (f < n: scanned frame f; f == n: text),
-// N = (I + A)^{-1} (d x d float32) followed by B (d x d float32).
+// N = (I + A)^{-1} as two d x d bf16 arrays N_hi, N_lo (N ~ N_hi + N_lo) in
+// MFMA fragment order (below), followed by B (d x d float32, row-major):
+// 8 d^2 bytes per slot.
 constexpr size_t kWsHeader = 256;
 
 __host__ __device__ inline size_t ws_slot_floats(int d) { return (size_t)2 * d * d; }
+
+// Fragment order of N: the 16-byte chunk holding N[j][8c .. 8c+7] (row j,
+// k-chunk c) sits at chunk index ((ct * KS + kk) * LG + lg) * 16 + lr with
+// ct = j / 16, lr = j % 16, kk = c / 4, lg = c % 4, KS = max(1, d / 32) and
+// LG = min(4, d / 8).  A wavefront loading the B operand of one 16-column
+// tile and one 32-deep k-step reads 64 consecutive chunks (1 KB).
+__host__ __device__ inline int ntile_chunk(int d, int j, int c) {
+  const int KS = d >= 32 ? d / 32 : 1;
+  const int LG = d >= 32 ? 4 : d / 8;
+  return (((j >> 4) * KS + (c >> 2)) * LG + (c & 3)) * 16 + (j & 15);
+}
 
 }  // namespace vda

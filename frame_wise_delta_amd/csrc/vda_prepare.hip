@@ -1,27 +1,37 @@
-// Frame statistics and factorisation of the VDA frame write.
+// Frame statistics and factorisation of the VDA frame write, as two kernels.
 //
-// For every (head, frame) one workgroup computes, over the frame's U tokens,
+// stats_kernel: for every (head, frame) one workgroup computes, over the
+// frame's U tokens,
 //   A = K^T Diag(beta) K  and  B = V^T Diag(beta) K
 // ("Video DeltaNet: A Video-Native Hybrid Attention for Livestream Video
 // Generation", method-steps section, step (3)) on MFMA with float32
-// accumulation, then inverts G = I + A in registers with a blocked
-// Gauss-Jordan sweep and stores N = G^{-1} and B in the workspace.
-//
-// Data path: K, V rows are streamed from HBM in 64-token rounds, converted to
-// f16 (beta*K is rounded once to f16) and written channel-major into LDS so
-// that an MFMA operand lane reads eight consecutive tokens of one channel
+// accumulation and stores both in the frame's workspace slot (A in the place
+// N will take).  K, V rows are streamed from HBM in 64-token rounds, converted
+// to f16 (beta*K is rounded once to f16) and written channel-major into LDS
+// so that an MFMA operand lane reads eight consecutive tokens of one channel
 // with a single 16-byte LDS load.  The 16-byte token groups of each LDS row
 // are XOR-swizzled so that both the transposing writes and the operand reads
-// are free of bank conflicts.
+// are free of bank conflicts.  The next round's global loads are issued
+// before the current round's MFMAs.
 //
-// Gauss-Jordan: the 16-row strips of G are spread over the four wavefronts
-// and stay in MFMA accumulators.  Each of the d/16 block steps inverts the
-// 16x16 pivot block E in one wavefront (scalar Gauss-Jordan with lane
-// shuffles), forms r' = E^{-1} R and c' = -C E^{-1} on the VALU, and applies
-// the rank-16 update G -= C r' on MFMA with bf16 hi/lo splits of both factors
-// (four products), which keeps the update accurate to about 2^-16.  G is
-// symmetric positive definite (eigenvalues >= 1), so no pivoting is needed;
-// a pivot <= 0 or a non-finite value sets a bit of the device status word.
+// gj_kernel: inverts G = I + A in registers with a blocked Gauss-Jordan
+// sweep and overwrites A with N = G^{-1} as a bf16 hi/lo pair in the MFMA
+// fragment order the scan consumes.  The 16-row strips of G stay in MFMA
+// accumulators spread over the four wavefronts.  Block step p (16 pivot
+// columns):
+//   * the owner of strip p inverts the 16x16 pivot block E with a scalar
+//     Gauss-Jordan, one matrix row per lane, the pivot row broadcast by DPP
+//     row_newbcast, and forms r' = E^{-1} R on MFMA;
+//   * every other strip forms c' = -C E^{-1} on MFMA and applies the rank-16
+//     update G -= C r'.
+// MFMA products use bf16 hi/lo splits of both factors (four partial
+// products), accurate to about 2^-16 relative.  G is symmetric positive
+// definite (eigenvalues >= 1), so no pivoting is needed; a pivot <= 0 or a
+// non-finite value sets a bit of the device status word.  Splitting the two
+// phases lets the latency-bound sweep run at a higher occupancy than the
+// bandwidth-bound statistics.
+#include <utility>
+
 #include "vda_common.h"
 #include "vda_kernels.h"
 
@@ -66,30 +76,97 @@ struct Stage8<InF32> {
   }
 };
 
+// LDS layout of the factorisation phase (byte offsets).  E, R^T and r'^T are
+// double-buffered by step parity.
 template <int D>
-struct PrepSmem {
-  // stats phase: channel-major token tiles
-  static constexpr int kTile = D * kRound;  // halves
-  // factorisation phase (float offsets)
-  static constexpr int kR = 0;                  // [16][D]  pivot row strip
-  static constexpr int kC = kR + 16 * D;        // [D][16]  pivot column strip
-  static constexpr int kE = kC + 16 * D;        // [16][16] pivot block inverse
-  static constexpr int kRp = kE + 256;          // [16][D]  r' = E^-1 R
-  static constexpr int kCp = kRp + 16 * D;      // [D][16]  c' = -C E^-1
-  static constexpr int kRt = kCp + 16 * D;      // [D][16] bf16 hi, then lo, of r'^T
-  static constexpr int kFloats = kRt + 16 * D;  // (2 x D x 16 bf16 = D x 16 floats)
-  static constexpr int kBytes =
-      (3 * kTile * 2 > kFloats * 4) ? 3 * kTile * 2 : kFloats * 4;
+struct GjSmem {
+  static constexpr int kE = 0;                        // [16][16] f32
+  static constexpr int kRT = kE + 16 * 16 * 4;        // [D][16] bf16 hi, then lo
+  static constexpr int kRpT = kRT + 2 * D * 16 * 2;   // [D][16] bf16 hi, then lo
+  static constexpr int kPar = kRpT + 2 * D * 16 * 2;  // bytes per parity
+  static constexpr int kC = 2 * kPar;                 // [4 waves][NRW][16][16] f32
+  static constexpr int kBytes = kC + 4 * ((D / 16 + 3) / 4) * 256 * 4;
 };
+
+
+// Lane k of every 16-lane row, broadcast to the whole row (DPP row_newbcast).
+template <int K>
+__device__ __forceinline__ float row_bcast(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x150 + K, 0xF, 0xF, false));
+}
+
+// One pivot of the scalar Gauss-Jordan inverse below.  With t = x[K] (this
+// row's pivot-column entry) and g = (t - [row is pivot row]) / pivot, every
+// column c != K becomes x[c] - g * pivotrow[c]: this is x[c] / pivot on the
+// pivot row and the usual elimination elsewhere, one FMA per entry.
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+template <int K>
+__device__ __forceinline__ void gj_pivot(f32x16& x, int r, int& bad) {
+  const float piv = row_bcast<K>(x[K]);
+  if (!(piv > 0.f) || !__builtin_isfinite(piv)) bad |= VDA_DEV_PIVOT;
+  const float inv = __builtin_amdgcn_rcpf(piv);  // v_rcp_f32, 1 ulp
+  const float t = x[K];
+  const bool prow = (r == K);
+  const float g = (prow ? t - 1.0f : t) * inv;
+#pragma unroll
+  for (int c = 0; c < 16; ++c)
+    if (c != K) x[c] = fmaf(-g, row_bcast<K>(x[c]), x[c]);
+  x[K] = prow ? inv : -t * inv;
+}
+
+template <int... Ks>
+__device__ __forceinline__ void invert16_impl(f32x16& x, int r, int& bad, std::integer_sequence<int, Ks...>) {
+  (gj_pivot<Ks>(x, r, bad), ...);
+}
+
+// Scalar Gauss-Jordan inverse of a 16x16 matrix held one row per lane (lane
+// l of every 16-lane row holds row l % 16); the result has the same layout.
+__device__ __forceinline__ void invert16(f32x16& x, int r, int& bad) {
+  invert16_impl(x, r, bad, std::make_integer_sequence<int, 16>{});
+}
+
+__device__ __forceinline__ float pick4(const f32x16& x, int grp, int e) {
+  // x[4 * grp + e] for a lane-dependent grp in 0..3
+  return grp == 0 ? x[e] : grp == 1 ? x[4 + e] : grp == 2 ? x[8 + e] : x[12 + e];
+}
+
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
 }  // namespace
 
+// Stage 64 rows of a wavefront-strip-distributed d x d float32 matrix
+// (accumulator layout) through LDS and store them row-major, coalesced.
+template <int D, int NRW>
+__device__ __forceinline__ void store_rows(const f32x4 (&acc)[NRW][D / 16], float* stage, float* dst,
+                                           int tid, int wave, int lg, int lr) {
+  constexpr int RT = D / 16;
+#pragma unroll
+  for (int m = 0; m < NRW; ++m) {
+    const int ri = wave + 4 * m;
+    if (ri < RT) {
+#pragma unroll
+      for (int cj = 0; cj < RT; ++cj)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) stage[(16 * wave + 4 * lg + e) * D + 16 * cj + lr] = acc[m][cj][e];
+    }
+    lds_barrier();
+    const int rows = (D - 64 * m) < 64 ? (D - 64 * m) : 64;
+    float* d = dst + (size_t)64 * m * D;
+    for (int i = tid; i < rows * D / 4; i += kThreads)
+      reinterpret_cast<float4*>(d)[i] = reinterpret_cast<const float4*>(stage)[i];
+    lds_barrier();
+  }
+}
+
 template <int D, class TIN>
-__global__ __launch_bounds__(kThreads, 2) void prepare_kernel(PrepArgs args) {
+__global__ __launch_bounds__(kThreads, 2) void stats_kernel(PrepArgs args) {
   using T = typename TIN::T;
   constexpr int RT = D / 16;              // 16-row tiles
   constexpr int NRW = (RT + 3) / 4;       // row tiles per wavefront
-  __shared__ __attribute__((aligned(16))) char smem[PrepSmem<D>::kBytes];
+  constexpr int kTile = D * kRound;       // halves per LDS token tile
+  constexpr int kBytes = (3 * kTile * 2 > 64 * D * 4) ? 3 * kTile * 2 : 64 * D * 4;
+  __shared__ __attribute__((aligned(16))) char smem[kBytes];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -114,8 +191,8 @@ __global__ __launch_bounds__(kThreads, 2) void prepare_kernel(PrepArgs args) {
   }
 
   _Float16* sK = reinterpret_cast<_Float16*>(smem);
-  _Float16* sBK = sK + PrepSmem<D>::kTile;
-  _Float16* sV = sBK + PrepSmem<D>::kTile;
+  _Float16* sBK = sK + kTile;
+  _Float16* sV = sBK + kTile;
 
   f32x4 accA[NRW][RT], accB[NRW][RT];
 #pragma unroll
@@ -126,40 +203,45 @@ __global__ __launch_bounds__(kThreads, 2) void prepare_kernel(PrepArgs args) {
       accB[m][c] = f32x4{0, 0, 0, 0};
     }
 
-  // ------------------------------------------------------------ stats ----
-  constexpr int CG = D / 8;                    // channel groups of 8
-  constexpr int TASKS = 2 * (kRound / 8) * CG; // (K|V) x token groups x channel groups
-  for (int u0 = 0; u0 < U; u0 += kRound) {
-    for (int task = tid; task < TASKS; task += kThreads) {
-      const int tensor = task / ((kRound / 8) * CG);
-      const int rem = task - tensor * ((kRound / 8) * CG);
-      const int tg = rem / CG, cg = rem - (rem / CG) * CG;
-      const T* src = tensor == 0 ? kp : vp;
-      Stage8<TIN> x;
-      float bt[8];
+  // One load task per thread and round: 8 tokens x 8 channels of K or V.
+  constexpr int CG = D / 8;
+  constexpr int TASKS = 2 * (kRound / 8) * CG;  // <= 256
+  const bool has_task = tid < TASKS;
+  const int tensor = tid / ((kRound / 8) * CG);
+  const int trem = tid - tensor * ((kRound / 8) * CG);
+  const int tg = trem / CG, cg = trem - (trem / CG) * CG;
+  const T* src = tensor == 0 ? kp : vp;
+  Stage8<TIN> pre;
+  float pbt[8];
+  auto fetch = [&](int u0) {
 #pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        const int u = u0 + tg * 8 + s;
-        const bool ok = u < U;
-        x.load(s, src + (size_t)u * D + cg * 8, ok);
-        bt[s] = (tensor == 0 && ok) ? bp[u] : 0.f;
-      }
+    for (int s = 0; s < 8; ++s) {
+      const int u = u0 + tg * 8 + s;
+      const bool ok = has_task && u < U;
+      pre.load(s, src + (size_t)u * D + cg * 8, ok);
+      pbt[s] = (tensor == 0 && ok) ? bp[u] : 0.f;
+    }
+  };
+  if (U > 0) fetch(0);
+  for (int u0 = 0; u0 < U; u0 += kRound) {
+    if (has_task) {
       _Float16* dst = tensor == 0 ? sK : sV;
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
         f16x8 pk;
 #pragma unroll
-        for (int s = 0; s < 8; ++s) pk[s] = (_Float16)x.get(s, c);
+        for (int s = 0; s < 8; ++s) pk[s] = (_Float16)pre.get(s, c);
         *reinterpret_cast<f16x8*>(dst + tile_off(cg * 8 + c, tg)) = pk;
         if (tensor == 0) {
           f16x8 pb;
 #pragma unroll
-          for (int s = 0; s < 8; ++s) pb[s] = (_Float16)(bt[s] * x.get(s, c));
+          for (int s = 0; s < 8; ++s) pb[s] = (_Float16)(pbt[s] * pre.get(s, c));
           *reinterpret_cast<f16x8*>(sBK + tile_off(cg * 8 + c, tg)) = pb;
         }
       }
     }
-    __syncthreads();
+    lds_barrier();
+    if (u0 + kRound < U) fetch(u0 + kRound);  // in flight during the MFMAs
 #pragma unroll
     for (int kk = 0; kk < kRound / 32; ++kk) {
       const int grp = kk * 4 + lg;
@@ -184,182 +266,252 @@ __global__ __launch_bounds__(kThreads, 2) void prepare_kernel(PrepArgs args) {
         }
       }
     }
-    __syncthreads();
+    lds_barrier();
   }
 
-  // G = I + A; flag non-finite statistics
   int bad = 0;
 #pragma unroll
+  for (int m = 0; m < NRW; ++m)
+#pragma unroll
+    for (int cj = 0; cj < RT; ++cj)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (!__builtin_isfinite(accA[m][cj][e]) || !__builtin_isfinite(accB[m][cj][e])) bad |= VDA_DEV_NONFINITE;
+  float* slot = args.frames + ((size_t)h * args.n_eff + f) * ws_slot_floats(D);
+  float* stage = reinterpret_cast<float*>(smem);
+  store_rows<D, NRW>(accA, stage, slot, tid, wave, lg, lr);          // A where N will go
+  store_rows<D, NRW>(accB, stage, slot + D * D, tid, wave, lg, lr);  // B
+  if (bad) atomicOr(args.status, bad);
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads, 3) void gj_kernel(PrepArgs args) {
+  constexpr int RT = D / 16;
+  constexpr int NRW = (RT + 3) / 4;
+  constexpr int kStage = 64 * D * 4;
+  constexpr int kBytes = GjSmem<D>::kBytes > kStage ? GjSmem<D>::kBytes : kStage;
+  __shared__ __attribute__((aligned(16))) char smem[kBytes];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int lr = lane & 15, lg = lane >> 4;
+  float* slot = args.frames + (size_t)blockIdx.x * ws_slot_floats(D);
+  int bad = 0;
+
+  // ---- load A (row-major float32) into the accumulator layout, G = I + A
+  f32x4 accA[NRW][RT];
+  float* stage = reinterpret_cast<float*>(smem);
+#pragma unroll
   for (int m = 0; m < NRW; ++m) {
+    const int rows = (D - 64 * m) < 64 ? (D - 64 * m) : 64;
+    const float* src = slot + (size_t)64 * m * D;
+    for (int i = tid; i < rows * D / 4; i += kThreads)
+      reinterpret_cast<float4*>(stage)[i] = reinterpret_cast<const float4*>(src)[i];
+    lds_barrier();
     const int ri = wave + 4 * m;
     if (ri < RT) {
 #pragma unroll
       for (int cj = 0; cj < RT; ++cj)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          if (!__builtin_isfinite(accA[m][cj][e]) || !__builtin_isfinite(accB[m][cj][e])) bad |= VDA_DEV_NONFINITE;
-          if (cj == ri && 4 * lg + e == lr) accA[m][cj][e] += 1.0f;
+          float v = stage[(16 * wave + 4 * lg + e) * D + 16 * cj + lr];
+          if (cj == ri && 4 * lg + e == lr) v += 1.0f;
+          accA[m][cj][e] = v;
         }
     }
+    lds_barrier();
   }
 
-  // B goes to the workspace now; its registers are free during the sweep
-  float* out = args.frames + ((size_t)h * args.n_eff + f) * ws_slot_floats(D);
+  // ---- blocked Gauss-Jordan sweep
+  char* gj = smem;
+  float* sCw = reinterpret_cast<float*>(gj + GjSmem<D>::kC) + wave * NRW * 256;
+  // fully unrolled: every accumulator index below is a compile-time constant
 #pragma unroll
-  for (int m = 0; m < NRW; ++m) {
-    const int ri = wave + 4 * m;
-    if (ri < RT) {
-#pragma unroll
-      for (int cj = 0; cj < RT; ++cj)
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          out[D * D + (16 * ri + 4 * lg + e) * D + 16 * cj + lr] = accB[m][cj][e];
-    }
-  }
-
-  // ------------------------------------------------- Gauss-Jordan sweep ----
-  float* sf = reinterpret_cast<float*>(smem);
-  float* Rb = sf + PrepSmem<D>::kR;
-  float* Cb = sf + PrepSmem<D>::kC;
-  float* Eb = sf + PrepSmem<D>::kE;
-  float* Rp = sf + PrepSmem<D>::kRp;
-  float* Cp = sf + PrepSmem<D>::kCp;
-  __bf16* RtH = reinterpret_cast<__bf16*>(sf + PrepSmem<D>::kRt);
-  __bf16* RtL = RtH + 16 * D;
-
   for (int p = 0; p < RT; ++p) {
-    // 1. publish the pivot row strip and the pivot column strip
+    char* par = gj + (p & 1) * GjSmem<D>::kPar;
+    float* sE = reinterpret_cast<float*>(par + GjSmem<D>::kE);  // E, then E^{-1}
+    __bf16* sRTh = reinterpret_cast<__bf16*>(par + GjSmem<D>::kRT);
+    __bf16* sRTl = sRTh + D * 16;
+    __bf16* sRpTh = reinterpret_cast<__bf16*>(par + GjSmem<D>::kRpT);
+    __bf16* sRpTl = sRpTh + D * 16;
+    const bool owner = (p % 4) == wave;
+    const int mp = p / 4;
+
+    // A. owner publishes R^T (hi/lo); every wave stages its column strip
 #pragma unroll
     for (int m = 0; m < NRW; ++m) {
       const int ri = wave + 4 * m;
-      if (ri < RT) {
-        if (ri == p) {
+      if (ri >= RT) continue;
+      if (ri == p) {
 #pragma unroll
-          for (int cj = 0; cj < RT; ++cj)
+        for (int cj = 0; cj < RT; ++cj) {
+          bf16x4 hi, lo;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) Rb[(4 * lg + e) * D + 16 * cj + lr] = accA[m][cj][e];
+          for (int e = 0; e < 4; ++e) {
+            __bf16 hh, ll;
+            split_bf16(accA[m][cj][e], hh, ll);
+            hi[e] = hh;
+            lo[e] = ll;
+          }
+          *reinterpret_cast<bf16x4*>(sRTh + (16 * cj + lr) * 16 + 4 * lg) = hi;
+          *reinterpret_cast<bf16x4*>(sRTl + (16 * cj + lr) * 16 + 4 * lg) = lo;
         }
+      }
 #pragma unroll
-        for (int cj = 0; cj < RT; ++cj)
-          if (cj == p) {
+      for (int cj = 0; cj < RT; ++cj)
+        if (cj == p) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) Cb[(16 * ri + 4 * lg + e) * 16 + lr] = accA[m][cj][e];
+          for (int e = 0; e < 4; ++e) sCw[m * 256 + (4 * lg + e) * 16 + lr] = accA[m][cj][e];
+        }
+    }
+
+    // B. owner: E^{-1} (scalar Gauss-Jordan, row lr per lane), r' = E^{-1} R
+    if (owner) {
+      f32x16 x;
+#pragma unroll
+      for (int c = 0; c < 16; c += 4) {
+        const float4 v = *reinterpret_cast<const float4*>(sCw + mp * 256 + lr * 16 + c);
+        x[c] = v.x; x[c + 1] = v.y; x[c + 2] = v.z; x[c + 3] = v.w;
+      }
+      invert16(x, lr, bad);
+      if (lg == 0) {
+#pragma unroll
+        for (int c = 0; c < 16; c += 4)
+          *reinterpret_cast<float4*>(sE + lr * 16 + c) = make_float4(x[c], x[c + 1], x[c + 2], x[c + 3]);
+      }
+      bf16x8 aE;  // A operand [Einv_hi | Einv_lo] (row lr)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        __bf16 hh, ll;
+        split_bf16((lg & 1) ? x[8 + e] : x[e], hh, ll);
+        aE[e] = lg < 2 ? hh : ll;
+      }
+#pragma unroll
+      for (int cj = 0; cj < RT; ++cj) {
+        const bf16x8 rh = *reinterpret_cast<const bf16x8*>(sRTh + (16 * cj + lr) * 16 + 8 * (lg & 1));
+        const bf16x8 rl = *reinterpret_cast<const bf16x8*>(sRTl + (16 * cj + lr) * 16 + 8 * (lg & 1));
+        f32x4 rp = {0, 0, 0, 0};
+        rp = mfma_bf16(aE, rh, rp);
+        rp = mfma_bf16(aE, rl, rp);
+        bf16x4 hi, lo;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          __bf16 hh, ll;
+          split_bf16(rp[e], hh, ll);
+          hi[e] = hh;
+          lo[e] = ll;
+        }
+        *reinterpret_cast<bf16x4*>(sRpTh + (16 * cj + lr) * 16 + 4 * lg) = hi;
+        *reinterpret_cast<bf16x4*>(sRpTl + (16 * cj + lr) * 16 + 4 * lg) = lo;
+#pragma unroll
+        for (int m = 0; m < NRW; ++m)
+          if (m == mp) {
+            if (cj == p) {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) accA[m][cj][e] = pick4(x, lg, e);  // Einv[4lg+e][lr]
+            } else {
+              accA[m][cj] = rp;
+            }
           }
       }
     }
-    __syncthreads();
+    lds_barrier();
 
-    // 2. E^{-1} of the 16x16 pivot block, one wavefront, scalar Gauss-Jordan.
-    //    Lane holds E[r][c0 + e], r = lane % 16, c0 = 4 * (lane / 16).
-    if (wave == 0) {
-      const int r = lane & 15, c0 = 4 * (lane >> 4);
-      float x[4];
+    // C. c' = -C E^{-1} and the rank-16 update G -= C r' outside the pivot strips
+    bf16x8 eh, el;  // B operand rows of E^{-1} (E symmetric)
+    {
+      const float4 v0 = *reinterpret_cast<const float4*>(sE + lr * 16 + 8 * (lg & 1));
+      const float4 v1 = *reinterpret_cast<const float4*>(sE + lr * 16 + 8 * (lg & 1) + 4);
+      const float ev[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) x[e] = Rb[r * D + 16 * p + c0 + e];
-#pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        const float piv = __shfl(x[k & 3], k + 16 * (k >> 2), 64);
-        const float colk = __shfl(x[k & 3], r + 16 * (k >> 2), 64);
-        float rowk[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) rowk[e] = __shfl(x[e], k + 16 * (lane >> 4), 64);
-        if (!(piv > 0.f) || !__builtin_isfinite(piv)) bad |= VDA_DEV_PIVOT;
-        const float inv = 1.0f / piv;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int c = c0 + e;
-          if (r == k)
-            x[e] = (c == k) ? inv : x[e] * inv;
-          else
-            x[e] = (c == k) ? -colk * inv : x[e] - colk * (rowk[e] * inv);
-        }
+      for (int e = 0; e < 8; ++e) {
+        __bf16 hh, ll;
+        split_bf16(ev[e], hh, ll);
+        eh[e] = hh;
+        el[e] = ll;
       }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) Eb[r * 16 + c0 + e] = x[e];
     }
-    __syncthreads();
-
-    // 3. r' = E^{-1} R (16 x D) and c' = -C E^{-1} (D x 16) on the VALU
-    for (int idx = tid; idx < 16 * D; idx += kThreads) {
-      const int q = idx / D, j = idx - (idx / D) * D;
-      float s = 0.f;
-#pragma unroll
-      for (int t = 0; t < 16; ++t) s = fmaf(Eb[q * 16 + t], Rb[t * D + j], s);
-      Rp[q * D + j] = s;
-      __bf16 hi, lo;
-      split_bf16(s, hi, lo);
-      RtH[j * 16 + q] = hi;
-      RtL[j * 16 + q] = lo;
-    }
-    for (int idx = tid; idx < 16 * D; idx += kThreads) {
-      const int i = idx >> 4, q = idx & 15;
-      float s = 0.f;
-#pragma unroll
-      for (int t = 0; t < 16; ++t) s = fmaf(Cb[i * 16 + t], Eb[t * 16 + q], s);
-      Cp[i * 16 + q] = -s;
-    }
-    __syncthreads();
-
-    // 4. rank-16 update G -= C r' outside the pivot row/column strips
 #pragma unroll
     for (int m = 0; m < NRW; ++m) {
       const int ri = wave + 4 * m;
       if (ri < RT && ri != p) {
-        bf16x8 a;
+        bf16x8 aC;  // A operand [-C_hi | -C_lo]
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          __bf16 hi, lo;
-          split_bf16(-Cb[(16 * ri + lr) * 16 + 8 * (lg & 1) + e], hi, lo);
-          a[e] = lg < 2 ? hi : lo;
+          __bf16 hh, ll;
+          split_bf16(-sCw[m * 256 + lr * 16 + 8 * (lg & 1) + e], hh, ll);
+          aC[e] = lg < 2 ? hh : ll;
         }
+        f32x4 cp = {0, 0, 0, 0};
+        cp = mfma_bf16(aC, eh, cp);
+        cp = mfma_bf16(aC, el, cp);
 #pragma unroll
         for (int cj = 0; cj < RT; ++cj) {
-          if (cj != p) {
-            const bf16x8 bh = *reinterpret_cast<const bf16x8*>(RtH + (16 * cj + lr) * 16 + 8 * (lg & 1));
-            const bf16x8 bl = *reinterpret_cast<const bf16x8*>(RtL + (16 * cj + lr) * 16 + 8 * (lg & 1));
-            accA[m][cj] = mfma_bf16(a, bh, accA[m][cj]);
-            accA[m][cj] = mfma_bf16(a, bl, accA[m][cj]);
+          if (cj == p) {
+            accA[m][cj] = cp;
+          } else {
+            const bf16x8 bh = *reinterpret_cast<const bf16x8*>(sRpTh + (16 * cj + lr) * 16 + 8 * (lg & 1));
+            const bf16x8 bl = *reinterpret_cast<const bf16x8*>(sRpTl + (16 * cj + lr) * 16 + 8 * (lg & 1));
+            accA[m][cj] = mfma_bf16(aC, bh, accA[m][cj]);
+            accA[m][cj] = mfma_bf16(aC, bl, accA[m][cj]);
           }
         }
       }
     }
-    // 5. pivot strips take their Gauss-Jordan values
+  }
+  lds_barrier();
+
+  // ---- N -> workspace as bf16 hi/lo in fragment order, 64 rows at a time
+  //      through LDS (overwrites A)
+  // N is symmetric, so each pass stages rows [64m, 64m + 64) of N^T (columns
+  // of N): every lane writes four consecutive row entries with one 8-byte store.
+  __bf16* sh = reinterpret_cast<__bf16*>(smem);
+  __bf16* sl = sh + 64 * D;
+  __bf16* nhi = reinterpret_cast<__bf16*>(slot);
+  __bf16* nlo = nhi + D * D;
 #pragma unroll
-    for (int m = 0; m < NRW; ++m) {
-      const int ri = wave + 4 * m;
+  for (int m = 0; m < NRW; ++m) {
+#pragma unroll
+    for (int mm = 0; mm < NRW; ++mm) {
+      const int ri = wave + 4 * mm;
       if (ri < RT) {
-        if (ri == p) {
 #pragma unroll
-          for (int cj = 0; cj < RT; ++cj)
+        for (int cj = 4 * m; cj < RT && cj < 4 * m + 4; ++cj) {
+          bf16x4 hi, lo;
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-              accA[m][cj][e] = (cj == p) ? Eb[(4 * lg + e) * 16 + lr] : Rp[(4 * lg + e) * D + 16 * cj + lr];
-        } else {
-#pragma unroll
-          for (int cj = 0; cj < RT; ++cj)
-            if (cj == p) {
-#pragma unroll
-              for (int e = 0; e < 4; ++e) accA[m][cj][e] = Cp[(16 * ri + 4 * lg + e) * 16 + lr];
-            }
+          for (int e = 0; e < 4; ++e) {
+            const float v = accA[mm][cj][e];
+            if (!__builtin_isfinite(v)) bad |= VDA_DEV_NONFINITE;
+            __bf16 hh, ll;
+            split_bf16(v, hh, ll);
+            hi[e] = hh;
+            lo[e] = ll;
+          }
+          const int idx = (16 * (cj - 4 * m) + lr) * D + 16 * ri + 4 * lg;
+          *reinterpret_cast<bf16x4*>(sh + idx) = hi;
+          *reinterpret_cast<bf16x4*>(sl + idx) = lo;
         }
       }
     }
-    __syncthreads();
-  }
-
-  // ------------------------------------------------------------ output ----
-#pragma unroll
-  for (int m = 0; m < NRW; ++m) {
-    const int ri = wave + 4 * m;
-    if (ri < RT) {
-#pragma unroll
-      for (int cj = 0; cj < RT; ++cj)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          if (!__builtin_isfinite(accA[m][cj][e])) bad |= VDA_DEV_NONFINITE;
-          out[(16 * ri + 4 * lg + e) * D + 16 * cj + lr] = accA[m][cj][e];
-        }
+    lds_barrier();
+    // rows [64m, 64m + rows) are whole 16-column tiles, i.e. a contiguous
+    // range of fragment-order chunks starting at ntile_chunk(D, 64m, 0)
+    const int rows = (D - 64 * m) < 64 ? (D - 64 * m) : 64;
+    const int n16 = rows * D / 8;  // 16-byte chunks per array
+    const int base = ntile_chunk(D, 64 * m, 0);
+    for (int i = tid; i < 2 * n16; i += kThreads) {
+      const int which = i >= n16;
+      const int q = base + (i - which * n16);  // destination chunk
+      constexpr int KS = D >= 32 ? D / 32 : 1;
+      constexpr int LG = D >= 32 ? 4 : D / 8;
+      const int lrq = q & 15, g = q >> 4;
+      const int lgq = g % LG, t2 = g / LG;
+      const int kk = t2 % KS, ct = t2 / KS;
+      const int j = 16 * ct + lrq, c = 4 * kk + lgq;
+      const uint4 v = *reinterpret_cast<const uint4*>((which ? sl : sh) + (j - 64 * m) * D + 8 * c);
+      reinterpret_cast<uint4*>(which ? nlo : nhi)[q] = v;
     }
+    lds_barrier();
   }
   if (bad) atomicOr(args.status, bad);
 }
@@ -372,9 +524,10 @@ int launch_prepare(const PrepArgs& a, int d, bool in_f32, hipStream_t stream) {
 #define VDA_PREP(DD)                                                                  \
   if (d == DD) {                                                                      \
     if (in_f32)                                                                       \
-      hipLaunchKernelGGL((prepare_kernel<DD, InF32>), grid, block, 0, stream, a);     \
+      hipLaunchKernelGGL((stats_kernel<DD, InF32>), grid, block, 0, stream, a);       \
     else                                                                              \
-      hipLaunchKernelGGL((prepare_kernel<DD, InBF16>), grid, block, 0, stream, a);    \
+      hipLaunchKernelGGL((stats_kernel<DD, InBF16>), grid, block, 0, stream, a);      \
+    hipLaunchKernelGGL((gj_kernel<DD>), grid, block, 0, stream, a);                   \
     return 0;                                                                         \
   }
   VDA_PREP(16) VDA_PREP(32) VDA_PREP(64) VDA_PREP(128)

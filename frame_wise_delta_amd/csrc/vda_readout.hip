@@ -15,7 +15,8 @@
 //
 // One workgroup per (head, frame).  Wavefront w owns value-channel tiles
 // w, w+4, ... and keeps its rows of W_t in registers as bf16 hi/lo pairs;
-// 64-token tiles of Q are staged in LDS with one coalesced pass and each
+// 128-token tiles of Q are staged in LDS with one coalesced pass (the next
+// tile's loads are issued before the current tile's MFMAs) and each
 // wavefront computes O^T = W Q^T on MFMA (2 products per tile for bf16 Q,
 // 3 for float32 Q split hi/lo), accumulating in float32.
 #include "vda_common.h"
@@ -25,7 +26,9 @@ namespace vda {
 
 namespace {
 
-constexpr int kQT = 64;  // tokens per LDS tile
+constexpr int kQT = 128;  // tokens per LDS tile
+
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
 template <int OUT>
 struct OutT;
@@ -39,10 +42,8 @@ struct OutT<VDA_F32> {
 template <>
 struct OutT<VDA_BF16> {
   static __device__ __forceinline__ void store4(void* base, size_t idx, f32x4 v) {
-    uint2 p;
-    p.x = f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16);
-    p.y = f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16);
-    *reinterpret_cast<uint2*>(static_cast<u16*>(base) + idx) = p;
+    bf16x4 b = {(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
+    *reinterpret_cast<bf16x4*>(static_cast<u16*>(base) + idx) = b;
   }
   static constexpr int bytes = 2;
 };
@@ -95,6 +96,8 @@ __global__ __launch_bounds__(kThreads, 2) void readout_kernel(ReadArgs a) {
   constexpr int NVT = (VT + 3) / 4;                  // tiles per wavefront
   constexpr int KS = D / 32 > 0 ? D / 32 : 1;        // MFMA k-steps
   constexpr int PITCH = D * TIN::bytes + 16;         // LDS bytes per token row
+  constexpr int CH = D * TIN::bytes / 16;            // 16-byte chunks per token row
+  constexpr int PER = (kQT * CH + kThreads - 1) / kThreads;  // chunks per thread per tile
   __shared__ __attribute__((aligned(16))) char sQ[kQT * PITCH];
   __shared__ float sBf[D], sBr[D];
 
@@ -112,6 +115,21 @@ __global__ __launch_bounds__(kThreads, 2) void readout_kernel(ReadArgs a) {
     return;
   }
 
+  // ---- first Q tile in flight while the states and bridges are read
+  const T* qh = static_cast<const T*>(a.q) + frame_off;
+  uint4 pre[PER];
+  auto fetch = [&](int u0) {
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int i = tid + j * kThreads;
+      const int r = i / CH, ch = i - r * CH;
+      pre[j] = (i < kQT * CH && u0 + r < a.U)
+                   ? reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(qh + (size_t)(u0 + r) * D))[ch]
+                   : make_uint4(0, 0, 0, 0);
+    }
+  };
+  fetch(0);
+
   // ---- states and bridges for this frame
   const int f = t - a.a;
   const float* sf;
@@ -125,14 +143,22 @@ __global__ __launch_bounds__(kThreads, 2) void readout_kernel(ReadArgs a) {
     const int we = a.a + a.P * (hi + 1) - 1;
     sf = a.sf + ((size_t)h * a.count + lo) * D * D;
     sr = a.sr + ((size_t)h * a.count + (a.C - 1 - hi)) * D * D;
-    for (int k = tid; k < D; k += kThreads) {
-      float bf = 1.f, br = 1.f;
+    // thread k < D: forward bridge of channel k; D <= k < 2D: reverse bridge
+    for (int k2 = tid; k2 < 2 * D; k2 += kThreads) {
+      const bool rev = k2 >= D;
+      const int k = rev ? k2 - D : k2;
+      const int r0 = rev ? t : ws, r1 = rev ? we : t;  // inclusive frame range
+      float prod = 1.f;
       if (a.bridge) {
-        for (int r = ws; r <= t; ++r) bf *= alpha_h[(size_t)r * D + k];
-        for (int r = t; r <= we; ++r) br *= alpha_h[(size_t)r * D + k];
+        for (int rb = r0; rb <= r1; rb += 16) {  // 16 loads in flight per pass
+          float v[16];
+#pragma unroll
+          for (int j = 0; j < 16; ++j) v[j] = (rb + j <= r1) ? alpha_h[(size_t)(rb + j) * D + k] : 1.f;
+#pragma unroll
+          for (int j = 0; j < 16; ++j) prod *= v[j];
+        }
       }
-      sBf[k] = bf;
-      sBr[k] = br;
+      (rev ? sBr : sBf)[k] = prod;
     }
   } else {
     sf = a.sf + ((size_t)h * a.count + f + 1) * D * D;
@@ -141,7 +167,7 @@ __global__ __launch_bounds__(kThreads, 2) void readout_kernel(ReadArgs a) {
       sBr[k] = 0.f;
     }
   }
-  __syncthreads();
+  lds_barrier();
 
   // ---- W rows of this wavefront's value tiles, bf16 hi/lo, A-operand layout
   bf16x8 wh[NVT][KS], wl[NVT][KS];
@@ -151,37 +177,50 @@ __global__ __launch_bounds__(kThreads, 2) void readout_kernel(ReadArgs a) {
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
       const int k0 = 32 * kk + 8 * lg;
+      float x[8];
+      if (vt < VT && k0 < D) {
+        const size_t idx = (size_t)(16 * vt + lr) * D + k0;
+        const float4 f0 = *reinterpret_cast<const float4*>(sf + idx);
+        const float4 f1 = *reinterpret_cast<const float4*>(sf + idx + 4);
+        x[0] = f0.x * sBf[k0]; x[1] = f0.y * sBf[k0 + 1]; x[2] = f0.z * sBf[k0 + 2]; x[3] = f0.w * sBf[k0 + 3];
+        x[4] = f1.x * sBf[k0 + 4]; x[5] = f1.y * sBf[k0 + 5]; x[6] = f1.z * sBf[k0 + 6]; x[7] = f1.w * sBf[k0 + 7];
+        if (sr) {
+          const float4 r0 = *reinterpret_cast<const float4*>(sr + idx);
+          const float4 r1 = *reinterpret_cast<const float4*>(sr + idx + 4);
+          x[0] = fmaf(r0.x, sBr[k0], x[0]); x[1] = fmaf(r0.y, sBr[k0 + 1], x[1]);
+          x[2] = fmaf(r0.z, sBr[k0 + 2], x[2]); x[3] = fmaf(r0.w, sBr[k0 + 3], x[3]);
+          x[4] = fmaf(r1.x, sBr[k0 + 4], x[4]); x[5] = fmaf(r1.y, sBr[k0 + 5], x[5]);
+          x[6] = fmaf(r1.z, sBr[k0 + 6], x[6]); x[7] = fmaf(r1.w, sBr[k0 + 7], x[7]);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = 0.f;
+      }
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        float x = 0.f;
-        if (vt < VT && k0 + e < D) {
-          const size_t idx = (size_t)(16 * vt + lr) * D + k0 + e;
-          x = sf[idx] * sBf[k0 + e];
-          if (sr) x = fmaf(sr[idx], sBr[k0 + e], x);
-        }
         __bf16 hh, ll;
-        split_bf16(x, hh, ll);
+        split_bf16(x[e], hh, ll);
         wh[i][kk][e] = hh;
         wl[i][kk][e] = ll;
       }
     }
   }
 
-  // ---- token tiles
-  const T* qh = static_cast<const T*>(a.q) + frame_off;
-  constexpr int CH = D * TIN::bytes / 16;  // 16-byte chunks per token row
+  // ---- token tiles: the next tile's loads are in flight during the MFMAs
   for (int u0 = 0; u0 < a.U; u0 += kQT) {
-    for (int i = tid; i < kQT * CH; i += kThreads) {
-      const int r = i / CH, ch = i - r * CH;
-      uint4 val = make_uint4(0, 0, 0, 0);
-      if (u0 + r < a.U)
-        val = reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(qh + (size_t)(u0 + r) * D))[ch];
-      *reinterpret_cast<uint4*>(sQ + r * PITCH + 16 * ch) = val;
-    }
-    __syncthreads();
-    if (wave < VT) {
 #pragma unroll
-      for (int st = 0; st < kQT / 16; ++st) {
+    for (int j = 0; j < PER; ++j) {
+      const int i = tid + j * kThreads;
+      if (i < kQT * CH) {
+        const int r = i / CH, ch = i - r * CH;
+        *reinterpret_cast<uint4*>(sQ + r * PITCH + 16 * ch) = pre[j];
+      }
+    }
+    lds_barrier();
+    if (u0 + kQT < a.U) fetch(u0 + kQT);
+    if (wave < VT) {
+      const int nsub = (a.U - u0) >= kQT ? kQT / 16 : (a.U - u0 + 15) / 16;
+      for (int st = 0; st < nsub; ++st) {
         const int ul = 16 * st + lr;  // token of this lane's operand column
         f32x4 acc[NVT];
 #pragma unroll
@@ -210,7 +249,7 @@ __global__ __launch_bounds__(kThreads, 2) void readout_kernel(ReadArgs a) {
         }
       }
     }
-    __syncthreads();
+    lds_barrier();
   }
 }
 

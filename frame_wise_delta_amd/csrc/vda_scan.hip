@@ -7,13 +7,19 @@
 // method-steps section, step (4): both scans start from the text state.)
 //
 // The d_v rows of S evolve independently (row i: s_t = (s_{t-1} * alpha_t +
-// b_t) N_t), so one (head, direction) chain is split over d/16 workgroups of
-// 16 rows each.  A workgroup keeps its 16 x d slice of S in LDS in float32.
+// b_t) N_t), so one (head, direction) chain is split over d/32 workgroups of
+// 32 rows each (16 for d = 16); the row blocks of a head are mapped to one
+// XCD so that they share that XCD's L2 copy of N_t.  A workgroup keeps its
+// 32 x d slice of S in LDS in float32 and runs d/16 wavefronts, one per
+// 16-column output tile.
 // Per frame, the VALU forms X = S Diag(alpha) + B (float32) and splits it into
-// bf16 hi/lo; each wavefront then computes 16 x (d/4) of X N on MFMA as
-// X_hi N_hi + X_hi N_lo + X_lo N_hi (error about 2^-16 relative), with the N
-// columns read as rows (N is symmetric).  The next frame's N, B rows and alpha
-// are loaded into registers while the current frame is multiplied.
+// bf16 hi/lo in LDS; each wavefront computes its 16 x 16 tile of X N on MFMA
+// as X_hi N_hi + X_hi N_lo + X_lo N_hi (about 2^-16 relative error), N being
+// stored pre-split by the prepare kernel in MFMA fragment order and read as
+// rows (N is symmetric).
+// The chain is bound by the latency of these per-frame operand loads, so
+// frames are prefetched three or four steps ahead into registers; the barriers wait
+// for LDS traffic only, so the global loads stay in flight across them.
 #include "vda_common.h"
 #include "vda_kernels.h"
 
@@ -23,165 +29,189 @@ namespace {
 
 template <int D>
 struct ScanShape {
-  static constexpr int NW = (D / 16) < 4 ? (D / 16) : 4;  // active wavefronts
-  static constexpr int CTW = (D / 16) / NW;               // 16-column tiles per wavefront
-  static constexpr int KS = D / 32 > 0 ? D / 32 : 1;      // MFMA k-steps (D = 16: one, zero padded)
-  static constexpr int EPT = 16 * D / kThreads;           // X elements per thread (>= 1)
-  static constexpr int XP = D + 8;                        // LDS row pitch of X (halves)
+  static constexpr int ROWS = D < 32 ? D : 32;          // state rows per workgroup
+  static constexpr int RTS = ROWS / 16;                 // 16-row tiles per workgroup
+  static constexpr int NW = D / 16;                     // wavefronts = 16-column tiles
+  static constexpr int NT = 64 * NW;                    // threads
+  static constexpr int KS = D >= 32 ? D / 32 : 1;       // MFMA k-steps (D = 16: one, zero padded)
+  static constexpr int XP = D + 8;                      // LDS row pitch of X (halves)
+  static constexpr int NQ = ROWS / 16;                  // float4 X chunks per thread
+  static constexpr int TPR = D / 4;                     // threads per row in the elementwise phase
+  static constexpr int LG = D >= 32 ? 4 : D / 8;        // k-chunk groups per fragment-order block
+  static constexpr int PD = D >= 128 ? 3 : (D >= 64 ? 4 : 2);  // frames prefetched ahead
 };
 
-// Registers holding one frame's operands for this thread.
+// Operands of one frame held by one thread.
 template <int D>
 struct FrameRegs {
-  float n[ScanShape<D>::CTW][ScanShape<D>::KS][8];  // N columns of this wavefront's tiles
-  float b[ScanShape<D>::EPT > 0 ? ScanShape<D>::EPT : 1];
-  float al[ScanShape<D>::EPT > 0 ? ScanShape<D>::EPT : 1];
+  bf16x8 nh[ScanShape<D>::KS], nl[ScanShape<D>::KS];  // N column tile (k-slices of this lane)
+  float4 b[ScanShape<D>::NQ];                          // B row segments (rows xrow + 16 q)
+  float4 al;                                           // alpha segment
 };
-
-template <int D>
-__device__ __forceinline__ void load_frame(FrameRegs<D>& fr, const float* slot, const float* alpha_row,
-                                           int r0, int tid, int wave, int lane) {
-  using S = ScanShape<D>;
-  const int lr = lane & 15, lg = lane >> 4;
-  if (wave < S::NW) {
-#pragma unroll
-    for (int i = 0; i < S::CTW; ++i) {
-      const int col = 16 * (wave * S::CTW + i) + lr;
-#pragma unroll
-      for (int kk = 0; kk < S::KS; ++kk) {
-        const int k0 = 32 * kk + 8 * lg;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) fr.n[i][kk][e] = (k0 + e < D) ? slot[(size_t)col * D + k0 + e] : 0.f;
-      }
-    }
-  }
-  // X elements: row tid / (D / EPT), columns contiguous
-  constexpr int TPR = D / S::EPT;  // threads per row
-  const int row = tid / TPR, c0 = (tid - row * TPR) * S::EPT;
-  if (row < 16) {
-#pragma unroll
-    for (int e = 0; e < S::EPT; ++e) {
-      fr.b[e] = slot[(size_t)D * D + (size_t)(r0 + row) * D + c0 + e];
-      fr.al[e] = alpha_row ? alpha_row[c0 + e] : 1.f;
-    }
-  }
-}
 
 }  // namespace
 
 template <int D>
-__global__ __launch_bounds__(kThreads) void scan_kernel(ScanArgs a) {
-  using S = ScanShape<D>;
-  __shared__ __attribute__((aligned(16))) float sS[16 * D];
-  __shared__ __attribute__((aligned(16))) __bf16 sXh[16 * S::XP];
-  __shared__ __attribute__((aligned(16))) __bf16 sXl[16 * S::XP];
+__global__ __launch_bounds__(ScanShape<D>::NT) void scan_kernel(ScanArgs a) {
+  using SS = ScanShape<D>;
+  constexpr int ROWS = SS::ROWS, NQ = SS::NQ, PD = SS::PD;
+  __shared__ __attribute__((aligned(16))) float sS[ROWS * D];
+  __shared__ __attribute__((aligned(16))) __bf16 sXh[ROWS * SS::XP];
+  __shared__ __attribute__((aligned(16))) __bf16 sXl[ROWS * SS::XP];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, lg = lane >> 4;
-  constexpr int RB = D / 16;
-  const int h = blockIdx.x / RB;
-  const int r0 = 16 * (blockIdx.x - h * RB);
-  constexpr int TPR = D / S::EPT;
-  const int xrow = tid / TPR, xc0 = (tid - xrow * TPR) * S::EPT;
+  constexpr int RB = D / ROWS;  // row blocks per head
+  const int nb = gridDim.x;
+  const int b = blockIdx.x;
+  const int L = (nb % 8 == 0) ? (b % 8) * (nb / 8) + b / 8 : b;  // XCD-aware order
+  const int h = L / RB;
+  const int r0 = ROWS * (L - h * RB);
+  // elementwise phase: thread owns columns xc0..xc0+3 of rows xrow + 16 q
+  const int xrow = tid / SS::TPR, xc0 = 4 * (tid - xrow * SS::TPR);
+  const int ct = wave;  // output column tile
 
-  const float* frames = a.frames + (size_t)h * a.n_eff * ws_slot_floats(D);
+  const size_t slot_floats = ws_slot_floats(D);
+  const float* frames = a.frames + (size_t)h * a.n_eff * slot_floats;
   const float* alpha_h = a.alpha + (size_t)h * a.T * D;
   float* states_h = a.states + (size_t)h * a.count * D * D;
 
-  // one frame write on the LDS state slice: S <- (S Diag(al) + B) N
-  auto step = [&](const FrameRegs<D>& fr, float* rec) {
-    if (xrow < 16) {
+  auto load = [&](FrameRegs<D>& fr, int slot, const float* alpha_row) {
+    const float* base = frames + (size_t)slot * slot_floats;
+    const __bf16* nhi = reinterpret_cast<const __bf16*>(base);
+    const __bf16* nlo = nhi + D * D;
+    const float* bm = base + D * D;
+    // fragment order: one wavefront reads 64 consecutive 16-byte chunks
 #pragma unroll
-      for (int e = 0; e < S::EPT; ++e) {
-        const float x = fmaf(sS[xrow * D + xc0 + e], fr.al[e], fr.b[e]);
-        __bf16 hi, lo;
-        split_bf16(x, hi, lo);
-        sXh[xrow * S::XP + xc0 + e] = hi;
-        sXl[xrow * S::XP + xc0 + e] = lo;
+    for (int kk = 0; kk < SS::KS; ++kk) {
+      if (lg < SS::LG) {
+        const int chunk = ((ct * SS::KS + kk) * SS::LG + lg) * 16 + lr;
+        fr.nh[kk] = reinterpret_cast<const bf16x8*>(nhi)[chunk];
+        fr.nl[kk] = reinterpret_cast<const bf16x8*>(nlo)[chunk];
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) fr.nh[kk][e] = fr.nl[kk][e] = bits_to_bf16(0);
       }
     }
-    __syncthreads();
-    if (wave < S::NW) {
 #pragma unroll
-      for (int i = 0; i < S::CTW; ++i) {
-        const int ct = wave * S::CTW + i;
-        f32x4 acc = {0, 0, 0, 0};
+    for (int q = 0; q < NQ; ++q)
+      fr.b[q] = *reinterpret_cast<const float4*>(bm + (size_t)(r0 + xrow + 16 * q) * D + xc0);
+    fr.al = alpha_row ? *reinterpret_cast<const float4*>(alpha_row + xc0) : make_float4(1.f, 1.f, 1.f, 1.f);
+  };
+
+  // one frame write on the LDS state slice: S <- (S Diag(al) + B) N; a step
+  // with live == false leaves S unchanged (padding at the end of the chain)
+  auto step = [&](const FrameRegs<D>& fr, float* rec, bool live) {
 #pragma unroll
-        for (int kk = 0; kk < S::KS; ++kk) {
-          const int k0 = 32 * kk + 8 * lg;
-          bf16x8 xh, xl, nh, nl;
+    for (int q = 0; q < NQ; ++q) {
+      const int row = xrow + 16 * q;
+      const float4 s = *reinterpret_cast<const float4*>(sS + row * D + xc0);
+      const float4 al = fr.al, bb = fr.b[q];
+      const float x[4] = {fmaf(s.x, al.x, bb.x), fmaf(s.y, al.y, bb.y), fmaf(s.z, al.z, bb.z),
+                          fmaf(s.w, al.w, bb.w)};
+      typedef __bf16 bf4 __attribute__((ext_vector_type(4)));
+      bf4 hi, lo;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const bool in = k0 + e < D;
-            xh[e] = in ? sXh[lr * S::XP + k0 + e] : bits_to_bf16(0);
-            xl[e] = in ? sXl[lr * S::XP + k0 + e] : bits_to_bf16(0);
-            __bf16 hi, lo;
-            split_bf16(fr.n[i][kk][e], hi, lo);
-            nh[e] = hi;
-            nl[e] = lo;
-          }
-          acc = mfma_bf16(xh, nh, acc);
-          acc = mfma_bf16(xh, nl, acc);
-          acc = mfma_bf16(xl, nh, acc);
+      for (int e = 0; e < 4; ++e) {
+        __bf16 hh, ll;
+        split_bf16(x[e], hh, ll);
+        hi[e] = hh;
+        lo[e] = ll;
+      }
+      *reinterpret_cast<bf4*>(sXh + row * SS::XP + xc0) = hi;
+      *reinterpret_cast<bf4*>(sXl + row * SS::XP + xc0) = lo;
+    }
+    lds_barrier();
+    f32x4 acc[SS::RTS];
+#pragma unroll
+    for (int rt = 0; rt < SS::RTS; ++rt) acc[rt] = f32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int kk = 0; kk < SS::KS; ++kk) {
+      const int k0 = 32 * kk + 8 * lg;
+#pragma unroll
+      for (int rt = 0; rt < SS::RTS; ++rt) {
+        bf16x8 xh, xl;
+        if (k0 < D) {
+          xh = *reinterpret_cast<const bf16x8*>(sXh + (16 * rt + lr) * SS::XP + k0);
+          xl = *reinterpret_cast<const bf16x8*>(sXl + (16 * rt + lr) * SS::XP + k0);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) xh[e] = xl[e] = bits_to_bf16(0);
         }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          sS[(4 * lg + e) * D + 16 * ct + lr] = acc[e];
-          if (rec) rec[(size_t)(r0 + 4 * lg + e) * D + 16 * ct + lr] = acc[e];
-        }
+        acc[rt] = mfma_bf16(xh, fr.nh[kk], acc[rt]);
+        acc[rt] = mfma_bf16(xh, fr.nl[kk], acc[rt]);
+        acc[rt] = mfma_bf16(xl, fr.nh[kk], acc[rt]);
       }
     }
-    __syncthreads();
+#pragma unroll
+    for (int rt = 0; rt < SS::RTS; ++rt) {
+      if (live) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sS[(16 * rt + 4 * lg + e) * D + 16 * ct + lr] = acc[rt][e];
+      }
+      if (rec) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) rec[(size_t)(r0 + 16 * rt + 4 * lg + e) * D + 16 * ct + lr] = acc[rt][e];
+      }
+    }
+    lds_barrier();
   };
 
   // ---- initial state
-  for (int i = tid; i < 16 * D; i += kThreads) sS[i] = 0.f;
-  __syncthreads();
   if (a.s_init) {
-    const float* si = a.s_init + (size_t)h * D * D;
-    for (int i = tid; i < 16 * D; i += kThreads) sS[i] = si[(size_t)r0 * D + i];
-    __syncthreads();
-  } else if (a.use_text) {
-    FrameRegs<D> fr;
-    load_frame<D>(fr, frames + (size_t)a.n * ws_slot_floats(D), nullptr, r0, tid, wave, lane);
-    step(fr, nullptr);  // S^T = (0 + B_T) N_T
+    const float* si = a.s_init + (size_t)h * D * D + (size_t)r0 * D;
+    for (int i = tid; i < ROWS * D; i += SS::NT) sS[i] = si[i];
+  } else {
+    for (int i = tid; i < ROWS * D; i += SS::NT) sS[i] = 0.f;
   }
-  for (int i = tid; i < 16 * D; i += kThreads) {
+  lds_barrier();
+  if (!a.s_init && a.use_text) {
+    FrameRegs<D> fr;
+    load(fr, a.n, nullptr);
+    step(fr, nullptr, true);  // S^T = (0 + B_T) N_T
+  }
+  for (int i = tid; i < ROWS * D; i += SS::NT) {
     const float s0 = a.scale * sS[i];
     sS[i] = s0;
     states_h[(size_t)r0 * D + i] = s0;
   }
-  __syncthreads();
+  lds_barrier();
 
-  // ---- the chain, with the next frame's operands prefetched
-  if (a.n == 0) return;
-  FrameRegs<D> cur, nxt;
-  {
-    const int f0 = a.reverse ? a.n - 1 : 0;
-    load_frame<D>(cur, frames + (size_t)f0 * ws_slot_floats(D), alpha_h + (size_t)(a.a + f0) * D, r0, tid,
-                  wave, lane);
-  }
-  for (int i = 0; i < a.n; ++i) {
-    if (i + 1 < a.n) {
-      const int f1 = a.reverse ? a.n - 2 - i : i + 1;
-      load_frame<D>(nxt, frames + (size_t)f1 * ws_slot_floats(D), alpha_h + (size_t)(a.a + f1) * D, r0, tid,
-                    wave, lane);
+  // ---- the chain, operands prefetched PD frames ahead (PD + 1 register sets).
+  // Loads past the last frame re-read the last frame, so every step issues
+  // the same loads and the wait before a step covers only that step's operands.
+  const int n = a.n;
+  if (n == 0) return;
+  auto slot_of = [&](int i) { return a.reverse ? n - 1 - i : i; };
+  auto alpha_of = [&](int i) { return alpha_h + (size_t)(a.a + slot_of(i)) * D; };
+  auto cl = [&](int i) { return i < n ? i : n - 1; };
+  auto rec_of = [&](int i) -> float* {
+    const bool record = i < n && (((i + 1) % a.every == 0) || (i + 1 == n));
+    return record ? states_h + (size_t)((i + a.every) / a.every) * D * D : nullptr;
+  };
+  // The chain runs in blocks of PD + 1 steps without an early exit (a single
+  // loop exit keeps the waits before each step precise); steps past the last
+  // frame are no-ops.
+  FrameRegs<D> fr[PD + 1];
+#pragma unroll
+  for (int j = 0; j < PD; ++j) load(fr[j], slot_of(cl(j)), alpha_of(cl(j)));
+  for (int i0 = 0; i0 < n; i0 += PD + 1) {
+#pragma unroll
+    for (int j = 0; j <= PD; ++j) {
+      const int i = i0 + j;
+      load(fr[(j + PD) % (PD + 1)], slot_of(cl(i + PD)), alpha_of(cl(i + PD)));
+      step(fr[j], rec_of(i), i < n);
     }
-    const bool record = ((i + 1) % a.every == 0) || (i + 1 == a.n);
-    const int j = (i + a.every) / a.every;  // index of the state after i + 1 frames
-    step(cur, record ? states_h + (size_t)j * D * D : nullptr);
-    cur = nxt;
   }
 }
 
 int launch_scan(const ScanArgs& a, int d, hipStream_t stream) {
   if (a.H == 0) return 0;
-  dim3 block(kThreads);
-#define VDA_SCAN(DD)                                                                   \
-  if (d == DD) {                                                                       \
-    hipLaunchKernelGGL((scan_kernel<DD>), dim3((unsigned)(a.H * (DD / 16))), block, 0, \
-                       stream, a);                                                     \
-    return 0;                                                                          \
+#define VDA_SCAN(DD)                                                                     \
+  if (d == DD) {                                                                         \
+    hipLaunchKernelGGL((scan_kernel<DD>), dim3((unsigned)(a.H * (DD / ScanShape<DD>::ROWS))), \
+                       dim3(ScanShape<DD>::NT), 0, stream, a);                           \
+    return 0;                                                                            \
   }
   VDA_SCAN(16) VDA_SCAN(32) VDA_SCAN(64) VDA_SCAN(128)
 #undef VDA_SCAN

@@ -58,7 +58,22 @@ def _ws_frames(bufs, desc):
     n = desc.frames - 2 * desc.anchors
     n_eff = n + (1 if desc.text_tokens else 0)
     raw = bufs.ws.cpu().numpy()[256:256 + desc.heads * n_eff * 2 * d * d * 4]
-    return raw.view(np.float32).reshape(desc.heads, n_eff, 2, d, d).astype(np.float64)
+    slots = raw.reshape(desc.heads, n_eff, 8 * d * d)
+    # N is stored in MFMA fragment order: chunk ((ct*KS + kk)*LG + lg)*16 + lr
+    # holds N[16 ct + lr][32 kk + 8 lg .. +7]
+    KS, LG = max(1, d // 32), min(4, d // 8)
+    j = np.arange(d)[:, None]
+    c = np.arange(d // 8)[None, :]
+    chunk = (((j // 16) * KS + c // 4) * LG + c % 4) * 16 + j % 16
+    idx = (chunk[:, :, None] * 8 + np.arange(8)[None, None, :]).reshape(d, d)
+
+    def untile(part):
+        v = inp.bf16_bits_to_f32(part.copy().view(np.uint16)).reshape(desc.heads, n_eff, d * d)
+        return v[..., idx]
+    hi = untile(slots[..., :2 * d * d])
+    lo = untile(slots[..., 2 * d * d:4 * d * d])
+    B = slots[..., 4 * d * d:].copy().view(np.float32).reshape(desc.heads, n_eff, d, d)
+    return np.stack([hi.astype(np.float64) + lo, B.astype(np.float64)], axis=2)
 
 
 def test_tiny_config():
