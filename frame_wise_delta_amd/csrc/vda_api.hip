@@ -172,10 +172,14 @@ int vda_index_map(const vda_desc* desc, int32_t* chunk_rows, int32_t* frame_chun
   return ok();
 }
 
-int vda_prepare_frames(const vda_desc* desc, const void* k, const void* v, const float* beta,
-                       const void* k_text, const void* v_text, const float* beta_text, void* ws,
-                       size_t ws_size, void* stream) {
-  Shape s;
+}  // extern "C"
+
+namespace {
+
+// Validation + argument blocks of the individual steps (host only).
+int prep_args(const vda_desc* desc, const void* k, const void* v, const float* beta, const void* k_text,
+              const void* v_text, const float* beta_text, void* ws, size_t ws_size, Shape& s,
+              vda::PrepArgs& a) {
   int rc = check_desc(desc, &s);
   if (rc) return rc;
   const bool need_video = (size_t)s.H * s.n * s.U > 0;
@@ -187,10 +191,6 @@ int vda_prepare_frames(const vda_desc* desc, const void* k, const void* v, const
   if (!aligned16(k) || !aligned16(v) || !aligned16(beta) || !aligned16(k_text) || !aligned16(v_text) ||
       !aligned16(beta_text) || ((uintptr_t)ws & 255u))
     return fail(VDA_ERR_ALIGN, "k, v, beta, k_text, v_text, beta_text need 16-byte and ws 256-byte alignment");
-  rc = check_device();
-  if (rc) return rc;
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  vda::PrepArgs a;
   a.k = k;
   a.v = v;
   a.beta = beta;
@@ -206,14 +206,13 @@ int vda_prepare_frames(const vda_desc* desc, const void* k, const void* v, const
   a.n = s.n;
   a.n_eff = s.n_eff;
   a.Nt = s.Nt;
-  vda::launch_clear_status(a.status, st);
-  vda::launch_prepare(a, s.d, desc->in_dtype == VDA_F32, st);
-  return launch_status();
+  a.s0 = 0;
+  a.cnt = s.n_eff;
+  return VDA_OK;
 }
 
-static int scan_common(const vda_desc* desc, const void* ws, const float* alpha, const float* s_init,
-                       float* states, void* stream, int reverse) {
-  Shape s;
+int scan_args(const vda_desc* desc, const void* ws, const float* alpha, const float* s_init, float* states,
+              int reverse, Shape& s, vda::ScanArgs& a) {
   int rc = check_desc(desc, &s);
   if (rc) return rc;
   if (!ws) return fail(VDA_ERR_NULL, "ws is NULL");
@@ -221,9 +220,6 @@ static int scan_common(const vda_desc* desc, const void* ws, const float* alpha,
   if (s.H * (size_t)s.n > 0 && !alpha) return fail(VDA_ERR_NULL, "alpha is NULL");
   if (!aligned16(alpha) || !aligned16(s_init) || !aligned16(states) || ((uintptr_t)ws & 255u))
     return fail(VDA_ERR_ALIGN, "alpha, s_init, states need 16-byte and ws 256-byte alignment");
-  rc = check_device();
-  if (rc) return rc;
-  vda::ScanArgs a;
   a.frames = reinterpret_cast<const float*>(static_cast<const char*>(ws) + vda::kWsHeader);
   a.alpha = alpha;
   a.s_init = s_init;
@@ -238,26 +234,14 @@ static int scan_common(const vda_desc* desc, const void* ws, const float* alpha,
   a.reverse = reverse;
   a.use_text = s.Nt > 0;
   a.scale = desc->text_init_scale;
-  vda::launch_scan(a, s.d, static_cast<hipStream_t>(stream));
-  return launch_status();
+  return VDA_OK;
 }
 
-int vda_scan_fwd(const vda_desc* desc, const void* ws, const float* alpha, const float* s_init, float* states,
-                 void* stream) {
-  return scan_common(desc, ws, alpha, s_init, states, stream, 0);
-}
-
-int vda_scan_rev(const vda_desc* desc, const void* ws, const float* alpha, const float* s_init, float* states,
-                 void* stream) {
-  return scan_common(desc, ws, alpha, s_init, states, stream, 1);
-}
-
-int vda_readout(const vda_desc* desc, const void* q, const float* alpha, const float* states_fwd,
-                const float* states_rev, void* out, void* stream) {
-  Shape s;
+int read_args(const vda_desc* desc, const void* q, const float* alpha, const float* states_fwd,
+              const float* states_rev, void* out, Shape& s, vda::ReadArgs& a, bool& any) {
   int rc = check_desc(desc, &s);
   if (rc) return rc;
-  const bool any = (size_t)s.H * s.T * s.U > 0;
+  any = (size_t)s.H * s.T * s.U > 0;
   if (any && !out) return fail(VDA_ERR_NULL, "out is NULL");
   if (any && s.n > 0) {
     if (!q || !states_fwd) return fail(VDA_ERR_NULL, "q or states_fwd is NULL");
@@ -266,10 +250,6 @@ int vda_readout(const vda_desc* desc, const void* q, const float* alpha, const f
   }
   if (!aligned16(q) || !aligned16(alpha) || !aligned16(states_fwd) || !aligned16(states_rev) || !aligned16(out))
     return fail(VDA_ERR_ALIGN, "q, alpha, states, out need 16-byte alignment");
-  rc = check_device();
-  if (rc) return rc;
-  if (!any) return ok();
-  vda::ReadArgs a;
   a.q = q;
   a.alpha = alpha;
   a.sf = states_fwd;
@@ -285,7 +265,140 @@ int vda_readout(const vda_desc* desc, const void* q, const float* alpha, const f
   a.w = s.w;
   a.count = s.count;
   a.bridge = (desc->flags & VDA_NO_BRIDGE) ? 0 : 1;
+  return VDA_OK;
+}
+
+// Per-device side stream and event pool of vda_forward (created on first
+// use, default stream priority; kept until the process ends).
+struct Pipe {
+  bool ready = false;
+  hipStream_t side = nullptr;
+  hipEvent_t ev[32] = {};
+  std::mutex mu;
+};
+Pipe g_pipe[64];
+
+int pipe_for_current_device(Pipe** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return fail(VDA_ERR_DEVICE, "no HIP device");
+  Pipe& p = g_pipe[dev];
+  std::lock_guard<std::mutex> lock(p.mu);
+  if (!p.ready) {
+    if (hipStreamCreateWithFlags(&p.side, hipStreamNonBlocking) != hipSuccess)
+      return fail(VDA_ERR_HIP, "hipStreamCreateWithFlags failed");
+    for (auto& e : p.ev)
+      if (hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess)
+        return fail(VDA_ERR_HIP, "hipEventCreateWithFlags failed");
+    p.ready = true;
+  }
+  *out = &p;
+  return VDA_OK;
+}
+
+constexpr int kPrepGroups = 8;  // frame groups of the pipelined prepare
+
+}  // namespace
+
+extern "C" {
+
+int vda_prepare_frames(const vda_desc* desc, const void* k, const void* v, const float* beta,
+                       const void* k_text, const void* v_text, const float* beta_text, void* ws,
+                       size_t ws_size, void* stream) {
+  Shape s;
+  vda::PrepArgs a;
+  int rc = prep_args(desc, k, v, beta, k_text, v_text, beta_text, ws, ws_size, s, a);
+  if (rc) return rc;
+  rc = check_device();
+  if (rc) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  vda::launch_clear_status(a.status, st);
+  vda::launch_stats(a, s.d, desc->in_dtype == VDA_F32, st);
+  vda::launch_gj(a, s.d, st);
+  return launch_status();
+}
+
+int vda_scan_fwd(const vda_desc* desc, const void* ws, const float* alpha, const float* s_init, float* states,
+                 void* stream) {
+  Shape s;
+  vda::ScanArgs a;
+  int rc = scan_args(desc, ws, alpha, s_init, states, 0, s, a);
+  if (rc) return rc;
+  rc = check_device();
+  if (rc) return rc;
+  vda::launch_scan(a, s.d, static_cast<hipStream_t>(stream));
+  return launch_status();
+}
+
+int vda_scan_rev(const vda_desc* desc, const void* ws, const float* alpha, const float* s_init, float* states,
+                 void* stream) {
+  Shape s;
+  vda::ScanArgs a;
+  int rc = scan_args(desc, ws, alpha, s_init, states, 1, s, a);
+  if (rc) return rc;
+  rc = check_device();
+  if (rc) return rc;
+  vda::launch_scan(a, s.d, static_cast<hipStream_t>(stream));
+  return launch_status();
+}
+
+int vda_readout(const vda_desc* desc, const void* q, const float* alpha, const float* states_fwd,
+                const float* states_rev, void* out, void* stream) {
+  Shape s;
+  vda::ReadArgs a;
+  bool any = false;
+  int rc = read_args(desc, q, alpha, states_fwd, states_rev, out, s, a, any);
+  if (rc) return rc;
+  rc = check_device();
+  if (rc) return rc;
+  if (!any) return ok();
   vda::launch_readout(a, s.d, desc->in_dtype, desc->out_dtype, static_cast<hipStream_t>(stream));
+  return launch_status();
+}
+
+int vda_forward(const vda_desc* desc, const void* q, const void* k, const void* v, const float* beta,
+                const float* alpha, const void* k_text, const void* v_text, const float* beta_text, void* ws,
+                size_t ws_size, float* states_fwd, float* states_rev, void* out, void* stream) {
+  Shape s;
+  vda::PrepArgs pa;
+  vda::ScanArgs fa, ra;
+  vda::ReadArgs qa;
+  bool any = false;
+  int rc = prep_args(desc, k, v, beta, k_text, v_text, beta_text, ws, ws_size, s, pa);
+  if (rc) return rc;
+  const bool rev = states_rev != nullptr || s.w >= 0;
+  if ((rc = scan_args(desc, ws, alpha, nullptr, states_fwd, 0, s, fa))) return rc;
+  if (rev && (rc = scan_args(desc, ws, alpha, nullptr, states_rev, 1, s, ra))) return rc;
+  if ((rc = read_args(desc, q, alpha, states_fwd, states_rev, out, s, qa, any))) return rc;
+  if ((rc = check_device())) return rc;
+  Pipe* p = nullptr;
+  if ((rc = pipe_for_current_device(&p))) return rc;
+  std::lock_guard<std::mutex> lock(p->mu);
+  hipStream_t S = static_cast<hipStream_t>(stream), B = p->side;
+  int ne = 0;
+  bool err = false;
+  auto fork = [&](hipStream_t from, hipStream_t to) {  // `to` waits for `from`
+    err |= hipEventRecord(p->ev[ne], from) != hipSuccess;
+    err |= hipStreamWaitEvent(to, p->ev[ne], 0) != hipSuccess;
+    ++ne;
+  };
+  const bool f32 = desc->in_dtype == VDA_F32;
+  fork(S, B);
+  vda::launch_clear_status(pa.status, S);
+  // statistics of group g on S overlap the factorisation of group g - 1 on B
+  const int G = s.n_eff < kPrepGroups ? s.n_eff : kPrepGroups;
+  for (int g = 0; g < G; ++g) {
+    pa.s0 = (int)((long long)s.n_eff * g / G);
+    pa.cnt = (int)((long long)s.n_eff * (g + 1) / G) - pa.s0;
+    vda::launch_stats(pa, s.d, f32, S);
+    fork(S, B);
+    vda::launch_gj(pa, s.d, B);
+  }
+  fork(B, S);  // every factor is ready
+  if (rev) vda::launch_scan(ra, s.d, B);
+  vda::launch_scan(fa, s.d, S);
+  fork(B, S);  // reverse states are ready
+  if (any) vda::launch_readout(qa, s.d, desc->in_dtype, desc->out_dtype, S);
+  if (err) return fail(VDA_ERR_HIP, "hipEventRecord / hipStreamWaitEvent failed");
   return launch_status();
 }
 

@@ -15,6 +15,7 @@ struct PrepArgs {
   float* frames;  // workspace after the header: [H][n_eff][N | B]
   int* status;
   int H, T, U, a, n, n_eff, Nt;
+  int s0, cnt;    // frame slots [s0, s0 + cnt) of every head (slot n = text)
 };
 
 struct ScanArgs {
@@ -39,7 +40,8 @@ struct ReadArgs {
   int bridge;
 };
 
-int launch_prepare(const PrepArgs& a, int d, bool in_f32, hipStream_t stream);
+int launch_stats(const PrepArgs& a, int d, bool in_f32, hipStream_t stream);
+int launch_gj(const PrepArgs& a, int d, hipStream_t stream);
 void launch_clear_status(int* status, hipStream_t stream);
 int launch_scan(const ScanArgs& a, int d, hipStream_t stream);
 int launch_readout(const ReadArgs& a, int d, int in_dtype, int out_dtype, hipStream_t stream);

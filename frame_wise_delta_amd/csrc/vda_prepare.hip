@@ -76,31 +76,39 @@ struct Stage8<InF32> {
   }
 };
 
-// LDS layout of the factorisation phase (byte offsets).  E, R^T and r'^T are
-// double-buffered by step parity.
+// LDS layout of the factorisation phase (byte offsets).  E^{-1} and r'^T
+// are read by every wavefront after the step's barrier, so they are
+// double-buffered by step parity; R^T is read by its writer only.  Row
+// pitches are padded (24 bf16, 20 floats) so that the 16-byte operand reads
+// of 16 consecutive rows are free of LDS bank conflicts.
+constexpr int kTP = 24;  // bf16 row pitch of R^T / r'^T ([D][16] data)
+constexpr int kFP = 20;  // float row pitch of E^{-1} and the column strips ([16][16] data)
 template <int D>
 struct GjSmem {
-  static constexpr int kE = 0;                        // [16][16] f32
-  static constexpr int kRT = kE + 16 * 16 * 4;        // [D][16] bf16 hi, then lo
-  static constexpr int kRpT = kRT + 2 * D * 16 * 2;   // [D][16] bf16 hi, then lo
-  static constexpr int kPar = kRpT + 2 * D * 16 * 2;  // bytes per parity
-  static constexpr int kC = 2 * kPar;                 // [4 waves][NRW][16][16] f32
-  static constexpr int kBytes = kC + 4 * ((D / 16 + 3) / 4) * 256 * 4;
+  static constexpr int kRT = 0;                        // [D][kTP] bf16 hi, then lo
+  static constexpr int kPar0 = kRT + 2 * D * kTP * 2;  // parity buffers:
+  static constexpr int kE = 0;                         //   [16][kFP] f32 E^{-1}
+  static constexpr int kRpT = 16 * kFP * 4;            //   [D][kTP] bf16 hi, then lo
+  static constexpr int kPar = kRpT + 2 * D * kTP * 2;  //   bytes per parity
+  static constexpr int kC = kPar0 + 2 * kPar;          // [4 waves][NRW][16][kFP] f32
+  static constexpr int kBytes = kC + 4 * ((D / 16 + 3) / 4) * 16 * kFP * 4;
 };
 
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-// Lane k of every 16-lane row, broadcast to the whole row (DPP row_newbcast).
+// Lane K of every 16-lane row, broadcast to the whole row (DPP
+// row_newbcast; every lane is written, so the old value is irrelevant).
 template <int K>
 __device__ __forceinline__ float row_bcast(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x150 + K, 0xF, 0xF, false));
+  return __int_as_float(
+      __builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), 0x150 + K, 0xF, 0xF, true));
 }
 
 // One pivot of the scalar Gauss-Jordan inverse below.  With t = x[K] (this
 // row's pivot-column entry) and g = (t - [row is pivot row]) / pivot, every
 // column c != K becomes x[c] - g * pivotrow[c]: this is x[c] / pivot on the
-// pivot row and the usual elimination elsewhere, one FMA per entry.
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-
+// pivot row and the usual elimination elsewhere, one FMA per entry with the
+// pivot-row entry as a scalar operand.
 template <int K>
 __device__ __forceinline__ void gj_pivot(f32x16& x, int r, int& bad) {
   const float piv = row_bcast<K>(x[K]);
@@ -108,10 +116,14 @@ __device__ __forceinline__ void gj_pivot(f32x16& x, int r, int& bad) {
   const float inv = __builtin_amdgcn_rcpf(piv);  // v_rcp_f32, 1 ulp
   const float t = x[K];
   const bool prow = (r == K);
-  const float g = (prow ? t - 1.0f : t) * inv;
+  const float ng = -(prow ? t - 1.0f : t) * inv;
+  float pr[16];
 #pragma unroll
   for (int c = 0; c < 16; ++c)
-    if (c != K) x[c] = fmaf(-g, row_bcast<K>(x[c]), x[c]);
+    if (c != K) pr[c] = row_bcast<K>(x[c]);
+#pragma unroll
+  for (int c = 0; c < 16; ++c)
+    if (c != K) x[c] = fmaf(pr[c], ng, x[c]);
   x[K] = prow ? inv : -t * inv;
 }
 
@@ -121,7 +133,8 @@ __device__ __forceinline__ void invert16_impl(f32x16& x, int r, int& bad, std::i
 }
 
 // Scalar Gauss-Jordan inverse of a 16x16 matrix held one row per lane (lane
-// l of every 16-lane row holds row l % 16); the result has the same layout.
+// l holds row l % 16; the four 16-lane groups hold copies); the result has
+// the same layout.
 __device__ __forceinline__ void invert16(f32x16& x, int r, int& bad) {
   invert16_impl(x, r, bad, std::make_integer_sequence<int, 16>{});
 }
@@ -135,12 +148,18 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
 }  // namespace
 
+// Row pitch (floats) of the 64-row float32 staging buffers: d + 4 puts the
+// four 16-lane groups of an accumulator tile (rows 4 apart) on disjoint banks.
+template <int D>
+constexpr int kSP = D + 4;
+
 // Stage 64 rows of a wavefront-strip-distributed d x d float32 matrix
 // (accumulator layout) through LDS and store them row-major, coalesced.
 template <int D, int NRW>
 __device__ __forceinline__ void store_rows(const f32x4 (&acc)[NRW][D / 16], float* stage, float* dst,
                                            int tid, int wave, int lg, int lr) {
   constexpr int RT = D / 16;
+  constexpr int SP = kSP<D>;
 #pragma unroll
   for (int m = 0; m < NRW; ++m) {
     const int ri = wave + 4 * m;
@@ -148,13 +167,15 @@ __device__ __forceinline__ void store_rows(const f32x4 (&acc)[NRW][D / 16], floa
 #pragma unroll
       for (int cj = 0; cj < RT; ++cj)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) stage[(16 * wave + 4 * lg + e) * D + 16 * cj + lr] = acc[m][cj][e];
+        for (int e = 0; e < 4; ++e) stage[(16 * wave + 4 * lg + e) * SP + 16 * cj + lr] = acc[m][cj][e];
     }
     lds_barrier();
     const int rows = (D - 64 * m) < 64 ? (D - 64 * m) : 64;
     float* d = dst + (size_t)64 * m * D;
-    for (int i = tid; i < rows * D / 4; i += kThreads)
-      reinterpret_cast<float4*>(d)[i] = reinterpret_cast<const float4*>(stage)[i];
+    for (int i = tid; i < rows * D / 4; i += kThreads) {
+      const int r = i / (D / 4), c4 = i - r * (D / 4);
+      reinterpret_cast<float4*>(d)[i] = *reinterpret_cast<const float4*>(stage + r * SP + 4 * c4);
+    }
     lds_barrier();
   }
 }
@@ -165,15 +186,15 @@ __global__ __launch_bounds__(kThreads, 2) void stats_kernel(PrepArgs args) {
   constexpr int RT = D / 16;              // 16-row tiles
   constexpr int NRW = (RT + 3) / 4;       // row tiles per wavefront
   constexpr int kTile = D * kRound;       // halves per LDS token tile
-  constexpr int kBytes = (3 * kTile * 2 > 64 * D * 4) ? 3 * kTile * 2 : 64 * D * 4;
+  constexpr int kBytes = (3 * kTile * 2 > 64 * kSP<D> * 4) ? 3 * kTile * 2 : 64 * kSP<D> * 4;
   __shared__ __attribute__((aligned(16))) char smem[kBytes];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, lg = lane >> 4;
 
-  const int h = blockIdx.x / args.n_eff;
-  const int f = blockIdx.x - h * args.n_eff;
+  const int h = blockIdx.x / args.cnt;
+  const int f = args.s0 + (blockIdx.x - h * args.cnt);
   const bool text = f >= args.n;
   const int U = text ? args.Nt : args.U;
   const T* kp;
@@ -285,17 +306,21 @@ __global__ __launch_bounds__(kThreads, 2) void stats_kernel(PrepArgs args) {
 }
 
 template <int D>
-__global__ __launch_bounds__(kThreads, 3) void gj_kernel(PrepArgs args) {
+__global__ __launch_bounds__(kThreads, 4) void gj_kernel(PrepArgs args) {
   constexpr int RT = D / 16;
   constexpr int NRW = (RT + 3) / 4;
-  constexpr int kStage = 64 * D * 4;
+  constexpr int kStageA = 64 * kSP<D> * 4;        // float32 A rows
+  constexpr int kStageN = 2 * 64 * (D + 8) * 2;    // bf16 N hi and lo rows
+  constexpr int kStage = kStageA > kStageN ? kStageA : kStageN;
   constexpr int kBytes = GjSmem<D>::kBytes > kStage ? GjSmem<D>::kBytes : kStage;
   __shared__ __attribute__((aligned(16))) char smem[kBytes];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, lg = lane >> 4;
-  float* slot = args.frames + (size_t)blockIdx.x * ws_slot_floats(D);
+  const int h = blockIdx.x / args.cnt;
+  const int f = args.s0 + (blockIdx.x - h * args.cnt);
+  float* slot = args.frames + ((size_t)h * args.n_eff + f) * ws_slot_floats(D);
   int bad = 0;
 
   // ---- load A (row-major float32) into the accumulator layout, G = I + A
@@ -305,8 +330,10 @@ __global__ __launch_bounds__(kThreads, 3) void gj_kernel(PrepArgs args) {
   for (int m = 0; m < NRW; ++m) {
     const int rows = (D - 64 * m) < 64 ? (D - 64 * m) : 64;
     const float* src = slot + (size_t)64 * m * D;
-    for (int i = tid; i < rows * D / 4; i += kThreads)
-      reinterpret_cast<float4*>(stage)[i] = reinterpret_cast<const float4*>(src)[i];
+    for (int i = tid; i < rows * D / 4; i += kThreads) {
+      const int r = i / (D / 4), c4 = i - r * (D / 4);
+      *reinterpret_cast<float4*>(stage + r * kSP<D> + 4 * c4) = reinterpret_cast<const float4*>(src)[i];
+    }
     lds_barrier();
     const int ri = wave + 4 * m;
     if (ri < RT) {
@@ -314,7 +341,7 @@ __global__ __launch_bounds__(kThreads, 3) void gj_kernel(PrepArgs args) {
       for (int cj = 0; cj < RT; ++cj)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          float v = stage[(16 * wave + 4 * lg + e) * D + 16 * cj + lr];
+          float v = stage[(16 * wave + 4 * lg + e) * kSP<D> + 16 * cj + lr];
           if (cj == ri && 4 * lg + e == lr) v += 1.0f;
           accA[m][cj][e] = v;
         }
@@ -324,16 +351,16 @@ __global__ __launch_bounds__(kThreads, 3) void gj_kernel(PrepArgs args) {
 
   // ---- blocked Gauss-Jordan sweep
   char* gj = smem;
-  float* sCw = reinterpret_cast<float*>(gj + GjSmem<D>::kC) + wave * NRW * 256;
+  float* sCw = reinterpret_cast<float*>(gj + GjSmem<D>::kC) + wave * NRW * 16 * kFP;
   // fully unrolled: every accumulator index below is a compile-time constant
 #pragma unroll
   for (int p = 0; p < RT; ++p) {
-    char* par = gj + (p & 1) * GjSmem<D>::kPar;
-    float* sE = reinterpret_cast<float*>(par + GjSmem<D>::kE);  // E, then E^{-1}
-    __bf16* sRTh = reinterpret_cast<__bf16*>(par + GjSmem<D>::kRT);
-    __bf16* sRTl = sRTh + D * 16;
+    char* par = gj + GjSmem<D>::kPar0 + (p & 1) * GjSmem<D>::kPar;
+    float* sE = reinterpret_cast<float*>(par + GjSmem<D>::kE);  // E^{-1}
+    __bf16* sRTh = reinterpret_cast<__bf16*>(gj + GjSmem<D>::kRT);
+    __bf16* sRTl = sRTh + D * kTP;
     __bf16* sRpTh = reinterpret_cast<__bf16*>(par + GjSmem<D>::kRpT);
-    __bf16* sRpTl = sRpTh + D * 16;
+    __bf16* sRpTl = sRpTh + D * kTP;
     const bool owner = (p % 4) == wave;
     const int mp = p / 4;
 
@@ -353,15 +380,15 @@ __global__ __launch_bounds__(kThreads, 3) void gj_kernel(PrepArgs args) {
             hi[e] = hh;
             lo[e] = ll;
           }
-          *reinterpret_cast<bf16x4*>(sRTh + (16 * cj + lr) * 16 + 4 * lg) = hi;
-          *reinterpret_cast<bf16x4*>(sRTl + (16 * cj + lr) * 16 + 4 * lg) = lo;
+          *reinterpret_cast<bf16x4*>(sRTh + (16 * cj + lr) * kTP + 4 * lg) = hi;
+          *reinterpret_cast<bf16x4*>(sRTl + (16 * cj + lr) * kTP + 4 * lg) = lo;
         }
       }
 #pragma unroll
       for (int cj = 0; cj < RT; ++cj)
         if (cj == p) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) sCw[m * 256 + (4 * lg + e) * 16 + lr] = accA[m][cj][e];
+          for (int e = 0; e < 4; ++e) sCw[m * 16 * kFP + (4 * lg + e) * kFP + lr] = accA[m][cj][e];
         }
     }
 
@@ -370,14 +397,14 @@ __global__ __launch_bounds__(kThreads, 3) void gj_kernel(PrepArgs args) {
       f32x16 x;
 #pragma unroll
       for (int c = 0; c < 16; c += 4) {
-        const float4 v = *reinterpret_cast<const float4*>(sCw + mp * 256 + lr * 16 + c);
+        const float4 v = *reinterpret_cast<const float4*>(sCw + mp * 16 * kFP + lr * kFP + c);
         x[c] = v.x; x[c + 1] = v.y; x[c + 2] = v.z; x[c + 3] = v.w;
       }
       invert16(x, lr, bad);
       if (lg == 0) {
 #pragma unroll
         for (int c = 0; c < 16; c += 4)
-          *reinterpret_cast<float4*>(sE + lr * 16 + c) = make_float4(x[c], x[c + 1], x[c + 2], x[c + 3]);
+          *reinterpret_cast<float4*>(sE + lr * kFP + c) = make_float4(x[c], x[c + 1], x[c + 2], x[c + 3]);
       }
       bf16x8 aE;  // A operand [Einv_hi | Einv_lo] (row lr)
 #pragma unroll
@@ -386,23 +413,31 @@ __global__ __launch_bounds__(kThreads, 3) void gj_kernel(PrepArgs args) {
         split_bf16((lg & 1) ? x[8 + e] : x[e], hh, ll);
         aE[e] = lg < 2 ? hh : ll;
       }
+      // all operand reads, then all MFMAs, then the stores: the tiles overlap
+      bf16x8 rh[RT], rl[RT];
 #pragma unroll
       for (int cj = 0; cj < RT; ++cj) {
-        const bf16x8 rh = *reinterpret_cast<const bf16x8*>(sRTh + (16 * cj + lr) * 16 + 8 * (lg & 1));
-        const bf16x8 rl = *reinterpret_cast<const bf16x8*>(sRTl + (16 * cj + lr) * 16 + 8 * (lg & 1));
-        f32x4 rp = {0, 0, 0, 0};
-        rp = mfma_bf16(aE, rh, rp);
-        rp = mfma_bf16(aE, rl, rp);
+        rh[cj] = *reinterpret_cast<const bf16x8*>(sRTh + (16 * cj + lr) * kTP + 8 * (lg & 1));
+        rl[cj] = *reinterpret_cast<const bf16x8*>(sRTl + (16 * cj + lr) * kTP + 8 * (lg & 1));
+      }
+      f32x4 rp[RT];
+#pragma unroll
+      for (int cj = 0; cj < RT; ++cj) {
+        rp[cj] = mfma_bf16(aE, rh[cj], f32x4{0, 0, 0, 0});
+        rp[cj] = mfma_bf16(aE, rl[cj], rp[cj]);
+      }
+#pragma unroll
+      for (int cj = 0; cj < RT; ++cj) {
         bf16x4 hi, lo;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           __bf16 hh, ll;
-          split_bf16(rp[e], hh, ll);
+          split_bf16(rp[cj][e], hh, ll);
           hi[e] = hh;
           lo[e] = ll;
         }
-        *reinterpret_cast<bf16x4*>(sRpTh + (16 * cj + lr) * 16 + 4 * lg) = hi;
-        *reinterpret_cast<bf16x4*>(sRpTl + (16 * cj + lr) * 16 + 4 * lg) = lo;
+        *reinterpret_cast<bf16x4*>(sRpTh + (16 * cj + lr) * kTP + 4 * lg) = hi;
+        *reinterpret_cast<bf16x4*>(sRpTl + (16 * cj + lr) * kTP + 4 * lg) = lo;
 #pragma unroll
         for (int m = 0; m < NRW; ++m)
           if (m == mp) {
@@ -410,7 +445,7 @@ __global__ __launch_bounds__(kThreads, 3) void gj_kernel(PrepArgs args) {
 #pragma unroll
               for (int e = 0; e < 4; ++e) accA[m][cj][e] = pick4(x, lg, e);  // Einv[4lg+e][lr]
             } else {
-              accA[m][cj] = rp;
+              accA[m][cj] = rp[cj];
             }
           }
       }
@@ -420,8 +455,8 @@ __global__ __launch_bounds__(kThreads, 3) void gj_kernel(PrepArgs args) {
     // C. c' = -C E^{-1} and the rank-16 update G -= C r' outside the pivot strips
     bf16x8 eh, el;  // B operand rows of E^{-1} (E symmetric)
     {
-      const float4 v0 = *reinterpret_cast<const float4*>(sE + lr * 16 + 8 * (lg & 1));
-      const float4 v1 = *reinterpret_cast<const float4*>(sE + lr * 16 + 8 * (lg & 1) + 4);
+      const float4 v0 = *reinterpret_cast<const float4*>(sE + lr * kFP + 8 * (lg & 1));
+      const float4 v1 = *reinterpret_cast<const float4*>(sE + lr * kFP + 8 * (lg & 1) + 4);
       const float ev[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -439,7 +474,7 @@ __global__ __launch_bounds__(kThreads, 3) void gj_kernel(PrepArgs args) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           __bf16 hh, ll;
-          split_bf16(-sCw[m * 256 + lr * 16 + 8 * (lg & 1) + e], hh, ll);
+          split_bf16(-sCw[m * 16 * kFP + lr * kFP + 8 * (lg & 1) + e], hh, ll);
           aC[e] = lg < 2 ? hh : ll;
         }
         f32x4 cp = {0, 0, 0, 0};
@@ -450,8 +485,8 @@ __global__ __launch_bounds__(kThreads, 3) void gj_kernel(PrepArgs args) {
           if (cj == p) {
             accA[m][cj] = cp;
           } else {
-            const bf16x8 bh = *reinterpret_cast<const bf16x8*>(sRpTh + (16 * cj + lr) * 16 + 8 * (lg & 1));
-            const bf16x8 bl = *reinterpret_cast<const bf16x8*>(sRpTl + (16 * cj + lr) * 16 + 8 * (lg & 1));
+            const bf16x8 bh = *reinterpret_cast<const bf16x8*>(sRpTh + (16 * cj + lr) * kTP + 8 * (lg & 1));
+            const bf16x8 bl = *reinterpret_cast<const bf16x8*>(sRpTl + (16 * cj + lr) * kTP + 8 * (lg & 1));
             accA[m][cj] = mfma_bf16(aC, bh, accA[m][cj]);
             accA[m][cj] = mfma_bf16(aC, bl, accA[m][cj]);
           }
@@ -465,8 +500,9 @@ __global__ __launch_bounds__(kThreads, 3) void gj_kernel(PrepArgs args) {
   //      through LDS (overwrites A)
   // N is symmetric, so each pass stages rows [64m, 64m + 64) of N^T (columns
   // of N): every lane writes four consecutive row entries with one 8-byte store.
+  constexpr int NP = D + 8;  // bf16 row pitch of the staging (conflict-free 16-byte reads)
   __bf16* sh = reinterpret_cast<__bf16*>(smem);
-  __bf16* sl = sh + 64 * D;
+  __bf16* sl = sh + 64 * NP;
   __bf16* nhi = reinterpret_cast<__bf16*>(slot);
   __bf16* nlo = nhi + D * D;
 #pragma unroll
@@ -487,7 +523,7 @@ __global__ __launch_bounds__(kThreads, 3) void gj_kernel(PrepArgs args) {
             hi[e] = hh;
             lo[e] = ll;
           }
-          const int idx = (16 * (cj - 4 * m) + lr) * D + 16 * ri + 4 * lg;
+          const int idx = (16 * (cj - 4 * m) + lr) * NP + 16 * ri + 4 * lg;
           *reinterpret_cast<bf16x4*>(sh + idx) = hi;
           *reinterpret_cast<bf16x4*>(sl + idx) = lo;
         }
@@ -508,7 +544,7 @@ __global__ __launch_bounds__(kThreads, 3) void gj_kernel(PrepArgs args) {
       const int lgq = g % LG, t2 = g / LG;
       const int kk = t2 % KS, ct = t2 / KS;
       const int j = 16 * ct + lrq, c = 4 * kk + lgq;
-      const uint4 v = *reinterpret_cast<const uint4*>((which ? sl : sh) + (j - 64 * m) * D + 8 * c);
+      const uint4 v = *reinterpret_cast<const uint4*>((which ? sl : sh) + (j - 64 * m) * NP + 8 * c);
       reinterpret_cast<uint4*>(which ? nlo : nhi)[q] = v;
     }
     lds_barrier();
@@ -518,20 +554,32 @@ __global__ __launch_bounds__(kThreads, 3) void gj_kernel(PrepArgs args) {
 
 __global__ void clear_status_kernel(int* status) { *status = 0; }
 
-int launch_prepare(const PrepArgs& a, int d, bool in_f32, hipStream_t stream) {
-  if (a.H == 0 || a.n_eff == 0) return 0;
-  dim3 grid((unsigned)(a.H * a.n_eff)), block(kThreads);
-#define VDA_PREP(DD)                                                                  \
+int launch_stats(const PrepArgs& a, int d, bool in_f32, hipStream_t stream) {
+  if (a.H == 0 || a.cnt == 0) return 0;
+  dim3 grid((unsigned)(a.H * a.cnt)), block(kThreads);
+#define VDA_STATS(DD)                                                                 \
   if (d == DD) {                                                                      \
     if (in_f32)                                                                       \
       hipLaunchKernelGGL((stats_kernel<DD, InF32>), grid, block, 0, stream, a);       \
     else                                                                              \
       hipLaunchKernelGGL((stats_kernel<DD, InBF16>), grid, block, 0, stream, a);      \
+    return 0;                                                                         \
+  }
+  VDA_STATS(16) VDA_STATS(32) VDA_STATS(64) VDA_STATS(128)
+#undef VDA_STATS
+  return -1;
+}
+
+int launch_gj(const PrepArgs& a, int d, hipStream_t stream) {
+  if (a.H == 0 || a.cnt == 0) return 0;
+  dim3 grid((unsigned)(a.H * a.cnt)), block(kThreads);
+#define VDA_GJ(DD)                                                                    \
+  if (d == DD) {                                                                      \
     hipLaunchKernelGGL((gj_kernel<DD>), grid, block, 0, stream, a);                   \
     return 0;                                                                         \
   }
-  VDA_PREP(16) VDA_PREP(32) VDA_PREP(64) VDA_PREP(128)
-#undef VDA_PREP
+  VDA_GJ(16) VDA_GJ(32) VDA_GJ(64) VDA_GJ(128)
+#undef VDA_GJ
   return -1;
 }
 

@@ -70,8 +70,24 @@ def allocate(desc: vda.vda_desc, out_dtype: str, device="cuda") -> Buffers:
     return Buffers(ws=ws, ws_bytes=wsb, states_f=sf, states_r=sr, out=out)
 
 
+class Forward:
+    """Enqueues the whole hot path with one vda_forward call (the library
+    pipelines it over its own side stream)."""
+
+    def __init__(self, desc: vda.vda_desc, dev: DeviceInputs, bufs: Buffers):
+        import torch
+        self.desc, self.dev, self.bufs = desc, dev, bufs
+        self.main = torch.cuda.current_stream()
+
+    def enqueue(self):
+        d, x, b = self.desc, self.dev, self.bufs
+        vda.vda_forward(d, x.q, x.k, x.v, x.beta, x.alpha, x.kt, x.vt, x.bt, b.ws, b.states_f, b.states_r,
+                        b.out, ws_bytes=b.ws_bytes, stream=self.main)
+
+
 class Path:
-    """Enqueues the whole hot path; the two scans run on two streams."""
+    """Enqueues the whole hot path step by step; the two scans run on two
+    streams."""
 
     def __init__(self, desc: vda.vda_desc, dev: DeviceInputs, bufs: Buffers, s_init=None):
         import torch
@@ -93,13 +109,18 @@ class Path:
         vda.vda_readout(d, x.q, x.alpha, b.states_f, b.states_r, b.out, stream=self.main)
 
 
-def run(cfg: inp.Config, heads_in, device="cuda", s_init=None, **desc_over):
-    """Upload, run once, synchronise; return (desc, DeviceInputs, Buffers)."""
+def run(cfg: inp.Config, heads_in, device="cuda", s_init=None, fused=False, **desc_over):
+    """Upload, run once, synchronise; return (desc, DeviceInputs, Buffers).
+    fused=True runs the path through vda_forward (no explicit s_init)."""
     import torch
     desc = vda.desc_for(cfg, **desc_over)
     dev = upload(cfg, heads_in, device)
     bufs = allocate(desc, desc_over.get("out_dtype", cfg.out_dtype), device)
-    Path(desc, dev, bufs, s_init=s_init).enqueue()
+    if fused:
+        assert s_init is None
+        Forward(desc, dev, bufs).enqueue()
+    else:
+        Path(desc, dev, bufs, s_init=s_init).enqueue()
     torch.cuda.synchronize()
     return desc, dev, bufs
 

@@ -31,7 +31,7 @@ VDA_DEV_NONFINITE, VDA_DEV_PIVOT = 1, 2
 DTYPES = {"f32": VDA_F32, "bf16": VDA_BF16, "f16": VDA_F16}
 
 EXPORTS = ("vda_workspace_bytes", "vda_state_count", "vda_index_map", "vda_prepare_frames",
-           "vda_scan_fwd", "vda_scan_rev", "vda_readout", "vda_device_status",
+           "vda_scan_fwd", "vda_scan_rev", "vda_readout", "vda_forward", "vda_device_status",
            "vda_status_string", "vda_last_error")
 
 
@@ -73,6 +73,8 @@ def load(path: str | None = None):
         "vda_scan_fwd": [D, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p],
         "vda_scan_rev": [D, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p],
         "vda_readout": [D, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p],
+        "vda_forward": [D, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                        c_void_p, c_void_p, c_size_t, c_void_p, c_void_p, c_void_p, c_void_p],
         "vda_device_status": [D, c_void_p, c_void_p, POINTER(c_int32)],
     }
     for name, argt in sig.items():
@@ -174,6 +176,15 @@ def vda_scan_rev(desc, ws, alpha, s_init, states, stream=None):
 def vda_readout(desc, q, alpha, states_fwd, states_rev, out, stream=None):
     _check(load().vda_readout(ctypes.byref(desc), _ptr(q), _ptr(alpha), _ptr(states_fwd),
                               _ptr(states_rev), _ptr(out), _stream(stream)))
+
+
+def vda_forward(desc, q, k, v, beta, alpha, k_text, v_text, beta_text, ws, states_fwd, states_rev, out,
+                ws_bytes=None, stream=None):
+    if ws_bytes is None:
+        ws_bytes = ws.numel() * ws.element_size()
+    _check(load().vda_forward(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(alpha),
+                              _ptr(k_text), _ptr(v_text), _ptr(beta_text), _ptr(ws), ws_bytes,
+                              _ptr(states_fwd), _ptr(states_rev), _ptr(out), _stream(stream)))
 
 
 def vda_device_status(desc, ws, stream=None) -> int:

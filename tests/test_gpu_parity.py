@@ -29,10 +29,11 @@ def _scanned_rel(O, ref, cfg):
     return orc.rel_l2(O[sl], ref[sl])
 
 
-def _check(cfg, heads=None, tol_o=TOL_O, bridge=True, **over):
-    print(f"[parity] {cfg.name} H={cfg.heads} T={cfg.frames} U={cfg.tokens} d={cfg.d} {over}", flush=True)
+def _check(cfg, heads=None, tol_o=TOL_O, bridge=True, fused=False, **over):
+    print(f"[parity] {cfg.name} H={cfg.heads} T={cfg.frames} U={cfg.tokens} d={cfg.d} fused={fused} {over}",
+          flush=True)
     heads_in = inp.all_heads(cfg)
-    desc, dev, bufs = runner.run(cfg, heads_in, bridge=bridge, **over)
+    desc, dev, bufs = runner.run(cfg, heads_in, bridge=bridge, fused=fused, **over)
     O = runner.out_f64(bufs)
     sf = bufs.states_f.cpu().numpy()
     sr = bufs.states_r.cpu().numpy()
@@ -92,6 +93,23 @@ def test_tiny_config():
 
 def test_scan_only_config():
     _check(inp.CONFIG_BY_NAME["scan_only"])
+
+
+@pytest.mark.parametrize("name", ["tiny", "scan_only"])
+def test_fused_entry_point_matches_oracle(name):
+    _check(inp.CONFIG_BY_NAME[name], fused=True)
+
+
+def test_fused_entry_point_equals_step_by_step():
+    """vda_forward runs the same kernels as the four calls: identical bits."""
+    import torch
+    cfg = inp.scaled(inp.CONFIG_BY_NAME["h3"], heads=3, frames=32, tokens=300)
+    heads_in = inp.all_heads(cfg)
+    _, _, b1 = runner.run(cfg, heads_in)
+    _, _, b2 = runner.run(cfg, heads_in, fused=True)
+    assert torch.equal(b1.states_f, b2.states_f)
+    assert torch.equal(b1.states_r, b2.states_r)
+    assert torch.equal(b1.out.view(torch.int16), b2.out.view(torch.int16))
 
 
 def test_h3_shape_reduced_frames():
