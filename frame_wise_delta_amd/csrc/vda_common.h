@@ -27,6 +27,15 @@ __device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
 __device__ __forceinline__ f32x4 mfma_f16(f16x8 a, f16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
+// D(16x16) += A(16x16) * B(16x16), bf16 operands: lane l holds A row (l % 16)
+// and B column (l % 16) with k = 4*(l/16) .. 4*(l/16)+3, i.e. the same layout
+// as the result (rows 4*(l/16) .. 4*(l/16)+3 of column l % 16).
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ f32x4 mfma16_bf16(bf16x4 a, bf16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a), __builtin_bit_cast(s16x4, b),
+                                                    c, 0, 0, 0);
+}
 
 // Workgroup barrier that orders LDS traffic only: outstanding global loads
 // and stores stay in flight across it.
@@ -62,7 +71,10 @@ struct InBF16 { typedef u16 T; static constexpr int bytes = 2; };
 // then, per head h and frame slot f (f < n: scanned frame f; f == n: text),
 // N = (I + A)^{-1} as two d x d bf16 arrays N_hi, N_lo (N ~ N_hi + N_lo) in
 // MFMA fragment order (below), followed by B (d x d float32, row-major):
-// 8 d^2 bytes per slot.
+// 8 d^2 bytes per slot.  Between the two prepare kernels the N half holds
+// the upper-triangle 16x16 tiles of A (float32) in accumulator order: tile
+// (ri, cj), cj >= ri, lane l holds A[16ri + 4(l/16) + e][16cj + l % 16],
+// e = 0..3, as 16 bytes at float offset ((ri * d/16 + cj) * 64 + l) * 4.
 constexpr size_t kWsHeader = 256;
 
 __host__ __device__ inline size_t ws_slot_floats(int d) { return (size_t)2 * d * d; }

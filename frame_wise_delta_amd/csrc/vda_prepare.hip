@@ -5,8 +5,9 @@
 //   A = K^T Diag(beta) K  and  B = V^T Diag(beta) K
 // ("Video DeltaNet: A Video-Native Hybrid Attention for Livestream Video
 // Generation", method-steps section, step (3)) on MFMA with float32
-// accumulation and stores both in the frame's workspace slot (A in the place
-// N will take).  K, V rows are streamed from HBM in 64-token rounds, converted
+// accumulation, and stores B (row-major) and the upper-triangle tiles of A
+// (accumulator layout, in the place N will take) in the frame's workspace
+// slot.  K, V rows are streamed from HBM in 64-token rounds, converted
 // to f16 (beta*K is rounded once to f16) and written channel-major into LDS
 // so that an MFMA operand lane reads eight consecutive tokens of one channel
 // with a single 16-byte LDS load.  The 16-byte token groups of each LDS row
@@ -14,22 +15,13 @@
 // are free of bank conflicts.  The next round's global loads are issued
 // before the current round's MFMAs.
 //
-// gj_kernel: inverts G = I + A in registers with a blocked Gauss-Jordan
-// sweep and overwrites A with N = G^{-1} as a bf16 hi/lo pair in the MFMA
-// fragment order the scan consumes.  The 16-row strips of G stay in MFMA
-// accumulators spread over the four wavefronts.  Block step p (16 pivot
-// columns):
-//   * the owner of strip p inverts the 16x16 pivot block E with a scalar
-//     Gauss-Jordan, one matrix row per lane, the pivot row broadcast by DPP
-//     row_newbcast, and forms r' = E^{-1} R on MFMA;
-//   * every other strip forms c' = -C E^{-1} on MFMA and applies the rank-16
-//     update G -= C r'.
-// MFMA products use bf16 hi/lo splits of both factors (four partial
-// products), accurate to about 2^-16 relative.  G is symmetric positive
-// definite (eigenvalues >= 1), so no pivoting is needed; a pivot <= 0 or a
-// non-finite value sets a bit of the device status word.  Splitting the two
-// phases lets the latency-bound sweep run at a higher occupancy than the
-// bandwidth-bound statistics.
+// gj_kernel: one wavefront per frame inverts G = I + A in registers with a
+// blocked Gauss-Jordan sweep (16x16 blocks on MFMA, scalar 16x16 pivot-block
+// inverses) and overwrites A with N = G^{-1} as a bf16 hi/lo pair in the MFMA
+// fragment order the scan consumes.  G is symmetric positive definite
+// (eigenvalues >= 1), so no pivoting is needed.  Running the latency-bound
+// sweep as single-wavefront workgroups, apart from the bandwidth-bound
+// statistics, lets every SIMD work on its own matrices without barriers.
 #include <utility>
 
 #include "vda_common.h"
@@ -76,25 +68,7 @@ struct Stage8<InF32> {
   }
 };
 
-// LDS layout of the factorisation phase (byte offsets).  E^{-1} and r'^T
-// are read by every wavefront after the step's barrier, so they are
-// double-buffered by step parity; R^T is read by its writer only.  Row
-// pitches are padded (24 bf16, 20 floats) so that the 16-byte operand reads
-// of 16 consecutive rows are free of LDS bank conflicts.
-constexpr int kTP = 24;  // bf16 row pitch of R^T / r'^T ([D][16] data)
-constexpr int kFP = 20;  // float row pitch of E^{-1} and the column strips ([16][16] data)
-template <int D>
-struct GjSmem {
-  static constexpr int kRT = 0;                        // [D][kTP] bf16 hi, then lo
-  static constexpr int kPar0 = kRT + 2 * D * kTP * 2;  // parity buffers:
-  static constexpr int kE = 0;                         //   [16][kFP] f32 E^{-1}
-  static constexpr int kRpT = 16 * kFP * 4;            //   [D][kTP] bf16 hi, then lo
-  static constexpr int kPar = kRpT + 2 * D * kTP * 2;  //   bytes per parity
-  static constexpr int kC = kPar0 + 2 * kPar;          // [4 waves][NRW][16][kFP] f32
-  static constexpr int kBytes = kC + 4 * ((D / 16 + 3) / 4) * 16 * kFP * 4;
-};
-
-typedef float f32x16 __attribute__((ext_vector_type(16)));
+// ---- helpers of the factorisation --------------------------------------
 
 // Lane K of every 16-lane row, broadcast to the whole row (DPP
 // row_newbcast; every lane is written, so the old value is irrelevant).
@@ -104,47 +78,98 @@ __device__ __forceinline__ float row_bcast(float v) {
       __builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), 0x150 + K, 0xF, 0xF, true));
 }
 
-// One pivot of the scalar Gauss-Jordan inverse below.  With t = x[K] (this
-// row's pivot-column entry) and g = (t - [row is pivot row]) / pivot, every
-// column c != K becomes x[c] - g * pivotrow[c]: this is x[c] / pivot on the
-// pivot row and the usual elimination elsewhere, one FMA per entry with the
-// pivot-row entry as a scalar operand.
+// Row R (lanes 16R .. 16R+15) of v, broadcast to all four 16-lane rows: lane
+// l gets v of lane 16R + l % 16.  permlane16_swap(v, v) yields the rows
+// (0,0,2,2) and (1,1,3,3); permlane32_swap(u, u) yields (0,1,0,1) and (2,3,2,3).
+template <int R>
+__device__ __forceinline__ float group_bcast(float v) {
+  const unsigned b = __float_as_uint(v);
+  const auto s16 = __builtin_amdgcn_permlane16_swap(b, b, false, false);
+  const unsigned u = (R & 1) ? s16[1] : s16[0];
+  const auto s32 = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __uint_as_float((R & 2) ? s32[1] : s32[0]);
+}
+
+// One pivot of the in-place Gauss-Jordan inverse of a 16x16 matrix W held
+// four columns per lane: lane (n, g) = (l % 16, l / 16) holds W[n][4g .. 4g+3].
+// With t = W[n][K] and g' = (t - [n == K]) / W[K][K], every column c != K
+// becomes W[n][c] - g' W[K][c] (this is W[K][c] / W[K][K] on the pivot row
+// and the usual elimination elsewhere), and column K becomes 1 / W[K][K] on
+// the pivot row and -t / W[K][K] elsewhere.
 template <int K>
-__device__ __forceinline__ void gj_pivot(f32x16& x, int r, int& bad) {
-  const float piv = row_bcast<K>(x[K]);
+__device__ __forceinline__ void gj_pivot(f32x4& y, int n, int g, int& bad) {
+  constexpr int KG = K >> 2, KE = K & 3;
+  const float t = group_bcast<KG>(y[KE]);  // W[n][K]
+  const float piv = row_bcast<K>(t);       // W[K][K]
   if (!(piv > 0.f) || !__builtin_isfinite(piv)) bad |= VDA_DEV_PIVOT;
   const float inv = __builtin_amdgcn_rcpf(piv);  // v_rcp_f32, 1 ulp
-  const float t = x[K];
-  const bool prow = (r == K);
+  const bool prow = n == K;
   const float ng = -(prow ? t - 1.0f : t) * inv;
-  float pr[16];
+  float pr[4];
 #pragma unroll
-  for (int c = 0; c < 16; ++c)
-    if (c != K) pr[c] = row_bcast<K>(x[c]);
+  for (int e = 0; e < 4; ++e) pr[e] = row_bcast<K>(y[e]);  // W[K][4g + e]
 #pragma unroll
-  for (int c = 0; c < 16; ++c)
-    if (c != K) x[c] = fmaf(pr[c], ng, x[c]);
-  x[K] = prow ? inv : -t * inv;
+  for (int e = 0; e < 4; ++e) y[e] = fmaf(pr[e], ng, y[e]);
+  const float colk = prow ? inv : -t * inv;
+  y[KE] = g == KG ? colk : y[KE];
 }
 
 template <int... Ks>
-__device__ __forceinline__ void invert16_impl(f32x16& x, int r, int& bad, std::integer_sequence<int, Ks...>) {
-  (gj_pivot<Ks>(x, r, bad), ...);
+__device__ __forceinline__ void invert16_impl(f32x4& y, int n, int g, int& bad, std::integer_sequence<int, Ks...>) {
+  (gj_pivot<Ks>(y, n, g, bad), ...);
 }
 
-// Scalar Gauss-Jordan inverse of a 16x16 matrix held one row per lane (lane
-// l holds row l % 16; the four 16-lane groups hold copies); the result has
-// the same layout.
-__device__ __forceinline__ void invert16(f32x16& x, int r, int& bad) {
-  invert16_impl(x, r, bad, std::make_integer_sequence<int, 16>{});
-}
-
-__device__ __forceinline__ float pick4(const f32x16& x, int grp, int e) {
-  // x[4 * grp + e] for a lane-dependent grp in 0..3
-  return grp == 0 ? x[e] : grp == 1 ? x[4 + e] : grp == 2 ? x[8 + e] : x[12 + e];
+// In-place inverse of the 16x16 matrix W held four columns per lane (above).
+__device__ __forceinline__ void invert16(f32x4& y, int n, int g, int& bad) {
+  invert16_impl(y, n, g, bad, std::make_integer_sequence<int, 16>{});
 }
 
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+
+// bf16 pair with v ~ hi + lo: hi is v truncated to bf16 (exact upper half
+// of the float32 word), lo = v - hi (exact) rounded to bf16, so hi + lo
+// holds v to about 2^-16 relative.
+__device__ __forceinline__ void split4(f32x4 v, bf16x4& hi, bf16x4& lo) {
+  uint32_t w[4];
+  f32x4 r;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    w[e] = __float_as_uint(v[e]);
+    r[e] = v[e] - __uint_as_float(w[e] & 0xffff0000u);
+  }
+  uint2 h;
+  h.x = __builtin_amdgcn_perm(w[1], w[0], 0x07060302u);  // upper halves of w0 (low) and w1 (high)
+  h.y = __builtin_amdgcn_perm(w[3], w[2], 0x07060302u);
+  hi = __builtin_bit_cast(bf16x4, h);
+  lo = __builtin_convertvector(r, bf16x4);
+}
+
+__device__ __forceinline__ bf16x8 cat8(bf16x4 a, bf16x4 b) {
+  return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+__device__ __forceinline__ bf16x8 neg8(bf16x8 a) {
+  uint4 u = __builtin_bit_cast(uint4, a);
+  u.x ^= 0x80008000u; u.y ^= 0x80008000u; u.z ^= 0x80008000u; u.w ^= 0x80008000u;
+  return __builtin_bit_cast(bf16x8, u);
+}
+
+// Index of the upper-triangle tile pair {i, j}, i <= j, of a RT x RT grid.
+__host__ __device__ constexpr int upair(int RT, int i, int j) { return i * RT - i * (i - 1) / 2 + (j - i); }
+
+// 16x16 float32 transposes through LDS, for accumulator-layout tiles (lane
+// (n, g) holds Z[4g + e][n]).  put stores Z^T row-major; get returns the
+// accumulator layout of Z^T.  The 20-float pitch keeps both conflict-free.
+constexpr int kXP = 20;
+__device__ __forceinline__ void tr_put(float* buf, f32x4 v, int n, int g) {
+  *reinterpret_cast<f32x4*>(buf + n * kXP + 4 * g) = v;
+}
+__device__ __forceinline__ f32x4 tr_get(const float* buf, int n, int g) {
+  f32x4 r;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) r[e] = buf[(4 * g + e) * kXP + n];
+  return r;
+}
 
 }  // namespace
 
@@ -299,255 +324,156 @@ __global__ __launch_bounds__(kThreads, 2) void stats_kernel(PrepArgs args) {
       for (int e = 0; e < 4; ++e)
         if (!__builtin_isfinite(accA[m][cj][e]) || !__builtin_isfinite(accB[m][cj][e])) bad |= VDA_DEV_NONFINITE;
   float* slot = args.frames + ((size_t)h * args.n_eff + f) * ws_slot_floats(D);
+  // A where N will go: the upper-triangle tiles, straight from the accumulators
+#pragma unroll
+  for (int m = 0; m < NRW; ++m) {
+    const int ri = wave + 4 * m;
+    if (ri < RT) {
+#pragma unroll
+      for (int cj = 0; cj < RT; ++cj)
+        if (cj >= ri) *reinterpret_cast<f32x4*>(slot + ((size_t)(ri * RT + cj) * 64 + lane) * 4) = accA[m][cj];
+    }
+  }
   float* stage = reinterpret_cast<float*>(smem);
-  store_rows<D, NRW>(accA, stage, slot, tid, wave, lg, lr);          // A where N will go
   store_rows<D, NRW>(accB, stage, slot + D * D, tid, wave, lg, lr);  // B
   if (bad) atomicOr(args.status, bad);
 }
 
+// One wavefront inverts one G = I + A.  G is symmetric, so only the pairs
+// {i, j}, i <= j, of 16x16 tiles are kept, each once, in MFMA accumulators
+// (lane (n, g) holds rows 4g .. 4g+3 of column n of the tile).  In-place
+// Gauss-Jordan over the blocks P processed so far keeps the working matrix M
+// symmetric within P and within the rest Q, and antisymmetric between them
+// (M[i][j] = -M[j][i]^T for i in P, j in Q), so either tile of a pair gives
+// the other.  A pair {i, j}, i < j, is held as M[i][j] until step j and as
+// M[j][i] from then on: at step p every pair {j, p} is held as M[p][j], the
+// row strip R_j of the pivot (the pairs {j, p}, j < p, are transposed through
+// LDS at the start of step p).  Step p:
+//   E = M[p][p] -> E^{-1}, scalar Gauss-Jordan, four columns per lane;
+//   r'_j = E^{-1} R_j on MFMA, the new M[p][j] (the new column strip follows
+//          by the symmetry above and is never formed);
+//   every other pair, held as M[x][y]: M[x][y] -= M[x][p] r'_y, where the
+//          operand M[x][p] comes from R_x (= +R_x^T for x > p and -R_x^T
+//          for x < p).
+// An accumulator tile Z used as the MFMA A operand is Z^T and as the B operand
+// Z itself, so every product above reads the tiles in place.  Products use
+// bf16 hi/lo splits of both factors; the K = 32 MFMA forms (a_hi + a_lo) b in
+// one instruction by pairing the hi and lo halves of one factor with two
+// copies of one half of the other, so a four-term product takes two MFMAs.
+// The pivot block is read as E^T (equal to E) and E^{-1} is used as its own
+// transpose.  A pivot <= 0 or a non-finite value sets a bit of the device
+// status word.
 template <int D>
-__global__ __launch_bounds__(kThreads, 4) void gj_kernel(PrepArgs args) {
+__global__ __launch_bounds__(64, 2) void gj_kernel(PrepArgs args) {
   constexpr int RT = D / 16;
-  constexpr int NRW = (RT + 3) / 4;
-  constexpr int kStageA = 64 * kSP<D> * 4;        // float32 A rows
-  constexpr int kStageN = 2 * 64 * (D + 8) * 2;    // bf16 N hi and lo rows
-  constexpr int kStage = kStageA > kStageN ? kStageA : kStageN;
-  constexpr int kBytes = GjSmem<D>::kBytes > kStage ? GjSmem<D>::kBytes : kStage;
-  __shared__ __attribute__((aligned(16))) char smem[kBytes];
+  constexpr int NPR = RT * (RT + 1) / 2;
+  constexpr int NB = RT > 1 ? RT - 1 : 1;  // transpose buffers
+  __shared__ __attribute__((aligned(16))) float sT[NB][16 * kXP];
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int lr = lane & 15, lg = lane >> 4;
+  const int lane = threadIdx.x;
+  const int n = lane & 15, g = lane >> 4;
   const int h = blockIdx.x / args.cnt;
   const int f = args.s0 + (blockIdx.x - h * args.cnt);
   float* slot = args.frames + ((size_t)h * args.n_eff + f) * ws_slot_floats(D);
   int bad = 0;
 
-  // ---- load A (row-major float32) into the accumulator layout, G = I + A
-  f32x4 accA[NRW][RT];
-  float* stage = reinterpret_cast<float*>(smem);
+  // ---- G = I + A from the upper-triangle tiles of A (accumulator layout)
+  f32x4 G[NPR];
 #pragma unroll
-  for (int m = 0; m < NRW; ++m) {
-    const int rows = (D - 64 * m) < 64 ? (D - 64 * m) : 64;
-    const float* src = slot + (size_t)64 * m * D;
-    for (int i = tid; i < rows * D / 4; i += kThreads) {
-      const int r = i / (D / 4), c4 = i - r * (D / 4);
-      *reinterpret_cast<float4*>(stage + r * kSP<D> + 4 * c4) = reinterpret_cast<const float4*>(src)[i];
-    }
-    lds_barrier();
-    const int ri = wave + 4 * m;
-    if (ri < RT) {
+  for (int i = 0; i < RT; ++i)
 #pragma unroll
-      for (int cj = 0; cj < RT; ++cj)
+    for (int j = i; j < RT; ++j)
+      G[upair(RT, i, j)] = *reinterpret_cast<const f32x4*>(slot + ((size_t)(i * RT + j) * 64 + lane) * 4);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          float v = stage[(16 * wave + 4 * lg + e) * kSP<D> + 16 * cj + lr];
-          if (cj == ri && 4 * lg + e == lr) v += 1.0f;
-          accA[m][cj][e] = v;
-        }
-    }
-    lds_barrier();
-  }
+  for (int i = 0; i < RT; ++i)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) G[upair(RT, i, i)][e] += (4 * g + e == n) ? 1.0f : 0.0f;
 
-  // ---- blocked Gauss-Jordan sweep
-  char* gj = smem;
-  float* sCw = reinterpret_cast<float*>(gj + GjSmem<D>::kC) + wave * NRW * 16 * kFP;
-  // fully unrolled: every accumulator index below is a compile-time constant
+  // ---- blocked Gauss-Jordan, fully unrolled (every tile index is constant)
 #pragma unroll
   for (int p = 0; p < RT; ++p) {
-    char* par = gj + GjSmem<D>::kPar0 + (p & 1) * GjSmem<D>::kPar;
-    float* sE = reinterpret_cast<float*>(par + GjSmem<D>::kE);  // E^{-1}
-    __bf16* sRTh = reinterpret_cast<__bf16*>(gj + GjSmem<D>::kRT);
-    __bf16* sRTl = sRTh + D * kTP;
-    __bf16* sRpTh = reinterpret_cast<__bf16*>(par + GjSmem<D>::kRpT);
-    __bf16* sRpTl = sRpTh + D * kTP;
-    const bool owner = (p % 4) == wave;
-    const int mp = p / 4;
-
-    // A. owner publishes R^T (hi/lo); every wave stages its column strip
+    if (p > 0) {  // pairs {j, p}, j < p: M[j][p] -> M[p][j] = -M[j][p]^T
 #pragma unroll
-    for (int m = 0; m < NRW; ++m) {
-      const int ri = wave + 4 * m;
-      if (ri >= RT) continue;
-      if (ri == p) {
+      for (int j = 0; j < p; ++j) tr_put(sT[j], G[upair(RT, j, p)], n, g);
+      lds_barrier();
 #pragma unroll
-        for (int cj = 0; cj < RT; ++cj) {
-          bf16x4 hi, lo;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            __bf16 hh, ll;
-            split_bf16(accA[m][cj][e], hh, ll);
-            hi[e] = hh;
-            lo[e] = ll;
-          }
-          *reinterpret_cast<bf16x4*>(sRTh + (16 * cj + lr) * kTP + 4 * lg) = hi;
-          *reinterpret_cast<bf16x4*>(sRTl + (16 * cj + lr) * kTP + 4 * lg) = lo;
-        }
-      }
-#pragma unroll
-      for (int cj = 0; cj < RT; ++cj)
-        if (cj == p) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) sCw[m * 16 * kFP + (4 * lg + e) * kFP + lr] = accA[m][cj][e];
-        }
+      for (int j = 0; j < p; ++j) G[upair(RT, j, p)] = -tr_get(sT[j], n, g);
+      lds_barrier();
     }
-
-    // B. owner: E^{-1} (scalar Gauss-Jordan, row lr per lane), r' = E^{-1} R
-    if (owner) {
-      f32x16 x;
-#pragma unroll
-      for (int c = 0; c < 16; c += 4) {
-        const float4 v = *reinterpret_cast<const float4*>(sCw + mp * 16 * kFP + lr * kFP + c);
-        x[c] = v.x; x[c + 1] = v.y; x[c + 2] = v.z; x[c + 3] = v.w;
-      }
-      invert16(x, lr, bad);
-      if (lg == 0) {
-#pragma unroll
-        for (int c = 0; c < 16; c += 4)
-          *reinterpret_cast<float4*>(sE + lr * kFP + c) = make_float4(x[c], x[c + 1], x[c + 2], x[c + 3]);
-      }
-      bf16x8 aE;  // A operand [Einv_hi | Einv_lo] (row lr)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        __bf16 hh, ll;
-        split_bf16((lg & 1) ? x[8 + e] : x[e], hh, ll);
-        aE[e] = lg < 2 ? hh : ll;
-      }
-      // all operand reads, then all MFMAs, then the stores: the tiles overlap
-      bf16x8 rh[RT], rl[RT];
-#pragma unroll
-      for (int cj = 0; cj < RT; ++cj) {
-        rh[cj] = *reinterpret_cast<const bf16x8*>(sRTh + (16 * cj + lr) * kTP + 8 * (lg & 1));
-        rl[cj] = *reinterpret_cast<const bf16x8*>(sRTl + (16 * cj + lr) * kTP + 8 * (lg & 1));
-      }
-      f32x4 rp[RT];
-#pragma unroll
-      for (int cj = 0; cj < RT; ++cj) {
-        rp[cj] = mfma_bf16(aE, rh[cj], f32x4{0, 0, 0, 0});
-        rp[cj] = mfma_bf16(aE, rl[cj], rp[cj]);
-      }
-#pragma unroll
-      for (int cj = 0; cj < RT; ++cj) {
-        bf16x4 hi, lo;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          __bf16 hh, ll;
-          split_bf16(rp[cj][e], hh, ll);
-          hi[e] = hh;
-          lo[e] = ll;
-        }
-        *reinterpret_cast<bf16x4*>(sRpTh + (16 * cj + lr) * kTP + 4 * lg) = hi;
-        *reinterpret_cast<bf16x4*>(sRpTl + (16 * cj + lr) * kTP + 4 * lg) = lo;
-#pragma unroll
-        for (int m = 0; m < NRW; ++m)
-          if (m == mp) {
-            if (cj == p) {
-#pragma unroll
-              for (int e = 0; e < 4; ++e) accA[m][cj][e] = pick4(x, lg, e);  // Einv[4lg+e][lr]
-            } else {
-              accA[m][cj] = rp[cj];
-            }
-          }
-      }
-    }
-    lds_barrier();
-
-    // C. c' = -C E^{-1} and the rank-16 update G -= C r' outside the pivot strips
-    bf16x8 eh, el;  // B operand rows of E^{-1} (E symmetric)
+    f32x4 y = G[upair(RT, p, p)];
+    invert16(y, n, g, bad);
+    G[upair(RT, p, p)] = y;
+    bf16x8 e_hh, e_ll;  // A operands [Einv_hi | Einv_hi], [Einv_lo | Einv_lo]
     {
-      const float4 v0 = *reinterpret_cast<const float4*>(sE + lr * kFP + 8 * (lg & 1));
-      const float4 v1 = *reinterpret_cast<const float4*>(sE + lr * kFP + 8 * (lg & 1) + 4);
-      const float ev[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        __bf16 hh, ll;
-        split_bf16(ev[e], hh, ll);
-        eh[e] = hh;
-        el[e] = ll;
-      }
+      bf16x4 hi, lo;
+      split4(y, hi, lo);
+      e_hh = cat8(hi, hi);
+      e_ll = cat8(lo, lo);
     }
+    bf16x8 xr[RT];  // [R_hi | R_lo] of the row strip
 #pragma unroll
-    for (int m = 0; m < NRW; ++m) {
-      const int ri = wave + 4 * m;
-      if (ri < RT && ri != p) {
-        bf16x8 aC;  // A operand [-C_hi | -C_lo]
+    for (int j = 0; j < RT; ++j)
+      if (j != p) {
+        bf16x4 hi, lo;
+        split4(G[upair(RT, j < p ? j : p, j < p ? p : j)], hi, lo);
+        xr[j] = cat8(hi, lo);
+      }
+    // r'_j, then every pair held as M[x][j]: for j > p the pairs {a, j}
+    // (held as M[a][j]), for j < p the pairs {j, b}, b < p (held as M[b][j])
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          __bf16 hh, ll;
-          split_bf16(-sCw[m * 16 * kFP + lr * kFP + 8 * (lg & 1) + e], hh, ll);
-          aC[e] = lg < 2 ? hh : ll;
-        }
-        f32x4 cp = {0, 0, 0, 0};
-        cp = mfma_bf16(aC, eh, cp);
-        cp = mfma_bf16(aC, el, cp);
+    for (int j = 0; j < RT; ++j)
+      if (j != p) {
+        f32x4 r = mfma_bf16(e_hh, xr[j], f32x4{0, 0, 0, 0});
+        r = mfma_bf16(e_ll, xr[j], r);
+        G[upair(RT, j < p ? j : p, j < p ? p : j)] = r;
+        bf16x4 hi, lo;
+        split4(r, hi, lo);
+        const bf16x8 b_hh = cat8(hi, hi), b_ll = cat8(lo, lo);  // B operands of r'_j
+        const bf16x8 n_hh = neg8(b_hh), n_ll = neg8(b_ll);
 #pragma unroll
-        for (int cj = 0; cj < RT; ++cj) {
-          if (cj == p) {
-            accA[m][cj] = cp;
-          } else {
-            const bf16x8 bh = *reinterpret_cast<const bf16x8*>(sRpTh + (16 * cj + lr) * kTP + 8 * (lg & 1));
-            const bf16x8 bl = *reinterpret_cast<const bf16x8*>(sRpTl + (16 * cj + lr) * kTP + 8 * (lg & 1));
-            accA[m][cj] = mfma_bf16(aC, bh, accA[m][cj]);
-            accA[m][cj] = mfma_bf16(aC, bl, accA[m][cj]);
-          }
+        for (int x = 0; x < RT; ++x) {
+          const bool held = j > p ? (x <= j && x != p) : (x >= j && x < p);
+          if (!held) continue;
+          const int t = upair(RT, x < j ? x : j, x < j ? j : x);
+          // M[x][j] -= M[x][p] r'_j with M[x][p] = -R_x^T (x < p), +R_x^T (x > p)
+          f32x4 acc = G[t];
+          acc = mfma_bf16(xr[x], x > p ? n_hh : b_hh, acc);
+          acc = mfma_bf16(xr[x], x > p ? n_ll : b_ll, acc);
+          G[t] = acc;
         }
       }
-    }
   }
-  lds_barrier();
 
-  // ---- N -> workspace as bf16 hi/lo in fragment order, 64 rows at a time
-  //      through LDS (overwrites A)
-  // N is symmetric, so each pass stages rows [64m, 64m + 64) of N^T (columns
-  // of N): every lane writes four consecutive row entries with one 8-byte store.
-  constexpr int NP = D + 8;  // bf16 row pitch of the staging (conflict-free 16-byte reads)
-  __bf16* sh = reinterpret_cast<__bf16*>(smem);
-  __bf16* sl = sh + 64 * NP;
+  // ---- N = G^{-1} -> workspace as bf16 hi/lo in fragment order.  Pair
+  //      {i, j}, i < j, is held as N[j][i]; N[i][j] is its transpose.  An
+  //      accumulator tile N[x][y] covers column 16y + n, rows 16x + 4g + e,
+  //      i.e. half of the 16-byte chunk (16y + n, 2x + g/2).
   __bf16* nhi = reinterpret_cast<__bf16*>(slot);
   __bf16* nlo = nhi + D * D;
+  auto put = [&](f32x4 v, int x, int yy) {
 #pragma unroll
-  for (int m = 0; m < NRW; ++m) {
+    for (int e = 0; e < 4; ++e)
+      if (!__builtin_isfinite(v[e])) bad |= VDA_DEV_NONFINITE;
+    bf16x4 hi, lo;
+    split4(v, hi, lo);
+    const size_t off = (size_t)ntile_chunk(D, 16 * yy + n, 2 * x + (g >> 1)) * 8 + 4 * (g & 1);
+    *reinterpret_cast<bf16x4*>(nhi + off) = hi;
+    *reinterpret_cast<bf16x4*>(nlo + off) = lo;
+  };
 #pragma unroll
-    for (int mm = 0; mm < NRW; ++mm) {
-      const int ri = wave + 4 * mm;
-      if (ri < RT) {
+  for (int j = 0; j < RT; ++j) {
+    put(G[upair(RT, j, j)], j, j);
 #pragma unroll
-        for (int cj = 4 * m; cj < RT && cj < 4 * m + 4; ++cj) {
-          bf16x4 hi, lo;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float v = accA[mm][cj][e];
-            if (!__builtin_isfinite(v)) bad |= VDA_DEV_NONFINITE;
-            __bf16 hh, ll;
-            split_bf16(v, hh, ll);
-            hi[e] = hh;
-            lo[e] = ll;
-          }
-          const int idx = (16 * (cj - 4 * m) + lr) * NP + 16 * ri + 4 * lg;
-          *reinterpret_cast<bf16x4*>(sh + idx) = hi;
-          *reinterpret_cast<bf16x4*>(sl + idx) = lo;
-        }
-      }
+    for (int i = 0; i < j; ++i) {
+      put(G[upair(RT, i, j)], j, i);
+      tr_put(sT[i], G[upair(RT, i, j)], n, g);
     }
-    lds_barrier();
-    // rows [64m, 64m + rows) are whole 16-column tiles, i.e. a contiguous
-    // range of fragment-order chunks starting at ntile_chunk(D, 64m, 0)
-    const int rows = (D - 64 * m) < 64 ? (D - 64 * m) : 64;
-    const int n16 = rows * D / 8;  // 16-byte chunks per array
-    const int base = ntile_chunk(D, 64 * m, 0);
-    for (int i = tid; i < 2 * n16; i += kThreads) {
-      const int which = i >= n16;
-      const int q = base + (i - which * n16);  // destination chunk
-      constexpr int KS = D >= 32 ? D / 32 : 1;
-      constexpr int LG = D >= 32 ? 4 : D / 8;
-      const int lrq = q & 15, g = q >> 4;
-      const int lgq = g % LG, t2 = g / LG;
-      const int kk = t2 % KS, ct = t2 / KS;
-      const int j = 16 * ct + lrq, c = 4 * kk + lgq;
-      const uint4 v = *reinterpret_cast<const uint4*>((which ? sl : sh) + (j - 64 * m) * NP + 8 * c);
-      reinterpret_cast<uint4*>(which ? nlo : nhi)[q] = v;
+    if (j > 0) {
+      lds_barrier();
+#pragma unroll
+      for (int i = 0; i < j; ++i) put(tr_get(sT[i], n, g), i, j);
+      lds_barrier();
     }
-    lds_barrier();
   }
   if (bad) atomicOr(args.status, bad);
 }
@@ -572,7 +498,7 @@ int launch_stats(const PrepArgs& a, int d, bool in_f32, hipStream_t stream) {
 
 int launch_gj(const PrepArgs& a, int d, hipStream_t stream) {
   if (a.H == 0 || a.cnt == 0) return 0;
-  dim3 grid((unsigned)(a.H * a.cnt)), block(kThreads);
+  dim3 grid((unsigned)(a.H * a.cnt)), block(64);
 #define VDA_GJ(DD)                                                                    \
   if (d == DD) {                                                                      \
     hipLaunchKernelGGL((gj_kernel<DD>), grid, block, 0, stream, a);                   \
