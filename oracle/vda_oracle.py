@@ -28,7 +28,7 @@ the section heading of that page:
 * [VDN 方法步骤详情 step (5)]        window-boundary states are carried to the
   query through the decay bridge prod(alpha_r).
 
-Readings of points the page leaves open (listed in the design doc as well):
+Readings of points the page leaves open:
 
 * S^T is one joint write of all text tokens into a zero state with no decay.
 * "By halves": each scan starts from ``text_init_scale * S^T`` (default 1/2)
