@@ -270,10 +270,11 @@ int read_args(const vda_desc* desc, const void* q, const float* alpha, const flo
 
 // Per-device side stream and event pool of vda_forward (created on first
 // use, default stream priority; kept until the process ends).
+constexpr int kEvents = 8;
 struct Pipe {
   bool ready = false;
-  hipStream_t side = nullptr;
-  hipEvent_t ev[32] = {};
+  hipStream_t side = nullptr;  // reverse scan
+  hipEvent_t ev[kEvents] = {};
   std::mutex mu;
 };
 Pipe g_pipe[64];
@@ -294,8 +295,6 @@ int pipe_for_current_device(Pipe** out) {
   *out = &p;
   return VDA_OK;
 }
-
-constexpr int kPrepGroups = 8;  // frame groups of the pipelined prepare
 
 }  // namespace
 
@@ -373,30 +372,31 @@ int vda_forward(const vda_desc* desc, const void* q, const void* k, const void* 
   Pipe* p = nullptr;
   if ((rc = pipe_for_current_device(&p))) return rc;
   std::lock_guard<std::mutex> lock(p->mu);
-  hipStream_t S = static_cast<hipStream_t>(stream), B = p->side;
+  hipStream_t S = static_cast<hipStream_t>(stream), R = p->side;
   int ne = 0;
   bool err = false;
-  auto fork = [&](hipStream_t from, hipStream_t to) {  // `to` waits for `from`
+  auto fork = [&](hipStream_t from, hipStream_t to) {  // `to` waits for the work enqueued on `from`
+    if (ne >= kEvents) {
+      err = true;
+      return;
+    }
     err |= hipEventRecord(p->ev[ne], from) != hipSuccess;
     err |= hipStreamWaitEvent(to, p->ev[ne], 0) != hipSuccess;
     ++ne;
   };
+  // The scans are bound by the latency of their per-frame operand loads, so
+  // they run only beside each other: statistics and factors on S, then the
+  // reverse scan on R and the forward scan on S, then the readout on S.
   const bool f32 = desc->in_dtype == VDA_F32;
-  fork(S, B);
   vda::launch_clear_status(pa.status, S);
-  // statistics of group g on S overlap the factorisation of group g - 1 on B
-  const int G = s.n_eff < kPrepGroups ? s.n_eff : kPrepGroups;
-  for (int g = 0; g < G; ++g) {
-    pa.s0 = (int)((long long)s.n_eff * g / G);
-    pa.cnt = (int)((long long)s.n_eff * (g + 1) / G) - pa.s0;
-    vda::launch_stats(pa, s.d, f32, S);
-    fork(S, B);
-    vda::launch_gj(pa, s.d, B);
+  vda::launch_stats(pa, s.d, f32, S);
+  vda::launch_gj(pa, s.d, S);
+  if (rev) {
+    fork(S, R);
+    vda::launch_scan(ra, s.d, R);
   }
-  fork(B, S);  // every factor is ready
-  if (rev) vda::launch_scan(ra, s.d, B);
   vda::launch_scan(fa, s.d, S);
-  fork(B, S);  // reverse states are ready
+  if (rev) fork(R, S);
   if (any) vda::launch_readout(qa, s.d, desc->in_dtype, desc->out_dtype, S);
   if (err) return fail(VDA_ERR_HIP, "hipEventRecord / hipStreamWaitEvent failed");
   return launch_status();

@@ -158,15 +158,13 @@ int vda_readout(const vda_desc* desc, const void* q, const float* alpha, const f
 /* The whole path in one call: vda_prepare_frames, vda_scan_fwd and
  * vda_scan_rev (S_init = S^T from the text tokens, or zero) and vda_readout,
  * with the same arguments, layouts and results as those calls made in that
- * order on `stream`.  Internally the work is pipelined over groups of
- * frames on two further HIP streams of the current device (created on first
- * use, default priority, kept until the process ends): the factorisation of
- * one group overlaps the statistics of the next, and the two scans run
- * concurrently.  All of it is ordered after the work already enqueued on
- * `stream`, and work enqueued on `stream` afterwards is ordered after all of
- * it.  Calls from several host threads are serialised while they enqueue.
- * states_rev may be NULL when window == -1 (the reverse scan is then
- * skipped). */
+ * order on `stream`.  The reverse scan runs on a further HIP stream of the
+ * current device (created on first use, default priority, kept until the
+ * process ends), concurrently with the forward scan.  All of it is ordered
+ * after the work already enqueued on `stream`, and work enqueued on `stream`
+ * afterwards is ordered after all of it.  Calls from several host threads
+ * are serialised while they enqueue.  states_rev may be NULL when
+ * window == -1 (the reverse scan is then skipped). */
 int vda_forward(const vda_desc* desc, const void* q, const void* k, const void* v, const float* beta,
                 const float* alpha, const void* k_text, const void* v_text, const float* beta_text,
                 void* ws, size_t ws_bytes, float* states_fwd, float* states_rev, void* out,

@@ -112,6 +112,45 @@ def test_fused_entry_point_equals_step_by_step():
     assert torch.equal(b1.out.view(torch.int16), b2.out.view(torch.int16))
 
 
+@pytest.mark.parametrize("frames,d,window,text,anchors", [
+    (32, 64, 1, 16, 1),    # C = 6: three prepare groups from each end
+    (27, 32, 1, 16, 1),    # C = 5: odd, the reverse half is one chunk shorter
+    (7, 32, 1, 16, 1),     # C = 1
+    (42, 128, 2, 0, 1),    # C = 8, wide window, no text
+    (30, 64, 0, 16, 0),    # window = own chunk only, no anchors
+    (23, 64, -1, 16, 0),   # per-frame readout, ragged group sizes
+])
+def test_fused_schedule_equals_step_by_step(frames, d, window, text, anchors):
+    """vda_forward (the reverse scan on its own stream) gives the same bits
+    as the four calls in order, over chunk counts, windows, text and anchor
+    settings."""
+    import torch
+    cfg = inp.scaled(inp.CONFIG_BY_NAME["h3"], heads=3, d=d, frames=frames, tokens=64, window=window,
+                     text_tokens=text, anchors=anchors)
+    print(f"[parity] fused schedule T={frames} d={d} w={window} text={text} anchors={anchors}", flush=True)
+    heads_in = inp.all_heads(cfg)
+    _, _, b1 = runner.run(cfg, heads_in)
+    _, _, b2 = runner.run(cfg, heads_in, fused=True)
+    assert torch.equal(b1.states_f, b2.states_f)
+    assert torch.equal(b1.states_r, b2.states_r)
+    assert torch.equal(b1.out.view(torch.int16), b2.out.view(torch.int16))
+
+
+def test_fused_without_reverse_states():
+    """window = -1 with states_rev = NULL: the reverse scan is skipped."""
+    import torch
+    cfg = inp.scaled(inp.CONFIG_BY_NAME["scan_only"], heads=2, frames=13, tokens=40)
+    heads_in = inp.all_heads(cfg)
+    _, dev, b1 = runner.run(cfg, heads_in)
+    desc = vda.desc_for(cfg)
+    b2 = runner.allocate(desc, cfg.out_dtype, "cuda")
+    vda.vda_forward(desc, dev.q, dev.k, dev.v, dev.beta, dev.alpha, None, None, None, b2.ws, b2.states_f,
+                    None, b2.out, ws_bytes=b2.ws_bytes)
+    torch.cuda.synchronize()
+    assert torch.equal(b1.states_f, b2.states_f)
+    assert torch.equal(b1.out.view(torch.int16), b2.out.view(torch.int16))
+
+
 def test_h3_shape_reduced_frames():
     """H3 frame shape (U = 1008, d = 128, 512 text tokens), 2 heads, 4 chunks."""
     cfg = inp.scaled(inp.CONFIG_BY_NAME["h3"], heads=2, frames=22)
