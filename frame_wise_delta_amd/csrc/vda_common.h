@@ -37,6 +37,20 @@ __device__ __forceinline__ f32x4 mfma16_bf16(bf16x4 a, bf16x4 b, f32x4 c) {
                                                     c, 0, 0, 0);
 }
 
+// Workgroups are dispatched round-robin over the 8 XCDs (block b runs on XCD
+// b % 8), each with its own L2.  xcd_block maps b to a logical index that
+// numbers the blocks of XCD 0 first, then those of XCD 1, and so on, so that
+// consecutive logical blocks (which share data) run on one XCD.  It is a
+// bijection on [0, nb) for any nb.
+__device__ __forceinline__ int xcd_block(int b, int nb) {
+  const int x = b & 7, j = b >> 3;
+  int first = 0;  // logical index of the first block of XCD x
+#pragma unroll
+  for (int i = 0; i < 7; ++i)
+    if (i < x) first += (nb - i + 7) >> 3;
+  return first + j;
+}
+
 // Workgroup barrier that orders LDS traffic only: outstanding global loads
 // and stores stay in flight across it.
 __device__ __forceinline__ void lds_barrier() {

@@ -13,8 +13,12 @@
 // per frame, so the token GEMM runs once.  With no window exclusion the
 // readout is O_t = Q_t (S^f_t)^T.  Anchor frames get zero rows.
 //
-// One workgroup per (head, frame).  Wavefront w owns value-channel tiles
-// w, w+4, ... and keeps its rows of W_t in registers as bf16 hi/lo pairs;
+// One workgroup per (head, frame), ordered so that the frames of one head
+// run on one XCD.  Wavefront w owns value-channel tiles
+// w, w+4, ... (for d = 128: the two tiles of wavefront w interleave channels
+// 32w .. 32w+31 so that each lane stores 8 consecutive channels of a token
+// with one 16-byte store) and keeps its rows of W_t in registers as bf16
+// hi/lo pairs;
 // 128-token tiles of Q are staged in LDS with one coalesced pass (the next
 // tile's loads are issued before the current tile's MFMAs) and each
 // wavefront computes O^T = W Q^T on MFMA (2 products per tile for bf16 Q,
@@ -37,6 +41,10 @@ struct OutT<VDA_F32> {
   static __device__ __forceinline__ void store4(void* base, size_t idx, f32x4 v) {
     *reinterpret_cast<float4*>(static_cast<float*>(base) + idx) = make_float4(v[0], v[1], v[2], v[3]);
   }
+  static __device__ __forceinline__ void store8(void* base, size_t idx, f32x4 v, f32x4 w) {
+    store4(base, idx, v);
+    store4(base, idx + 4, w);
+  }
   static constexpr int bytes = 4;
 };
 template <>
@@ -44,6 +52,11 @@ struct OutT<VDA_BF16> {
   static __device__ __forceinline__ void store4(void* base, size_t idx, f32x4 v) {
     bf16x4 b = {(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
     *reinterpret_cast<bf16x4*>(static_cast<u16*>(base) + idx) = b;
+  }
+  static __device__ __forceinline__ void store8(void* base, size_t idx, f32x4 v, f32x4 w) {
+    bf16x8 b = {(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3],
+                (__bf16)w[0], (__bf16)w[1], (__bf16)w[2], (__bf16)w[3]};
+    *reinterpret_cast<bf16x8*>(static_cast<u16*>(base) + idx) = b;
   }
   static constexpr int bytes = 2;
 };
@@ -53,6 +66,12 @@ struct OutT<VDA_F16> {
     typedef _Float16 h4 __attribute__((ext_vector_type(4)));
     h4 p = {(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
     *reinterpret_cast<h4*>(static_cast<_Float16*>(base) + idx) = p;
+  }
+  static __device__ __forceinline__ void store8(void* base, size_t idx, f32x4 v, f32x4 w) {
+    typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+    h8 p = {(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3],
+            (_Float16)w[0], (_Float16)w[1], (_Float16)w[2], (_Float16)w[3]};
+    *reinterpret_cast<h8*>(static_cast<_Float16*>(base) + idx) = p;
   }
   static constexpr int bytes = 2;
 };
@@ -98,13 +117,22 @@ __global__ __launch_bounds__(kThreads, 2) void readout_kernel(ReadArgs a) {
   constexpr int PITCH = D * TIN::bytes + 16;         // LDS bytes per token row
   constexpr int CH = D * TIN::bytes / 16;            // 16-byte chunks per token row
   constexpr int PER = (kQT * CH + kThreads - 1) / kThreads;  // chunks per thread per tile
+  // d = 128: the two tiles of wavefront w interleave its 32 value channels so
+  // that a lane's outputs of one token are 8 consecutive channels
+  constexpr bool kPair = VT == 8;
+  auto chan = [](int w, int i, int r) {
+    return kPair ? 32 * w + 8 * (r >> 2) + 4 * i + (r & 3) : 16 * (w + 4 * i) + r;
+  };
   __shared__ __attribute__((aligned(16))) char sQ[kQT * PITCH];
   __shared__ float sBf[D], sBr[D];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, lg = lane >> 4;
-  const int h = blockIdx.x / a.T;
-  const int t = blockIdx.x - h * a.T;
+  // the frames of one head run on one XCD: its L2 keeps the states that
+  // the frames of a chunk and its neighbours share
+  const int L = xcd_block(blockIdx.x, gridDim.x);
+  const int h = L / a.T;
+  const int t = L - h * a.T;
   const size_t frame_off = ((size_t)h * a.T + t) * (size_t)a.U * D;
 
   if (t < a.a || t >= a.T - a.a) {  // anchor frame: zero rows
@@ -179,7 +207,7 @@ __global__ __launch_bounds__(kThreads, 2) void readout_kernel(ReadArgs a) {
       const int k0 = 32 * kk + 8 * lg;
       float x[8];
       if (vt < VT && k0 < D) {
-        const size_t idx = (size_t)(16 * vt + lr) * D + k0;
+        const size_t idx = (size_t)chan(wave, i, lr) * D + k0;
         const float4 f0 = *reinterpret_cast<const float4*>(sf + idx);
         const float4 f1 = *reinterpret_cast<const float4*>(sf + idx + 4);
         x[0] = f0.x * sBf[k0]; x[1] = f0.y * sBf[k0 + 1]; x[2] = f0.z * sBf[k0 + 2]; x[3] = f0.w * sBf[k0 + 3];
@@ -241,10 +269,14 @@ __global__ __launch_bounds__(kThreads, 2) void readout_kernel(ReadArgs a) {
         }
         const int u = u0 + ul;
         if (u < a.U) {
+          if constexpr (kPair) {
+            OutT<OUT>::store8(a.out, frame_off + (size_t)u * D + 32 * wave + 8 * lg, acc[0], acc[1]);
+          } else {
 #pragma unroll
-          for (int i = 0; i < NVT; ++i) {
-            const int vt = wave + 4 * i;
-            if (vt < VT) OutT<OUT>::store4(a.out, frame_off + (size_t)u * D + 16 * vt + 4 * lg, acc[i]);
+            for (int i = 0; i < NVT; ++i) {
+              const int vt = wave + 4 * i;
+              if (vt < VT) OutT<OUT>::store4(a.out, frame_off + (size_t)u * D + 16 * vt + 4 * lg, acc[i]);
+            }
           }
         }
       }

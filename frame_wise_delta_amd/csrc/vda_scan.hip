@@ -64,7 +64,7 @@ __global__ __launch_bounds__(ScanShape<D>::NT) void scan_kernel(ScanArgs a) {
   constexpr int RB = D / ROWS;  // row blocks per head
   const int nb = gridDim.x;
   const int b = blockIdx.x;
-  const int L = (nb % 8 == 0) ? (b % 8) * (nb / 8) + b / 8 : b;  // XCD-aware order
+  const int L = xcd_block(b, nb);  // the row blocks of a head share an XCD
   const int h = L / RB;
   const int r0 = ROWS * (L - h * RB);
   // elementwise phase: thread owns columns xc0..xc0+3 of rows xrow + 16 q
