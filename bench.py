@@ -1,22 +1,34 @@
 """Benchmark of the VDA linear-branch hot path on one MI355X.
 
-One step = the whole path for one layer of the H3-shaped workload (24 heads,
-d = 128, 102 latent frames of which 2 are anchors, U = 1008 tokens per frame,
-512 text tokens, bf16 inputs, float32 state, bf16 output):
+One step = the whole path for one attention layer of the H3-shaped workload
+(24 heads, d = 128, 102 latent frames of which 2 are anchors, U = 1008
+tokens per frame, 512 text tokens, bf16 inputs, float32 state, bf16 output):
 
-    vda_prepare_frames -> vda_scan_fwd || vda_scan_rev -> vda_readout
+    vda_frame_stats -> vda_factor_frames -> vda_scan_fwd || vda_scan_rev
+        -> vda_readout
 
-Inputs are seeded synthetic draws (frame_wise_delta_amd.inputs) resident in
-HBM before timing starts.  Prints one JSON line: latent frames/s (value),
-algorithmic TFLOP/s and the fraction of the bf16 MFMA peak, a roofline entry
-for the dominant kernel timed with HIP events on its own stream, and the
-float64 oracle timed on this host's cores on the same inputs.
+(the same kernels, in the same order, as one vda_forward call).  Inputs are
+seeded synthetic draws (frame_wise_delta_amd.inputs) resident in HBM before
+timing starts.  Prints one JSON line: latent frames/s, algorithmic TFLOP/s,
+a roofline entry for the dominant HBM-bound kernel timed with HIP events on
+the stream it runs on, and the float64 oracle timed on this host's cores.
 
     python bench.py [--steps K] [--warmup W] [--config h3] [--no-cpu-baseline]
+
+Measurement helpers (used to make the files under profiles/):
+
+    python bench.py --copy-calibration
+        copies a 512 MiB device buffer three times (a plain copy of known
+        size, profiled with rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE)
+    python bench.py --traffic FETCH.csv WRITE.csv COPY_FETCH.csv COPY_WRITE.csv
+        turns the four rocprofv3 counter_collection files into
+        profiles/traffic.json: HBM bytes per launch of each kernel, with both
+        counters scaled by the factor that maps the copy's counts to its size
 """
 from __future__ import annotations
 
 import argparse
+import csv
 import hashlib
 import json
 import os
@@ -30,6 +42,8 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16/f16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+COPY_BYTES = 512 * 1024 * 1024
+KERNELS = ("stats_kernel", "gj_kernel", "scan_kernel", "readout_kernel")
 
 
 def algorithmic_work(cfg):
@@ -50,13 +64,16 @@ def algorithmic_work(cfg):
 
 
 def kernel_bytes(cfg):
-    """Algorithmic HBM bytes of one launch of each kernel."""
+    """Algorithmic HBM bytes of one launch of the two HBM-bound kernels:
+    statistics read K, V (16-bit) and beta of every scanned frame and the
+    text tokens; the readout reads Q and alpha of every scanned frame and
+    writes every output row (anchor rows are zeros)."""
     U, d, n, H, Nt, T = cfg.tokens, cfg.d, cfg.scanned, cfg.heads, cfg.text_tokens, cfg.frames
     ib = 4 if cfg.in_dtype == "f32" else 2
     ob = {"f32": 4, "bf16": 2, "f16": 2}[cfg.out_dtype]
-    prep = H * (n * (2 * U * d * ib + 4 * U) + (2 * Nt * d * ib + 4 * Nt))
-    read = H * n * (U * d * ib + U * d * ob + 4 * d)
-    return {"prepare": prep, "readout": read}
+    stats = H * (n * (2 * U * d * ib + 4 * U) + (2 * Nt * d * ib + 4 * Nt))
+    read = H * (n * (U * d * ib + 4 * d) + T * U * d * ob)
+    return {"stats_kernel": stats, "readout_kernel": read}
 
 
 def _src_hash():
@@ -68,12 +85,14 @@ def _src_hash():
     return h.hexdigest()[:16]
 
 
+TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
+
+
 def _traffic(kernel):
-    """HBM traffic per launch measured with rocprofv3 counters (committed
-    under profiles/), or None if the kernels changed since."""
-    p = os.path.join(ROOT, "profiles", "traffic.json")
+    """HBM bytes per launch measured with rocprofv3 counters (profiles/
+    traffic.json), or None if the kernel sources changed since."""
     try:
-        with open(p) as f:
+        with open(TRAFFIC_JSON) as f:
             t = json.load(f)
     except OSError:
         return None
@@ -83,6 +102,99 @@ def _traffic(kernel):
     return None if k is None else k.get("bytes_per_launch")
 
 
+# ------------------------------------------------------------- helpers --
+
+def copy_calibration():
+    import torch
+    x = torch.ones(COPY_BYTES // 4, device="cuda")
+    y = torch.empty_like(x)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": COPY_BYTES, "copies": 3}))
+
+
+def _short(name):
+    for k in KERNELS:
+        if k in name:
+            return k
+    return None
+
+
+def _counter_means(path, counter):
+    """Mean counter value (KiB) per dispatch of each kernel in a
+    counter_collection file; for the copy, only the copy dispatches."""
+    sums, counts = {}, {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] != counter:
+                continue
+            name = r["Kernel_Name"]
+            key = _short(name) or ("copy" if "copyBuffer" in name else None)
+            if key is None:
+                continue
+            sums[key] = sums.get(key, 0.0) + float(r["Counter_Value"])
+            counts[key] = counts.get(key, 0) + 1
+    return {k: sums[k] / counts[k] for k in sums}
+
+
+def write_traffic(fetch_csv, write_csv, cal_fetch_csv, cal_write_csv):
+    f = _counter_means(fetch_csv, "FETCH_SIZE")
+    w = _counter_means(write_csv, "WRITE_SIZE")
+    cf = _counter_means(cal_fetch_csv, "FETCH_SIZE")["copy"]
+    cw = _counter_means(cal_write_csv, "WRITE_SIZE")["copy"]
+    ff = COPY_BYTES / (cf * 1024.0)
+    wf = COPY_BYTES / (cw * 1024.0)
+    out = {"src_hash": _src_hash(),
+           "calibration": {"copy_bytes": COPY_BYTES, "fetch_kib": cf, "write_kib": cw,
+                           "fetch_factor": round(ff, 4), "write_factor": round(wf, 4)},
+           "kernels": {}}
+    for k in KERNELS:
+        if k in f and k in w:
+            fb, wb = f[k] * 1024.0 * ff, w[k] * 1024.0 * wf
+            out["kernels"][k] = {"fetch_bytes": round(fb), "write_bytes": round(wb),
+                                 "bytes_per_launch": round(fb + wb)}
+    os.makedirs(os.path.dirname(TRAFFIC_JSON), exist_ok=True)
+    with open(TRAFFIC_JSON, "w") as fh:
+        json.dump(out, fh, indent=1)
+    print(json.dumps(out))
+
+
+# ---------------------------------------------------------------- bench --
+
+def cpu_baseline(cfg, heads_in, out0, budget_s=15.0):
+    """The float64 oracle, as it stands, on whole heads of the same workload
+    until about budget_s seconds of CPU time are spent (at least one head)."""
+    from oracle import vda_oracle as orc
+    try:
+        from threadpoolctl import threadpool_info
+        info = threadpool_info()
+        cores = max(x.get("num_threads", 1) for x in info) if info else 1
+    except Exception:
+        cores = len(os.sched_getaffinity(0))
+    text = cfg.text_tokens > 0
+    t_cpu, done, rel = 0.0, 0, None
+    for h in range(cfg.heads):
+        f = heads_in[h].f64
+        args = [f(x) for x in ("q", "k", "v", "beta", "alpha")] + [f(x) if text else None for x in ("kt", "vt", "bt")]
+        c0 = time.perf_counter()
+        ref = orc.run_head(cfg.frames, cfg.chunk, cfg.window, cfg.anchors, *args)
+        t_cpu += time.perf_counter() - c0
+        done += 1
+        if h == 0:
+            sl = slice(cfg.anchors, cfg.frames - cfg.anchors)
+            rel = orc.rel_l2(out0[sl], ref["O"][sl])
+        if t_cpu >= budget_s:
+            break
+    frac = done / cfg.heads
+    return ({"value": round(cfg.frames * frac / t_cpu, 4), "unit": "frames/s", "cores": int(cores),
+             "kind": "oracle",
+             "sample": f"{done} of {cfg.heads} heads of the same workload (all {cfg.frames} frames of each), "
+                       f"float64 NumPy/LAPACK, {t_cpu:.1f} s; frames/s scaled by the fraction of heads"},
+            rel)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -90,14 +202,22 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="h3")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-heads", type=int, default=None,
-                    help="heads the oracle runs for the CPU baseline (default: all)")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="CPU time budget of the oracle baseline (whole heads)")
+    ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--traffic", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"))
     args = ap.parse_args()
+    if args.traffic:
+        write_traffic(*args.traffic)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (--gpus {args.gpus} requested): the VDA path is "
               "built and measured on a single MI355X; heads would shard across GPUs with no "
               "communication, which this build does not run.", file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
 
     import torch
     from frame_wise_delta_amd import inputs as inp
@@ -106,48 +226,46 @@ def main():
     cfg = inp.CONFIG_BY_NAME[args.config]
     t0 = time.time()
     heads_in = inp.all_heads(cfg)
-    t_gen = time.time() - t0
-    print(f"[bench] inputs for {cfg.name} drawn in {t_gen:.1f}s", file=sys.stderr, flush=True)
+    print(f"[bench] inputs for {cfg.name} drawn in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
     desc = vda.desc_for(cfg)
     dev = runner.upload(cfg, heads_in, "cuda")
     bufs = runner.allocate(desc, cfg.out_dtype, "cuda")
-    path = runner.Path(desc, dev, bufs)
-    main_s, side_s = path.main, path.side
+    main_s = torch.cuda.current_stream()
+    side_s = torch.cuda.Stream()
+    ev_fact, ev_rev = torch.cuda.Event(), torch.cuda.Event()
 
-    # events around each kernel, on the stream it runs on
-    names = ["prepare", "scan_fwd", "scan_rev", "readout"]
+    # events around each call, on the stream it runs on
+    names = ["stats", "factor", "scan_fwd", "scan_rev", "readout"]
     ev = {k: [] for k in names}
 
     def step(record):
-        pairs = {}
-        if record:
-            for k in names:
-                pairs[k] = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
         x, b = dev, bufs
-        if record:
-            pairs["prepare"][0].record(main_s)
-        vda.vda_prepare_frames(desc, x.k, x.v, x.beta, x.kt, x.vt, x.bt, b.ws, b.ws_bytes, stream=main_s)
-        if record:
-            pairs["prepare"][1].record(main_s)
-        path.ev_prep.record(main_s)
-        side_s.wait_event(path.ev_prep)
-        if record:
-            pairs["scan_rev"][0].record(side_s)
+        pairs = {k: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                 for k in names} if record else None
+
+        def mark(k, i, stream):
+            if record:
+                pairs[k][i].record(stream)
+        mark("stats", 0, main_s)
+        vda.vda_frame_stats(desc, x.k, x.v, x.beta, x.kt, x.vt, x.bt, b.ws, b.ws_bytes, stream=main_s)
+        mark("stats", 1, main_s)
+        mark("factor", 0, main_s)
+        vda.vda_factor_frames(desc, b.ws, b.ws_bytes, stream=main_s)
+        mark("factor", 1, main_s)
+        ev_fact.record(main_s)
+        side_s.wait_event(ev_fact)
+        mark("scan_rev", 0, side_s)
         vda.vda_scan_rev(desc, b.ws, x.alpha, None, b.states_r, stream=side_s)
-        if record:
-            pairs["scan_rev"][1].record(side_s)
-        path.ev_rev.record(side_s)
-        if record:
-            pairs["scan_fwd"][0].record(main_s)
+        mark("scan_rev", 1, side_s)
+        ev_rev.record(side_s)
+        mark("scan_fwd", 0, main_s)
         vda.vda_scan_fwd(desc, b.ws, x.alpha, None, b.states_f, stream=main_s)
-        if record:
-            pairs["scan_fwd"][1].record(main_s)
-        main_s.wait_event(path.ev_rev)
-        if record:
-            pairs["readout"][0].record(main_s)
+        mark("scan_fwd", 1, main_s)
+        main_s.wait_event(ev_rev)
+        mark("readout", 0, main_s)
         vda.vda_readout(desc, x.q, x.alpha, b.states_f, b.states_r, b.out, stream=main_s)
+        mark("readout", 1, main_s)
         if record:
-            pairs["readout"][1].record(main_s)
             for k in names:
                 ev[k].append(pairs[k])
 
@@ -163,53 +281,26 @@ def main():
     status = vda.vda_device_status(desc, bufs.ws)
     ms_step = 1e3 * t_total / args.steps
     kms = {k: float(np.mean([a.elapsed_time(b) for a, b in ev[k]])) for k in names}
-    print(f"[bench] {args.steps} steps: {ms_step:.3f} ms/step; kernels {kms}", file=sys.stderr, flush=True)
+    print(f"[bench] {args.steps} steps: {ms_step:.3f} ms/step; calls {kms}", file=sys.stderr, flush=True)
 
     flops, nbytes = algorithmic_work(cfg)
     t_s = ms_step / 1e3
-    frames_s = cfg.frames / t_s
-    tflops = flops / t_s / 1e12
     kb = kernel_bytes(cfg)
-    dom = max(("prepare", "readout"), key=lambda k: kms[k])
-    ach = kb[dom] / (kms[dom] / 1e3) / 1e9
-    roofline = {"kernel": dom, "bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
-                "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": _traffic(dom),
-                "algorithmic_bytes": kb[dom], "avg_ms": round(kms[dom], 4)}
+    call_of = {"stats_kernel": "stats", "readout_kernel": "readout"}
+    dom = max(kb, key=lambda k: kms[call_of[k]])
+    ach = kb[dom] / (kms[call_of[dom]] / 1e3) / 1e9
+    roofline = {"kernel": dom, "bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": _traffic(dom),
+                "algorithmic_bytes_per_launch": kb[dom], "avg_ms": round(kms[call_of[dom]], 4)}
 
-    cpu = None
-    rel = None
+    cpu, rel = None, None
     if not args.no_cpu_baseline:
-        from oracle import vda_oracle as orc
-        try:
-            from threadpoolctl import threadpool_info
-            cores = max(x.get("num_threads", 1) for x in threadpool_info()) if threadpool_info() else 1
-        except Exception:
-            cores = len(os.sched_getaffinity(0))
-        hs = list(range(cfg.heads if args.cpu_heads is None else min(args.cpu_heads, cfg.heads)))
-        O0 = bufs.out[0].float().cpu().numpy().astype(np.float64)
-        t_cpu = 0.0
-        errs = []
-        for h in hs:
-            f = heads_in[h].f64
-            text = cfg.text_tokens > 0
-            a = [f(x) for x in ("q", "k", "v", "beta", "alpha")]
-            tt = [f(x) if text else None for x in ("kt", "vt", "bt")]
-            c0 = time.perf_counter()
-            ref = orc.run_head(cfg.frames, cfg.chunk, cfg.window, cfg.anchors, *a, *tt)
-            t_cpu += time.perf_counter() - c0
-            if h == 0:
-                sl = slice(cfg.anchors, cfg.frames - cfg.anchors)
-                errs.append(orc.rel_l2(O0[sl], ref["O"][sl]))
-        frac = len(hs) / cfg.heads
-        cpu = {"value": round(cfg.frames * frac / t_cpu, 4), "unit": "frames/s", "cores": int(cores),
-               "kind": "oracle",
-               "sample": f"{len(hs)} of {cfg.heads} heads of the same workload (all {cfg.frames} frames), "
-                         f"float64 NumPy/LAPACK, {t_cpu:.1f}s; frames/s scaled by heads fraction"}
-        rel = errs[0] if errs else None
+        out0 = bufs.out[0].float().cpu().numpy().astype(np.float64)
+        cpu, rel = cpu_baseline(cfg, heads_in, out0, args.cpu_seconds)
 
     out = {
         "metric": "VDA scan+readout latent frames/s and % of MI355X bf16 MFMA peak",
-        "value": round(frames_s, 2),
+        "value": round(cfg.frames / t_s, 2),
         "unit": "frames/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -227,10 +318,10 @@ def main():
                    "text_tokens": cfg.text_tokens, "in_dtype": cfg.in_dtype, "out_dtype": cfg.out_dtype,
                    "state_dtype": "f32", "global_batch": 1, "seq_len": cfg.frames * cfg.tokens,
                    "parallelism": "single GPU"},
-        "tflops_algorithmic": round(tflops, 2),
-        "mfma_peak_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "tflops_algorithmic": round(flops / t_s / 1e12, 2),
+        "mfma_peak_frac": round(flops / t_s / 1e12 / PEAK_BF16_TFLOPS, 4),
         "hbm_frac_path": round(nbytes / t_s / 1e9 / PEAK_HBM_GBS, 4),
-        "kernel_ms": {k: round(v, 4) for k, v in kms.items()},
+        "call_ms": {k: round(v, 4) for k, v in kms.items()},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "rel_l2_head0": rel,

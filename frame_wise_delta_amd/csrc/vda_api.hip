@@ -316,6 +316,45 @@ int vda_prepare_frames(const vda_desc* desc, const void* k, const void* v, const
   return launch_status();
 }
 
+int vda_frame_stats(const vda_desc* desc, const void* k, const void* v, const float* beta, const void* k_text,
+                    const void* v_text, const float* beta_text, void* ws, size_t ws_size, void* stream) {
+  Shape s;
+  vda::PrepArgs a;
+  int rc = prep_args(desc, k, v, beta, k_text, v_text, beta_text, ws, ws_size, s, a);
+  if (rc) return rc;
+  rc = check_device();
+  if (rc) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  vda::launch_clear_status(a.status, st);
+  vda::launch_stats(a, s.d, desc->in_dtype == VDA_F32, st);
+  return launch_status();
+}
+
+int vda_factor_frames(const vda_desc* desc, void* ws, size_t ws_size, void* stream) {
+  Shape s;
+  int rc = check_desc(desc, &s);
+  if (rc) return rc;
+  if (!ws) return fail(VDA_ERR_NULL, "ws is NULL");
+  if (ws_size < ws_bytes(s)) return fail(VDA_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_size, ws_bytes(s));
+  if ((uintptr_t)ws & 255u) return fail(VDA_ERR_ALIGN, "ws needs 256-byte alignment");
+  rc = check_device();
+  if (rc) return rc;
+  vda::PrepArgs a = {};
+  a.status = static_cast<int*>(ws);
+  a.frames = reinterpret_cast<float*>(static_cast<char*>(ws) + vda::kWsHeader);
+  a.H = s.H;
+  a.T = s.T;
+  a.U = s.U;
+  a.a = s.a;
+  a.n = s.n;
+  a.n_eff = s.n_eff;
+  a.Nt = s.Nt;
+  a.s0 = 0;
+  a.cnt = s.n_eff;
+  vda::launch_gj(a, s.d, static_cast<hipStream_t>(stream));
+  return launch_status();
+}
+
 int vda_scan_fwd(const vda_desc* desc, const void* ws, const float* alpha, const float* s_init, float* states,
                  void* stream) {
   Shape s;

@@ -31,8 +31,8 @@ VDA_DEV_NONFINITE, VDA_DEV_PIVOT = 1, 2
 DTYPES = {"f32": VDA_F32, "bf16": VDA_BF16, "f16": VDA_F16}
 
 EXPORTS = ("vda_workspace_bytes", "vda_state_count", "vda_index_map", "vda_prepare_frames",
-           "vda_scan_fwd", "vda_scan_rev", "vda_readout", "vda_forward", "vda_device_status",
-           "vda_status_string", "vda_last_error")
+           "vda_frame_stats", "vda_factor_frames", "vda_scan_fwd", "vda_scan_rev", "vda_readout",
+           "vda_forward", "vda_device_status", "vda_status_string", "vda_last_error")
 
 
 class vda_desc(ctypes.Structure):
@@ -70,6 +70,9 @@ def load(path: str | None = None):
         "vda_index_map": [D, c_void_p, c_void_p],
         "vda_prepare_frames": [D, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                c_void_p, c_size_t, c_void_p],
+        "vda_frame_stats": [D, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                            c_void_p, c_size_t, c_void_p],
+        "vda_factor_frames": [D, c_void_p, c_size_t, c_void_p],
         "vda_scan_fwd": [D, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p],
         "vda_scan_rev": [D, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p],
         "vda_readout": [D, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p],
@@ -161,6 +164,19 @@ def vda_prepare_frames(desc, k, v, beta, k_text, v_text, beta_text, ws, ws_bytes
         ws_bytes = ws.numel() * ws.element_size()
     _check(load().vda_prepare_frames(ctypes.byref(desc), _ptr(k), _ptr(v), _ptr(beta), _ptr(k_text),
                                      _ptr(v_text), _ptr(beta_text), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def vda_frame_stats(desc, k, v, beta, k_text, v_text, beta_text, ws, ws_bytes=None, stream=None):
+    if ws_bytes is None:
+        ws_bytes = ws.numel() * ws.element_size()
+    _check(load().vda_frame_stats(ctypes.byref(desc), _ptr(k), _ptr(v), _ptr(beta), _ptr(k_text),
+                                  _ptr(v_text), _ptr(beta_text), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def vda_factor_frames(desc, ws, ws_bytes=None, stream=None):
+    if ws_bytes is None:
+        ws_bytes = ws.numel() * ws.element_size()
+    _check(load().vda_factor_frames(ctypes.byref(desc), _ptr(ws), ws_bytes, _stream(stream)))
 
 
 def vda_scan_fwd(desc, ws, alpha, s_init, states, stream=None):

@@ -129,6 +129,21 @@ int vda_prepare_frames(const vda_desc* desc, const void* k, const void* v, const
                        const void* k_text, const void* v_text, const float* beta_text,
                        void* ws, size_t ws_bytes, void* stream);
 
+/* The two halves of vda_prepare_frames, for callers (and profilers) that
+ * enqueue them separately; together, in this order on one stream, they do
+ * exactly what vda_prepare_frames does.
+ * vda_frame_stats [VDN 方法步骤详情 step (3)]: clears the device status word,
+ * computes A_t and B_t of every scanned frame and of the text tokens, and
+ * stores B_t and the upper triangle of A_t in `ws` (arguments as for
+ * vda_prepare_frames).
+ * vda_factor_frames [VDN 核心方法 para 2]: replaces every A_t in `ws` by
+ * N_t = (I + A_t)^{-1}; `ws` must hold the output of vda_frame_stats for the
+ * same desc. */
+int vda_frame_stats(const vda_desc* desc, const void* k, const void* v, const float* beta,
+                    const void* k_text, const void* v_text, const float* beta_text, void* ws,
+                    size_t ws_bytes, void* stream);
+int vda_factor_frames(const vda_desc* desc, void* ws, size_t ws_bytes, void* stream);
+
 /* Forward scan [VDN 核心方法 para 1; 方法步骤详情 step (4)]: starting from
  * S_0 = text_init_scale * S_init, applies S_t = (S_{t-1} Diag(alpha_t) + B_t) N_t
  * over the scanned frames in increasing order and records vda_state_count()

@@ -92,6 +92,16 @@ def test_null_and_workspace_checks_precede_any_device_call():
     # misaligned
     rc = lib.vda_prepare_frames(ctypes.byref(d), fake + 4, fake, fake, fake, fake, fake, fake, wsb, None)
     assert rc == vda.VDA_ERR_ALIGN
+    rc = lib.vda_frame_stats(ctypes.byref(d), fake, None, fake, fake, fake, fake, fake, wsb, None)
+    assert rc == vda.VDA_ERR_NULL
+    rc = lib.vda_frame_stats(ctypes.byref(d), fake, fake, fake, fake, fake, fake, fake, wsb - 1, None)
+    assert rc == vda.VDA_ERR_WORKSPACE
+    rc = lib.vda_factor_frames(ctypes.byref(d), None, wsb, None)
+    assert rc == vda.VDA_ERR_NULL
+    rc = lib.vda_factor_frames(ctypes.byref(d), fake, wsb - 1, None)
+    assert rc == vda.VDA_ERR_WORKSPACE
+    rc = lib.vda_factor_frames(ctypes.byref(d), fake + 16, wsb, None)
+    assert rc == vda.VDA_ERR_ALIGN
     rc = lib.vda_scan_fwd(ctypes.byref(d), fake, fake, None, None, None)
     assert rc == vda.VDA_ERR_NULL
     rc = lib.vda_readout(ctypes.byref(d), fake, fake, fake, None, fake, None)
@@ -109,6 +119,10 @@ def test_valid_call_without_gpu_reports_no_device():
     wsb = vda.vda_workspace_bytes(d)
     fake = 1 << 20
     rc = lib.vda_prepare_frames(ctypes.byref(d), fake, fake, fake, fake, fake, fake, fake, wsb, None)
+    assert rc == vda.VDA_ERR_DEVICE
+    rc = lib.vda_frame_stats(ctypes.byref(d), fake, fake, fake, fake, fake, fake, fake, wsb, None)
+    assert rc == vda.VDA_ERR_DEVICE
+    rc = lib.vda_factor_frames(ctypes.byref(d), fake, wsb, None)
     assert rc == vda.VDA_ERR_DEVICE
 
 

@@ -136,6 +136,21 @@ def test_fused_schedule_equals_step_by_step(frames, d, window, text, anchors):
     assert torch.equal(b1.out.view(torch.int16), b2.out.view(torch.int16))
 
 
+def test_stats_then_factor_equals_prepare():
+    """vda_frame_stats followed by vda_factor_frames fills the workspace with
+    the same bits as vda_prepare_frames."""
+    import torch
+    cfg = inp.scaled(inp.CONFIG_BY_NAME["h3"], heads=2, frames=12, tokens=200)
+    heads_in = inp.all_heads(cfg)
+    desc, dev, b1 = runner.run(cfg, heads_in)
+    b2 = runner.allocate(desc, cfg.out_dtype, "cuda")
+    vda.vda_frame_stats(desc, dev.k, dev.v, dev.beta, dev.kt, dev.vt, dev.bt, b2.ws, b2.ws_bytes)
+    vda.vda_factor_frames(desc, b2.ws, b2.ws_bytes)
+    torch.cuda.synchronize()
+    assert torch.equal(b1.ws[:4], b2.ws[:4])      # status word
+    assert torch.equal(b1.ws[256:], b2.ws[256:])  # every frame slot
+
+
 def test_fused_without_reverse_states():
     """window = -1 with states_rev = NULL: the reverse scan is skipped."""
     import torch
