@@ -4,8 +4,7 @@ One step = the whole path for one attention layer of the H3-shaped workload
 (24 heads, d = 128, 102 latent frames of which 2 are anchors, U = 1008
 tokens per frame, 512 text tokens, bf16 inputs, float32 state, bf16 output):
 
-    vda_frame_stats -> vda_factor_frames -> vda_scan_fwd || vda_scan_rev
-        -> vda_readout
+    vda_frame_stats -> vda_factor_frames -> vda_scan_bidir -> vda_readout
 
 (the same kernels, in the same order, as one vda_forward call).  Inputs are
 seeded synthetic draws (frame_wise_delta_amd.inputs) resident in HBM before
@@ -76,10 +75,16 @@ def kernel_bytes(cfg):
     return {"stats_kernel": stats, "readout_kernel": read}
 
 
-def _src_hash():
+KERNEL_SRC = {"stats_kernel": "vda_prepare.hip", "gj_kernel": "vda_prepare.hip",
+              "scan_kernel": "vda_scan.hip", "readout_kernel": "vda_readout.hip"}
+
+
+def _src_hash(kernel):
+    """Hash of the sources a kernel is compiled from (its file and the
+    shared headers)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "frame_wise_delta_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    for name in (KERNEL_SRC[kernel], "vda_common.h", "vda_kernels.h"):
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + f.read())
     return h.hexdigest()[:16]
@@ -90,16 +95,16 @@ TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
 
 def _traffic(kernel):
     """HBM bytes per launch measured with rocprofv3 counters (profiles/
-    traffic.json), or None if the kernel sources changed since."""
+    traffic.json), or None if the kernel's sources changed since."""
     try:
         with open(TRAFFIC_JSON) as f:
             t = json.load(f)
     except OSError:
         return None
-    if t.get("src_hash") != _src_hash():
-        return None
     k = t.get("kernels", {}).get(kernel)
-    return None if k is None else k.get("bytes_per_launch")
+    if k is None or k.get("src_hash") != _src_hash(kernel):
+        return None
+    return k.get("bytes_per_launch")
 
 
 # ------------------------------------------------------------- helpers --
@@ -146,15 +151,14 @@ def write_traffic(fetch_csv, write_csv, cal_fetch_csv, cal_write_csv):
     cw = _counter_means(cal_write_csv, "WRITE_SIZE")["copy"]
     ff = COPY_BYTES / (cf * 1024.0)
     wf = COPY_BYTES / (cw * 1024.0)
-    out = {"src_hash": _src_hash(),
-           "calibration": {"copy_bytes": COPY_BYTES, "fetch_kib": cf, "write_kib": cw,
+    out = {"calibration": {"copy_bytes": COPY_BYTES, "fetch_kib": cf, "write_kib": cw,
                            "fetch_factor": round(ff, 4), "write_factor": round(wf, 4)},
            "kernels": {}}
     for k in KERNELS:
         if k in f and k in w:
             fb, wb = f[k] * 1024.0 * ff, w[k] * 1024.0 * wf
             out["kernels"][k] = {"fetch_bytes": round(fb), "write_bytes": round(wb),
-                                 "bytes_per_launch": round(fb + wb)}
+                                 "bytes_per_launch": round(fb + wb), "src_hash": _src_hash(k)}
     os.makedirs(os.path.dirname(TRAFFIC_JSON), exist_ok=True)
     with open(TRAFFIC_JSON, "w") as fh:
         json.dump(out, fh, indent=1)
@@ -231,11 +235,9 @@ def main():
     dev = runner.upload(cfg, heads_in, "cuda")
     bufs = runner.allocate(desc, cfg.out_dtype, "cuda")
     main_s = torch.cuda.current_stream()
-    side_s = torch.cuda.Stream()
-    ev_fact, ev_rev = torch.cuda.Event(), torch.cuda.Event()
 
-    # events around each call, on the stream it runs on
-    names = ["stats", "factor", "scan_fwd", "scan_rev", "readout"]
+    # events around each call, on the stream they all run on
+    names = ["stats", "factor", "scans", "readout"]
     ev = {k: [] for k in names}
 
     def step(record):
@@ -243,28 +245,21 @@ def main():
         pairs = {k: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                  for k in names} if record else None
 
-        def mark(k, i, stream):
+        def mark(k, i):
             if record:
-                pairs[k][i].record(stream)
-        mark("stats", 0, main_s)
+                pairs[k][i].record(main_s)
+        mark("stats", 0)
         vda.vda_frame_stats(desc, x.k, x.v, x.beta, x.kt, x.vt, x.bt, b.ws, b.ws_bytes, stream=main_s)
-        mark("stats", 1, main_s)
-        mark("factor", 0, main_s)
+        mark("stats", 1)
+        mark("factor", 0)
         vda.vda_factor_frames(desc, b.ws, b.ws_bytes, stream=main_s)
-        mark("factor", 1, main_s)
-        ev_fact.record(main_s)
-        side_s.wait_event(ev_fact)
-        mark("scan_rev", 0, side_s)
-        vda.vda_scan_rev(desc, b.ws, x.alpha, None, b.states_r, stream=side_s)
-        mark("scan_rev", 1, side_s)
-        ev_rev.record(side_s)
-        mark("scan_fwd", 0, main_s)
-        vda.vda_scan_fwd(desc, b.ws, x.alpha, None, b.states_f, stream=main_s)
-        mark("scan_fwd", 1, main_s)
-        main_s.wait_event(ev_rev)
-        mark("readout", 0, main_s)
+        mark("factor", 1)
+        mark("scans", 0)
+        vda.vda_scan_bidir(desc, b.ws, x.alpha, None, b.states_f, b.states_r, stream=main_s)
+        mark("scans", 1)
+        mark("readout", 0)
         vda.vda_readout(desc, x.q, x.alpha, b.states_f, b.states_r, b.out, stream=main_s)
-        mark("readout", 1, main_s)
+        mark("readout", 1)
         if record:
             for k in names:
                 ev[k].append(pairs[k])

@@ -268,34 +268,6 @@ int read_args(const vda_desc* desc, const void* q, const float* alpha, const flo
   return VDA_OK;
 }
 
-// Per-device side stream and event pool of vda_forward (created on first
-// use, default stream priority; kept until the process ends).
-constexpr int kEvents = 8;
-struct Pipe {
-  bool ready = false;
-  hipStream_t side = nullptr;  // reverse scan
-  hipEvent_t ev[kEvents] = {};
-  std::mutex mu;
-};
-Pipe g_pipe[64];
-
-int pipe_for_current_device(Pipe** out) {
-  int dev = -1;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return fail(VDA_ERR_DEVICE, "no HIP device");
-  Pipe& p = g_pipe[dev];
-  std::lock_guard<std::mutex> lock(p.mu);
-  if (!p.ready) {
-    if (hipStreamCreateWithFlags(&p.side, hipStreamNonBlocking) != hipSuccess)
-      return fail(VDA_ERR_HIP, "hipStreamCreateWithFlags failed");
-    for (auto& e : p.ev)
-      if (hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess)
-        return fail(VDA_ERR_HIP, "hipEventCreateWithFlags failed");
-    p.ready = true;
-  }
-  *out = &p;
-  return VDA_OK;
-}
-
 }  // namespace
 
 extern "C" {
@@ -363,7 +335,8 @@ int vda_scan_fwd(const vda_desc* desc, const void* ws, const float* alpha, const
   if (rc) return rc;
   rc = check_device();
   if (rc) return rc;
-  vda::launch_scan(a, s.d, static_cast<hipStream_t>(stream));
+  vda::ScanPair p = {{a, a}, 1};
+  vda::launch_scan(p, s.d, static_cast<hipStream_t>(stream));
   return launch_status();
 }
 
@@ -375,7 +348,22 @@ int vda_scan_rev(const vda_desc* desc, const void* ws, const float* alpha, const
   if (rc) return rc;
   rc = check_device();
   if (rc) return rc;
-  vda::launch_scan(a, s.d, static_cast<hipStream_t>(stream));
+  vda::ScanPair p = {{a, a}, 1};
+  vda::launch_scan(p, s.d, static_cast<hipStream_t>(stream));
+  return launch_status();
+}
+
+int vda_scan_bidir(const vda_desc* desc, const void* ws, const float* alpha, const float* s_init,
+                   float* states_fwd, float* states_rev, void* stream) {
+  Shape s;
+  vda::ScanPair p;
+  int rc = scan_args(desc, ws, alpha, s_init, states_fwd, 0, s, p.dir[0]);
+  if (rc) return rc;
+  if ((rc = scan_args(desc, ws, alpha, s_init, states_rev, 1, s, p.dir[1]))) return rc;
+  rc = check_device();
+  if (rc) return rc;
+  p.ndir = 2;
+  vda::launch_scan(p, s.d, static_cast<hipStream_t>(stream));
   return launch_status();
 }
 
@@ -398,46 +386,25 @@ int vda_forward(const vda_desc* desc, const void* q, const void* k, const void* 
                 size_t ws_size, float* states_fwd, float* states_rev, void* out, void* stream) {
   Shape s;
   vda::PrepArgs pa;
-  vda::ScanArgs fa, ra;
+  vda::ScanPair sp;
   vda::ReadArgs qa;
   bool any = false;
   int rc = prep_args(desc, k, v, beta, k_text, v_text, beta_text, ws, ws_size, s, pa);
   if (rc) return rc;
   const bool rev = states_rev != nullptr || s.w >= 0;
-  if ((rc = scan_args(desc, ws, alpha, nullptr, states_fwd, 0, s, fa))) return rc;
-  if (rev && (rc = scan_args(desc, ws, alpha, nullptr, states_rev, 1, s, ra))) return rc;
+  if ((rc = scan_args(desc, ws, alpha, nullptr, states_fwd, 0, s, sp.dir[0]))) return rc;
+  sp.dir[1] = sp.dir[0];
+  if (rev && (rc = scan_args(desc, ws, alpha, nullptr, states_rev, 1, s, sp.dir[1]))) return rc;
+  sp.ndir = rev ? 2 : 1;
   if ((rc = read_args(desc, q, alpha, states_fwd, states_rev, out, s, qa, any))) return rc;
   if ((rc = check_device())) return rc;
-  Pipe* p = nullptr;
-  if ((rc = pipe_for_current_device(&p))) return rc;
-  std::lock_guard<std::mutex> lock(p->mu);
-  hipStream_t S = static_cast<hipStream_t>(stream), R = p->side;
-  int ne = 0;
-  bool err = false;
-  auto fork = [&](hipStream_t from, hipStream_t to) {  // `to` waits for the work enqueued on `from`
-    if (ne >= kEvents) {
-      err = true;
-      return;
-    }
-    err |= hipEventRecord(p->ev[ne], from) != hipSuccess;
-    err |= hipStreamWaitEvent(to, p->ev[ne], 0) != hipSuccess;
-    ++ne;
-  };
-  // The scans are bound by the latency of their per-frame operand loads, so
-  // they run only beside each other: statistics and factors on S, then the
-  // reverse scan on R and the forward scan on S, then the readout on S.
+  hipStream_t st = static_cast<hipStream_t>(stream);
   const bool f32 = desc->in_dtype == VDA_F32;
-  vda::launch_clear_status(pa.status, S);
-  vda::launch_stats(pa, s.d, f32, S);
-  vda::launch_gj(pa, s.d, S);
-  if (rev) {
-    fork(S, R);
-    vda::launch_scan(ra, s.d, R);
-  }
-  vda::launch_scan(fa, s.d, S);
-  if (rev) fork(R, S);
-  if (any) vda::launch_readout(qa, s.d, desc->in_dtype, desc->out_dtype, S);
-  if (err) return fail(VDA_ERR_HIP, "hipEventRecord / hipStreamWaitEvent failed");
+  vda::launch_clear_status(pa.status, st);
+  vda::launch_stats(pa, s.d, f32, st);
+  vda::launch_gj(pa, s.d, st);
+  vda::launch_scan(sp, s.d, st);  // both directions in one launch
+  if (any) vda::launch_readout(qa, s.d, desc->in_dtype, desc->out_dtype, st);
   return launch_status();
 }
 

@@ -30,6 +30,13 @@ struct ScanArgs {
   float scale;
 };
 
+// One or two scans in one launch: blocks [0, H RB) run dir[0], the next
+// H RB blocks (when ndir == 2) run dir[1].
+struct ScanPair {
+  ScanArgs dir[2];
+  int ndir;
+};
+
 struct ReadArgs {
   const void* q;          // [H][T][U][d]
   const float* alpha;     // [H][T][d]
@@ -43,7 +50,7 @@ struct ReadArgs {
 int launch_stats(const PrepArgs& a, int d, bool in_f32, hipStream_t stream);
 int launch_gj(const PrepArgs& a, int d, hipStream_t stream);
 void launch_clear_status(int* status, hipStream_t stream);
-int launch_scan(const ScanArgs& a, int d, hipStream_t stream);
+int launch_scan(const ScanPair& p, int d, hipStream_t stream);
 int launch_readout(const ReadArgs& a, int d, int in_dtype, int out_dtype, hipStream_t stream);
 
 }  // namespace vda

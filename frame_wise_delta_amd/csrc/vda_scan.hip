@@ -52,7 +52,7 @@ struct FrameRegs {
 }  // namespace
 
 template <int D>
-__global__ __launch_bounds__(ScanShape<D>::NT) void scan_kernel(ScanArgs a) {
+__global__ __launch_bounds__(ScanShape<D>::NT) void scan_kernel(ScanPair p) {
   using SS = ScanShape<D>;
   constexpr int ROWS = SS::ROWS, NQ = SS::NQ, PD = SS::PD;
   __shared__ __attribute__((aligned(16))) float sS[ROWS * D];
@@ -62,9 +62,12 @@ __global__ __launch_bounds__(ScanShape<D>::NT) void scan_kernel(ScanArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, lg = lane >> 4;
   constexpr int RB = D / ROWS;  // row blocks per head
-  const int nb = gridDim.x;
-  const int b = blockIdx.x;
-  const int L = xcd_block(b, nb);  // the row blocks of a head share an XCD
+  // the row blocks of a head (and the heads of a direction) share an XCD
+  int L = xcd_block(blockIdx.x, gridDim.x);
+  const int per_dir = p.dir[0].H * RB;
+  const int dir = L >= per_dir ? 1 : 0;
+  L -= dir * per_dir;
+  const ScanArgs& a = p.dir[dir];
   const int h = L / RB;
   const int r0 = ROWS * (L - h * RB);
   // elementwise phase: thread owns columns xc0..xc0+3 of rows xrow + 16 q
@@ -205,13 +208,14 @@ __global__ __launch_bounds__(ScanShape<D>::NT) void scan_kernel(ScanArgs a) {
   }
 }
 
-int launch_scan(const ScanArgs& a, int d, hipStream_t stream) {
-  if (a.H == 0) return 0;
-#define VDA_SCAN(DD)                                                                     \
-  if (d == DD) {                                                                         \
-    hipLaunchKernelGGL((scan_kernel<DD>), dim3((unsigned)(a.H * (DD / ScanShape<DD>::ROWS))), \
-                       dim3(ScanShape<DD>::NT), 0, stream, a);                           \
-    return 0;                                                                            \
+int launch_scan(const ScanPair& p, int d, hipStream_t stream) {
+  const int H = p.dir[0].H;
+  if (H == 0) return 0;
+#define VDA_SCAN(DD)                                                                              \
+  if (d == DD) {                                                                                  \
+    hipLaunchKernelGGL((scan_kernel<DD>), dim3((unsigned)(p.ndir * H * (DD / ScanShape<DD>::ROWS))), \
+                       dim3(ScanShape<DD>::NT), 0, stream, p);                                    \
+    return 0;                                                                                     \
   }
   VDA_SCAN(16) VDA_SCAN(32) VDA_SCAN(64) VDA_SCAN(128)
 #undef VDA_SCAN

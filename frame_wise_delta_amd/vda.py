@@ -31,8 +31,8 @@ VDA_DEV_NONFINITE, VDA_DEV_PIVOT = 1, 2
 DTYPES = {"f32": VDA_F32, "bf16": VDA_BF16, "f16": VDA_F16}
 
 EXPORTS = ("vda_workspace_bytes", "vda_state_count", "vda_index_map", "vda_prepare_frames",
-           "vda_frame_stats", "vda_factor_frames", "vda_scan_fwd", "vda_scan_rev", "vda_readout",
-           "vda_forward", "vda_device_status", "vda_status_string", "vda_last_error")
+           "vda_frame_stats", "vda_factor_frames", "vda_scan_fwd", "vda_scan_rev", "vda_scan_bidir",
+           "vda_readout", "vda_forward", "vda_device_status", "vda_status_string", "vda_last_error")
 
 
 class vda_desc(ctypes.Structure):
@@ -75,6 +75,7 @@ def load(path: str | None = None):
         "vda_factor_frames": [D, c_void_p, c_size_t, c_void_p],
         "vda_scan_fwd": [D, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p],
         "vda_scan_rev": [D, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p],
+        "vda_scan_bidir": [D, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p],
         "vda_readout": [D, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p],
         "vda_forward": [D, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                         c_void_p, c_void_p, c_size_t, c_void_p, c_void_p, c_void_p, c_void_p],
@@ -187,6 +188,11 @@ def vda_scan_fwd(desc, ws, alpha, s_init, states, stream=None):
 def vda_scan_rev(desc, ws, alpha, s_init, states, stream=None):
     _check(load().vda_scan_rev(ctypes.byref(desc), _ptr(ws), _ptr(alpha), _ptr(s_init), _ptr(states),
                                _stream(stream)))
+
+
+def vda_scan_bidir(desc, ws, alpha, s_init, states_fwd, states_rev, stream=None):
+    _check(load().vda_scan_bidir(ctypes.byref(desc), _ptr(ws), _ptr(alpha), _ptr(s_init), _ptr(states_fwd),
+                                 _ptr(states_rev), _stream(stream)))
 
 
 def vda_readout(desc, q, alpha, states_fwd, states_rev, out, stream=None):

@@ -160,6 +160,12 @@ int vda_scan_fwd(const vda_desc* desc, const void* ws, const float* alpha, const
 int vda_scan_rev(const vda_desc* desc, const void* ws, const float* alpha, const float* s_init,
                  float* states, void* stream);
 
+/* Both scans in one launch: the same work and results as vda_scan_fwd
+ * (into states_fwd) and vda_scan_rev (into states_rev) with the same s_init,
+ * run side by side on the GPU. */
+int vda_scan_bidir(const vda_desc* desc, const void* ws, const float* alpha, const float* s_init,
+                   float* states_fwd, float* states_rev, void* stream);
+
 /* Readout [VDN 核心方法 para 1; 方法步骤详情 step (5)].  window >= 0: for a
  * scanned frame t of chunk c and each token,
  *   o = states_fwd[F(c)] (b_f * q) + states_rev[R(c)] (b_r * q),
@@ -170,16 +176,11 @@ int vda_scan_rev(const vda_desc* desc, const void* ws, const float* alpha, const
 int vda_readout(const vda_desc* desc, const void* q, const float* alpha, const float* states_fwd,
                 const float* states_rev, void* out, void* stream);
 
-/* The whole path in one call: vda_prepare_frames, vda_scan_fwd and
- * vda_scan_rev (S_init = S^T from the text tokens, or zero) and vda_readout,
- * with the same arguments, layouts and results as those calls made in that
- * order on `stream`.  The reverse scan runs on a further HIP stream of the
- * current device (created on first use, default priority, kept until the
- * process ends), concurrently with the forward scan.  All of it is ordered
- * after the work already enqueued on `stream`, and work enqueued on `stream`
- * afterwards is ordered after all of it.  Calls from several host threads
- * are serialised while they enqueue.  states_rev may be NULL when
- * window == -1 (the reverse scan is then skipped). */
+/* The whole path in one call: vda_prepare_frames, vda_scan_bidir (S_init =
+ * S^T from the text tokens, or zero) and vda_readout, with the same
+ * arguments, layouts and results as those calls made in that order on
+ * `stream`; everything is enqueued on `stream` alone.  states_rev may be
+ * NULL when window == -1 (the reverse scan is then skipped). */
 int vda_forward(const vda_desc* desc, const void* q, const void* k, const void* v, const float* beta,
                 const float* alpha, const void* k_text, const void* v_text, const float* beta_text,
                 void* ws, size_t ws_bytes, float* states_fwd, float* states_rev, void* out,

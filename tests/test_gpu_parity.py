@@ -136,6 +136,62 @@ def test_fused_schedule_equals_step_by_step(frames, d, window, text, anchors):
     assert torch.equal(b1.out.view(torch.int16), b2.out.view(torch.int16))
 
 
+@pytest.mark.parametrize("name", ["tiny", "scan_only"])
+def test_bidirectional_scan_equals_two_scans(name):
+    """vda_scan_bidir (one launch) records the same bits as vda_scan_fwd and
+    vda_scan_rev, also with an explicit initial state."""
+    import torch
+    cfg = inp.CONFIG_BY_NAME[name]
+    heads_in = inp.all_heads(cfg)
+    desc, dev, b1 = runner.run(cfg, heads_in)
+    sf, sr = torch.empty_like(b1.states_f), torch.empty_like(b1.states_r)
+    vda.vda_scan_bidir(desc, b1.ws, dev.alpha, None, sf, sr)
+    torch.cuda.synchronize()
+    assert torch.equal(sf, b1.states_f) and torch.equal(sr, b1.states_r)
+    g = np.random.default_rng(7)
+    s0 = torch.from_numpy(g.standard_normal((cfg.heads, cfg.d, cfg.d)).astype(np.float32)).cuda()
+    f1, r1 = torch.empty_like(sf), torch.empty_like(sr)
+    vda.vda_scan_fwd(desc, b1.ws, dev.alpha, s0, f1)
+    vda.vda_scan_rev(desc, b1.ws, dev.alpha, s0, r1)
+    vda.vda_scan_bidir(desc, b1.ws, dev.alpha, s0, sf, sr)
+    torch.cuda.synchronize()
+    assert torch.equal(sf, f1) and torch.equal(sr, r1)
+
+
+def test_forward_replays_from_a_hip_graph():
+    """vda_forward enqueues only kernels on the caller's stream (no memsets,
+    no other streams), so it can be captured in a HIP graph.  Every replay,
+    with eager work on the same buffers between replays, gives the eager
+    result bit for bit."""
+    import torch
+    cfg = inp.scaled(inp.CONFIG_BY_NAME["h3"], heads=2, frames=22, tokens=96)
+    heads_in = inp.all_heads(cfg)
+    desc, dev, bufs = runner.run(cfg, heads_in, fused=True)
+    ref = [bufs.out.clone(), bufs.states_f.clone(), bufs.states_r.clone()]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fw = runner.Forward(desc, dev, bufs)
+        fw.main = s
+        fw.enqueue()
+        s.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            fw.enqueue()
+    torch.cuda.synchronize()
+    for i in range(3):
+        bufs.out.zero_()
+        bufs.states_f.fill_(float("nan"))
+        bufs.states_r.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        print(f"[parity] graph replay {i}", flush=True)
+        assert torch.equal(bufs.out.view(torch.int16), ref[0].view(torch.int16))
+        assert torch.equal(bufs.states_f, ref[1]) and torch.equal(bufs.states_r, ref[2])
+        assert vda.vda_device_status(desc, bufs.ws) == 0
+
+
 def test_stats_then_factor_equals_prepare():
     """vda_frame_stats followed by vda_factor_frames fills the workspace with
     the same bits as vda_prepare_frames."""
