@@ -12,6 +12,7 @@ namespace vda {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint16_t u16;
 
@@ -83,10 +84,10 @@ struct InBF16 { typedef u16 T; static constexpr int bytes = 2; };
 // ------------------------------------------------------------ workspace --
 // [0, 256): device status word (int32) + padding.
 // then, per head h and frame slot f (f < n: scanned frame f; f == n: text),
-// N = (I + A)^{-1} as two d x d bf16 arrays N_hi, N_lo (N ~ N_hi + N_lo) in
-// MFMA fragment order (below), followed by B (d x d float32, row-major):
-// 8 d^2 bytes per slot.  Between the two prepare kernels the N half holds
-// the upper-triangle 16x16 tiles of A (float32) in accumulator order: tile
+// 8 d^2 bytes: N = (I + A)^{-1} as a d x d f16 array in MFMA fragment order
+// (below) in the first 2 d^2 bytes, then (at byte 4 d^2) B as a d x d f16
+// array, row-major.  Between the two prepare kernels the first half holds the
+// upper-triangle 16x16 tiles of A (float32) in accumulator order: tile
 // (ri, cj), cj >= ri, lane l holds A[16ri + 4(l/16) + e][16cj + l % 16],
 // e = 0..3, as 16 bytes at float offset ((ri * d/16 + cj) * 64 + l) * 4.
 constexpr size_t kWsHeader = 256;

@@ -17,7 +17,7 @@
 //
 // gj_kernel: one wavefront per frame inverts G = I + A in registers with a
 // blocked Gauss-Jordan sweep (16x16 blocks on MFMA, scalar 16x16 pivot-block
-// inverses) and overwrites A with N = G^{-1} as a bf16 hi/lo pair in the MFMA
+// inverses) and overwrites A with N = G^{-1}, rounded to f16, in the MFMA
 // fragment order the scan consumes.  G is symmetric positive definite
 // (eigenvalues >= 1), so no pivoting is needed.  Running the latency-bound
 // sweep as single-wavefront workgroups, apart from the bandwidth-bound
@@ -179,9 +179,10 @@ template <int D>
 constexpr int kSP = D + 4;
 
 // Stage 64 rows of a wavefront-strip-distributed d x d float32 matrix
-// (accumulator layout) through LDS and store them row-major, coalesced.
+// (accumulator layout) through LDS and store them row-major as f16,
+// coalesced.
 template <int D, int NRW>
-__device__ __forceinline__ void store_rows(const f32x4 (&acc)[NRW][D / 16], float* stage, float* dst,
+__device__ __forceinline__ void store_rows(const f32x4 (&acc)[NRW][D / 16], float* stage, _Float16* dst,
                                            int tid, int wave, int lg, int lr) {
   constexpr int RT = D / 16;
   constexpr int SP = kSP<D>;
@@ -196,10 +197,11 @@ __device__ __forceinline__ void store_rows(const f32x4 (&acc)[NRW][D / 16], floa
     }
     lds_barrier();
     const int rows = (D - 64 * m) < 64 ? (D - 64 * m) : 64;
-    float* d = dst + (size_t)64 * m * D;
+    _Float16* d = dst + (size_t)64 * m * D;
     for (int i = tid; i < rows * D / 4; i += kThreads) {
       const int r = i / (D / 4), c4 = i - r * (D / 4);
-      reinterpret_cast<float4*>(d)[i] = *reinterpret_cast<const float4*>(stage + r * SP + 4 * c4);
+      const float4 v = *reinterpret_cast<const float4*>(stage + r * SP + 4 * c4);
+      reinterpret_cast<f16x4*>(d)[i] = f16x4{(_Float16)v.x, (_Float16)v.y, (_Float16)v.z, (_Float16)v.w};
     }
     lds_barrier();
   }
@@ -335,7 +337,7 @@ __global__ __launch_bounds__(kThreads, 2) void stats_kernel(PrepArgs args) {
     }
   }
   float* stage = reinterpret_cast<float*>(smem);
-  store_rows<D, NRW>(accB, stage, slot + D * D, tid, wave, lg, lr);  // B
+  store_rows<D, NRW>(accB, stage, reinterpret_cast<_Float16*>(slot + D * D), tid, wave, lg, lr);  // B (f16)
   if (bad) atomicOr(args.status, bad);
 }
 
@@ -444,21 +446,17 @@ __global__ __launch_bounds__(64, 2) void gj_kernel(PrepArgs args) {
       }
   }
 
-  // ---- N = G^{-1} -> workspace as bf16 hi/lo in fragment order.  Pair
+  // ---- N = G^{-1} -> workspace as f16 in fragment order.  Pair
   //      {i, j}, i < j, is held as N[j][i]; N[i][j] is its transpose.  An
   //      accumulator tile N[x][y] covers column 16y + n, rows 16x + 4g + e,
   //      i.e. half of the 16-byte chunk (16y + n, 2x + g/2).
-  __bf16* nhi = reinterpret_cast<__bf16*>(slot);
-  __bf16* nlo = nhi + D * D;
+  _Float16* nf = reinterpret_cast<_Float16*>(slot);
   auto put = [&](f32x4 v, int x, int yy) {
 #pragma unroll
     for (int e = 0; e < 4; ++e)
       if (!__builtin_isfinite(v[e])) bad |= VDA_DEV_NONFINITE;
-    bf16x4 hi, lo;
-    split4(v, hi, lo);
     const size_t off = (size_t)ntile_chunk(D, 16 * yy + n, 2 * x + (g >> 1)) * 8 + 4 * (g & 1);
-    *reinterpret_cast<bf16x4*>(nhi + off) = hi;
-    *reinterpret_cast<bf16x4*>(nlo + off) = lo;
+    *reinterpret_cast<f16x4*>(nf + off) = __builtin_convertvector(v, f16x4);
   };
 #pragma unroll
   for (int j = 0; j < RT; ++j) {

@@ -13,10 +13,12 @@
 // 32 x d slice of S in LDS in float32 and runs d/16 wavefronts, one per
 // 16-column output tile.
 // Per frame, the VALU forms X = S Diag(alpha) + B (float32) and splits it into
-// bf16 hi/lo in LDS; each wavefront computes its 16 x 16 tile of X N on MFMA
-// as X_hi N_hi + X_hi N_lo + X_lo N_hi (about 2^-16 relative error), N being
-// stored pre-split by the prepare kernel in MFMA fragment order and read as
-// rows (N is symmetric).
+// an f16 hi/lo pair in LDS; each wavefront computes its 16 x 16 tile of X N
+// on MFMA as X_hi N + X_lo N, N being stored by the prepare kernel as f16 in
+// MFMA fragment order and read as rows (N is symmetric).  Each workgroup
+// pulls N and its rows of B through its CU's vector-memory path once per
+// frame, and that is what bounds a step, so N and B are kept to 2 bytes per
+// entry (f16).
 // The chain is bound by the latency of these per-frame operand loads, so
 // frames are prefetched three or four steps ahead into registers; the barriers wait
 // for LDS traffic only, so the global loads stay in flight across them.
@@ -44,8 +46,8 @@ struct ScanShape {
 // Operands of one frame held by one thread.
 template <int D>
 struct FrameRegs {
-  bf16x8 nh[ScanShape<D>::KS], nl[ScanShape<D>::KS];  // N column tile (k-slices of this lane)
-  float4 b[ScanShape<D>::NQ];                          // B row segments (rows xrow + 16 q)
+  f16x8 nk[ScanShape<D>::KS];                          // N column tile (k-slices of this lane)
+  f16x4 b[ScanShape<D>::NQ];                           // B row segments (rows xrow + 16 q)
   float4 al;                                           // alpha segment
 };
 
@@ -56,8 +58,8 @@ __global__ __launch_bounds__(ScanShape<D>::NT) void scan_kernel(ScanPair p) {
   using SS = ScanShape<D>;
   constexpr int ROWS = SS::ROWS, NQ = SS::NQ, PD = SS::PD;
   __shared__ __attribute__((aligned(16))) float sS[ROWS * D];
-  __shared__ __attribute__((aligned(16))) __bf16 sXh[ROWS * SS::XP];
-  __shared__ __attribute__((aligned(16))) __bf16 sXl[ROWS * SS::XP];
+  __shared__ __attribute__((aligned(16))) _Float16 sXh[ROWS * SS::XP];
+  __shared__ __attribute__((aligned(16))) _Float16 sXl[ROWS * SS::XP];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, lg = lane >> 4;
@@ -81,24 +83,22 @@ __global__ __launch_bounds__(ScanShape<D>::NT) void scan_kernel(ScanPair p) {
 
   auto load = [&](FrameRegs<D>& fr, int slot, const float* alpha_row) {
     const float* base = frames + (size_t)slot * slot_floats;
-    const __bf16* nhi = reinterpret_cast<const __bf16*>(base);
-    const __bf16* nlo = nhi + D * D;
-    const float* bm = base + D * D;
+    const _Float16* nf = reinterpret_cast<const _Float16*>(base);
+    const _Float16* bm = reinterpret_cast<const _Float16*>(base + D * D);
     // fragment order: one wavefront reads 64 consecutive 16-byte chunks
 #pragma unroll
     for (int kk = 0; kk < SS::KS; ++kk) {
       if (lg < SS::LG) {
         const int chunk = ((ct * SS::KS + kk) * SS::LG + lg) * 16 + lr;
-        fr.nh[kk] = reinterpret_cast<const bf16x8*>(nhi)[chunk];
-        fr.nl[kk] = reinterpret_cast<const bf16x8*>(nlo)[chunk];
+        fr.nk[kk] = reinterpret_cast<const f16x8*>(nf)[chunk];
       } else {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) fr.nh[kk][e] = fr.nl[kk][e] = bits_to_bf16(0);
+        for (int e = 0; e < 8; ++e) fr.nk[kk][e] = (_Float16)0.f;
       }
     }
 #pragma unroll
     for (int q = 0; q < NQ; ++q)
-      fr.b[q] = *reinterpret_cast<const float4*>(bm + (size_t)(r0 + xrow + 16 * q) * D + xc0);
+      fr.b[q] = *reinterpret_cast<const f16x4*>(bm + (size_t)(r0 + xrow + 16 * q) * D + xc0);
     fr.al = alpha_row ? *reinterpret_cast<const float4*>(alpha_row + xc0) : make_float4(1.f, 1.f, 1.f, 1.f);
   };
 
@@ -109,20 +109,18 @@ __global__ __launch_bounds__(ScanShape<D>::NT) void scan_kernel(ScanPair p) {
     for (int q = 0; q < NQ; ++q) {
       const int row = xrow + 16 * q;
       const float4 s = *reinterpret_cast<const float4*>(sS + row * D + xc0);
-      const float4 al = fr.al, bb = fr.b[q];
-      const float x[4] = {fmaf(s.x, al.x, bb.x), fmaf(s.y, al.y, bb.y), fmaf(s.z, al.z, bb.z),
-                          fmaf(s.w, al.w, bb.w)};
-      typedef __bf16 bf4 __attribute__((ext_vector_type(4)));
-      bf4 hi, lo;
+      const float4 al = fr.al;
+      const f16x4 bb = fr.b[q];
+      const float x[4] = {fmaf(s.x, al.x, (float)bb[0]), fmaf(s.y, al.y, (float)bb[1]),
+                          fmaf(s.z, al.z, (float)bb[2]), fmaf(s.w, al.w, (float)bb[3])};
+      f16x4 hi, lo;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        __bf16 hh, ll;
-        split_bf16(x[e], hh, ll);
-        hi[e] = hh;
-        lo[e] = ll;
+        hi[e] = (_Float16)x[e];
+        lo[e] = (_Float16)(x[e] - (float)hi[e]);
       }
-      *reinterpret_cast<bf4*>(sXh + row * SS::XP + xc0) = hi;
-      *reinterpret_cast<bf4*>(sXl + row * SS::XP + xc0) = lo;
+      *reinterpret_cast<f16x4*>(sXh + row * SS::XP + xc0) = hi;
+      *reinterpret_cast<f16x4*>(sXl + row * SS::XP + xc0) = lo;
     }
     lds_barrier();
     f32x4 acc[SS::RTS];
@@ -133,17 +131,16 @@ __global__ __launch_bounds__(ScanShape<D>::NT) void scan_kernel(ScanPair p) {
       const int k0 = 32 * kk + 8 * lg;
 #pragma unroll
       for (int rt = 0; rt < SS::RTS; ++rt) {
-        bf16x8 xh, xl;
+        f16x8 xh, xl;
         if (k0 < D) {
-          xh = *reinterpret_cast<const bf16x8*>(sXh + (16 * rt + lr) * SS::XP + k0);
-          xl = *reinterpret_cast<const bf16x8*>(sXl + (16 * rt + lr) * SS::XP + k0);
+          xh = *reinterpret_cast<const f16x8*>(sXh + (16 * rt + lr) * SS::XP + k0);
+          xl = *reinterpret_cast<const f16x8*>(sXl + (16 * rt + lr) * SS::XP + k0);
         } else {
 #pragma unroll
-          for (int e = 0; e < 8; ++e) xh[e] = xl[e] = bits_to_bf16(0);
+          for (int e = 0; e < 8; ++e) xh[e] = xl[e] = (_Float16)0.f;
         }
-        acc[rt] = mfma_bf16(xh, fr.nh[kk], acc[rt]);
-        acc[rt] = mfma_bf16(xh, fr.nl[kk], acc[rt]);
-        acc[rt] = mfma_bf16(xl, fr.nh[kk], acc[rt]);
+        acc[rt] = mfma_f16(xh, fr.nk[kk], acc[rt]);
+        acc[rt] = mfma_f16(xl, fr.nk[kk], acc[rt]);
       }
     }
 #pragma unroll

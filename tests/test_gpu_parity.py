@@ -12,7 +12,8 @@ from oracle import vda_oracle as orc
 pytestmark = pytest.mark.gpu
 
 TOL_O = 2e-3       # output, relative L2 (bf16 inputs, float32 state)
-TOL_STATE = 1e-3   # recorded states and workspace factors, relative L2
+TOL_STATE = 1e-3   # recorded states and the workspace's B (f16), relative L2
+TOL_N = 6e-4       # N = (I + A)^-1 stored as f16: rounding alone is <= 2^-11 per entry
 
 
 def _oracle(cfg, h_in, bridge=True, scale=0.5):
@@ -60,21 +61,16 @@ def _ws_frames(bufs, desc):
     n_eff = n + (1 if desc.text_tokens else 0)
     raw = bufs.ws.cpu().numpy()[256:256 + desc.heads * n_eff * 2 * d * d * 4]
     slots = raw.reshape(desc.heads, n_eff, 8 * d * d)
-    # N is stored in MFMA fragment order: chunk ((ct*KS + kk)*LG + lg)*16 + lr
+    # N is stored as f16 in MFMA fragment order: chunk ((ct*KS + kk)*LG + lg)*16 + lr
     # holds N[16 ct + lr][32 kk + 8 lg .. +7]
     KS, LG = max(1, d // 32), min(4, d // 8)
     j = np.arange(d)[:, None]
     c = np.arange(d // 8)[None, :]
     chunk = (((j // 16) * KS + c // 4) * LG + c % 4) * 16 + j % 16
     idx = (chunk[:, :, None] * 8 + np.arange(8)[None, None, :]).reshape(d, d)
-
-    def untile(part):
-        v = inp.bf16_bits_to_f32(part.copy().view(np.uint16)).reshape(desc.heads, n_eff, d * d)
-        return v[..., idx]
-    hi = untile(slots[..., :2 * d * d])
-    lo = untile(slots[..., 2 * d * d:4 * d * d])
-    B = slots[..., 4 * d * d:].copy().view(np.float32).reshape(desc.heads, n_eff, d, d)
-    return np.stack([hi.astype(np.float64) + lo, B.astype(np.float64)], axis=2)
+    Nf = slots[..., :2 * d * d].copy().view(np.float16).reshape(desc.heads, n_eff, d * d)[..., idx]
+    B = slots[..., 4 * d * d:6 * d * d].copy().view(np.float16).reshape(desc.heads, n_eff, d, d)
+    return np.stack([Nf.astype(np.float64), B.astype(np.float64)], axis=2)
 
 
 def test_tiny_config():
@@ -87,7 +83,7 @@ def test_tiny_config():
         t = cfg.anchors + f
         A, B = orc.frame_stats(h.f64("k")[t], h.f64("v")[t], h.f64("beta")[t])
         N = np.linalg.inv(np.eye(cfg.d) + A)
-        assert orc.rel_l2(fr[0, f, 0], N) <= 1e-4
+        assert orc.rel_l2(fr[0, f, 0], N) <= TOL_N
         assert orc.rel_l2(fr[0, f, 1], B) <= 1e-3
 
 
@@ -203,8 +199,13 @@ def test_stats_then_factor_equals_prepare():
     vda.vda_frame_stats(desc, dev.k, dev.v, dev.beta, dev.kt, dev.vt, dev.bt, b2.ws, b2.ws_bytes)
     vda.vda_factor_frames(desc, b2.ws, b2.ws_bytes)
     torch.cuda.synchronize()
-    assert torch.equal(b1.ws[:4], b2.ws[:4])      # status word
-    assert torch.equal(b1.ws[256:], b2.ws[256:])  # every frame slot
+    assert torch.equal(b1.ws[:4], b2.ws[:4])  # status word
+    d = desc.d_k
+    n_eff = cfg.scanned + (1 if cfg.text_tokens else 0)
+    s1 = b1.ws[256:].view(desc.heads * n_eff, 8 * d * d)
+    s2 = b2.ws[256:].view(desc.heads * n_eff, 8 * d * d)
+    assert torch.equal(s1[:, :2 * d * d], s2[:, :2 * d * d])  # N (f16)
+    assert torch.equal(s1[:, 4 * d * d:6 * d * d], s2[:, 4 * d * d:6 * d * d])  # B (f16)
 
 
 def test_fused_without_reverse_states():
@@ -231,11 +232,11 @@ def test_h3_shape_reduced_frames():
     for f in (0, 7, 19):
         t = cfg.anchors + f
         A, B = orc.frame_stats(h.f64("k")[t], h.f64("v")[t], h.f64("beta")[t])
-        assert orc.rel_l2(fr[1, f, 0], np.linalg.inv(np.eye(cfg.d) + A)) <= 1e-4
+        assert orc.rel_l2(fr[1, f, 0], np.linalg.inv(np.eye(cfg.d) + A)) <= TOL_N
         assert orc.rel_l2(fr[1, f, 1], B) <= 1e-3
     # text slot
     A, B = orc.frame_stats(h.f64("kt"), h.f64("vt"), h.f64("bt"))
-    assert orc.rel_l2(fr[1, cfg.scanned, 0], np.linalg.inv(np.eye(cfg.d) + A)) <= 1e-4
+    assert orc.rel_l2(fr[1, cfg.scanned, 0], np.linalg.inv(np.eye(cfg.d) + A)) <= TOL_N
 
 
 @pytest.mark.parametrize("d,U", [(16, 5), (32, 70), (64, 100), (128, 37), (128, 1000)])
