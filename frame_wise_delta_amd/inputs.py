@@ -20,6 +20,8 @@ these draws stand in for them:
 * alpha: lo + (1 - lo) * U(0, 1) per frame and channel (lo = 0.9, or 0.97 for
          the long-video configuration)
 * text tokens (k_T, v_T, beta_T) follow the same laws as video tokens.
+* readout epilogue (``epilogue_inputs``): gate logits N(0, 1) per frame,
+  token and channel; RMSNorm weight 1 + 0.1 N(0, 1) per channel.
 
 Every tensor of every head comes from its own generator
 ``numpy.random.default_rng([seed, tensor_id, head])`` so that any head can be
@@ -36,7 +38,7 @@ from concurrent.futures import ThreadPoolExecutor
 import numpy as np
 
 # tensor ids for the per-tensor generators
-_Q, _K, _V, _BETA, _ALPHA, _KT, _VT, _BT = range(8)
+_Q, _K, _V, _BETA, _ALPHA, _KT, _VT, _BT, _GATE, _NORMW = range(10)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -185,6 +187,31 @@ def head_inputs(cfg: Config, head: int, parts=("q", "k", "v", "beta", "alpha", "
         out["vt"] = store(_rng(cfg, _VT, head).standard_normal((nt, d)), dt)
         out["bt"] = _sigmoid(_rng(cfg, _BT, head).standard_normal((nt,))).astype(np.float32)
     return HeadInputs(**out)
+
+
+@dataclasses.dataclass
+class EpilogueInputs:
+    """Stored inputs of the readout epilogue of one head: gate logits
+    [T, U, d] (float32 or bf16 bits per ``dtype``) and the RMSNorm weight
+    [d] float32."""
+
+    dtype: str
+    gate: np.ndarray
+    weight: np.ndarray
+
+    def f64(self, name: str) -> np.ndarray:
+        a = getattr(self, name)
+        return a.astype(np.float64) if name == "weight" else to_f64(a, self.dtype)
+
+
+def epilogue_inputs(cfg: Config, head: int) -> EpilogueInputs:
+    """Gate logits N(0, 1) per (frame, token, channel) and RMSNorm weights
+    1 + 0.1 N(0, 1) per channel: stand-ins for the gate projection of the
+    layer input and a trained norm weight."""
+    T, U, d = cfg.frames, cfg.tokens, cfg.d
+    gate = store(_rng(cfg, _GATE, head).standard_normal((T, U, d)), cfg.in_dtype)
+    weight = (1.0 + 0.1 * _rng(cfg, _NORMW, head).standard_normal(d)).astype(np.float32)
+    return EpilogueInputs(dtype=cfg.in_dtype, gate=gate, weight=weight)
 
 
 def all_heads(cfg: Config, heads=None, workers: int | None = None,

@@ -40,6 +40,9 @@ Readings of points the page leaves open:
   read by the linear branch (their output rows are zero).
 * With ``window = -1`` (no exclusion) the readout of frame t is S^f_t q where
   S^f_t includes frame t's own write.
+* Epilogue: RMSNorm over the d_v channels of each token with a per-head
+  weight and epsilon, then an elementwise sigmoid gate on per-channel logits
+  (which come from the layer input and are given here).
 
 Everything is float64; matrix products and linear solves are NumPy/LAPACK
 calls used as single steps.  No blocking, chunk composition or reordering.
@@ -172,6 +175,23 @@ def readout_full(Q, states_f, frame_chunk, anchors):
             continue
         O[t] = Q[t] @ states_f[t - a + 1].T
     return O
+
+
+# ------------------------------------------------------------- epilogue --
+
+def rmsnorm_gate(O, weight, gate, eps):
+    """Readout epilogue of the linear branch [VDN 方法步骤详情 step (5): the
+    read is RMS-normalised and then passes a sigmoid gate; VDN 核心方法 ¶1:
+    each branch is gated, the linear one after an RMSNorm, before its own
+    output projection].  Over the value channels c of each (frame, token):
+
+        y_c = o_c / sqrt(mean_c' o_c'^2 + eps) * weight_c * sigmoid(gate_c)
+
+    O [T, U, d_v]; weight [d_v] (per head); gate [T, U, d_v] logits.  Rows
+    that are zero (anchors) stay zero."""
+    ms = np.mean(O * O, axis=-1, keepdims=True)
+    sig = 1.0 / (1.0 + np.exp(-gate))
+    return O / np.sqrt(ms + eps) * weight[None, None, :] * sig
 
 
 # ------------------------------------------------------------------ run --

@@ -361,3 +361,65 @@ def test_inputs_are_deterministic_per_head():
     k = a.f64("k")
     assert np.allclose(np.linalg.norm(k, axis=-1), 1.0, atol=1e-6)
     assert ((a.alpha >= 0.9) & (a.alpha < 1.0)).all()
+
+
+# ----------------------------------------------------- readout epilogue (f1) --
+
+def test_epilogue_hand_worked_example():
+    """o = (3, 4): the mean square over the two channels is 12.5, so with
+    eps = 0 the normalised row is (3, 4) / sqrt(12.5) = (3, 4) * sqrt(2) / 5.
+    Weight (2, 1/2), gate logits (0, 0) -> sigmoid 1/2:
+    y = (3 sqrt(2) / 5, 4 sqrt(2) / 5) * (2, 1/2) * 1/2 = (3 sqrt(2) / 5, sqrt(2) / 5)."""
+    O = np.array([[[3.0, 4.0]]])
+    y = orc.rmsnorm_gate(O, np.array([2.0, 0.5]), np.zeros((1, 1, 2)), 0.0)
+    r2 = np.sqrt(2.0)
+    np.testing.assert_allclose(y[0, 0], [3 * r2 / 5, r2 / 5], rtol=1e-15)
+    # large logits saturate the gate: sigmoid(40) = 1 - 4.2e-18, sigmoid(-40) = 4.2e-18
+    y = orc.rmsnorm_gate(O, np.ones(2), np.array([[[40.0, -40.0]]]), 0.0)
+    np.testing.assert_allclose(y[0, 0, 0], 3 * r2 / 5, rtol=1e-15)
+    assert 0 < y[0, 0, 1] < 1e-17
+
+
+def test_epilogue_unit_rms_and_epsilon():
+    """With unit weight and an open gate, every output row has root mean
+    square sqrt(m / (m + eps)), m the row's mean square (1 for eps = 0)."""
+    g = np.random.default_rng(7)
+    O = g.standard_normal((3, 5, 16)) * np.exp(g.standard_normal((3, 5, 1)))
+    m = np.mean(O * O, axis=-1)
+    open_gate = np.full(O.shape, 60.0)
+    for eps in (0.0, 1e-6, 0.3):
+        y = orc.rmsnorm_gate(O, np.ones(16), open_gate, eps)
+        rms = np.sqrt(np.mean(y * y, axis=-1))
+        np.testing.assert_allclose(rms, np.sqrt(m / (m + eps)), rtol=1e-12)
+
+
+def test_epilogue_scale_sign_and_gate_symmetry():
+    """eps = 0: positive rescaling of a row does not change the output and
+    negation negates it; sigmoid(x) + sigmoid(-x) = 1, so the outputs for
+    opposite logits add up to the normalised, weighted row."""
+    g = np.random.default_rng(8)
+    O = g.standard_normal((2, 4, 8))
+    w = 1 + 0.1 * g.standard_normal(8)
+    z = g.standard_normal(O.shape)
+    y = orc.rmsnorm_gate(O, w, z, 0.0)
+    np.testing.assert_allclose(orc.rmsnorm_gate(3.7 * O, w, z, 0.0), y, rtol=1e-13)
+    np.testing.assert_allclose(orc.rmsnorm_gate(-O, w, z, 0.0), -y, rtol=1e-13)
+    both = y + orc.rmsnorm_gate(O, w, -z, 0.0)
+    norm = O / np.sqrt(np.mean(O * O, axis=-1, keepdims=True))
+    np.testing.assert_allclose(both, norm * w, rtol=1e-13)
+
+
+def test_epilogue_keeps_zero_rows():
+    """Anchor rows of the linear branch are zero and stay zero."""
+    O = np.zeros((1, 3, 4))
+    y = orc.rmsnorm_gate(O, np.ones(4), np.zeros(O.shape), 1e-6)
+    assert not y.any()
+
+
+def test_epilogue_inputs_are_deterministic_per_head():
+    cfg = inp.CONFIG_BY_NAME["tiny"]
+    a, b = inp.epilogue_inputs(cfg, 0), inp.epilogue_inputs(cfg, 0)
+    assert np.array_equal(a.gate, b.gate) and np.array_equal(a.weight, b.weight)
+    c = inp.epilogue_inputs(cfg, 1) if cfg.heads > 1 else inp.epilogue_inputs(inp.scaled(cfg, seed=cfg.seed + 1), 0)
+    assert not np.array_equal(a.gate, c.gate)
+    assert a.gate.shape == (cfg.frames, cfg.tokens, cfg.d) and a.weight.shape == (cfg.d,)
