@@ -12,7 +12,12 @@ timing starts.  Prints one JSON line: latent frames/s, algorithmic TFLOP/s,
 a roofline entry for the dominant HBM-bound kernel timed with HIP events on
 the stream it runs on, and the float64 oracle timed on this host's cores.
 
-    python bench.py [--steps K] [--warmup W] [--config h3] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--config h3] [--no-cpu-baseline] [--epilogue]
+
+--epilogue replaces the readout by vda_readout_gated (the readout followed by
+the RMSNorm + sigmoid-gate epilogue of the linear branch, with seeded gate
+logits and norm weights): a measurement of that next step of the path, not
+the default line.
 
 Measurement helpers (used to make the files under profiles/):
 
@@ -42,41 +47,47 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16/f16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 COPY_BYTES = 512 * 1024 * 1024
-KERNELS = ("stats_kernel", "gj_kernel", "scan_kernel", "readout_kernel")
+KERNELS = ("stats_kernel", "gj_kernel", "scan_kernel", "readout_kernel", "readout_gated")
+EPS = 1e-6  # RMSNorm epsilon of the epilogue
 
 
-def algorithmic_work(cfg):
+def algorithmic_work(cfg, epilogue=False):
     """Algorithmic FLOPs and HBM bytes of one step.  Per scanned frame-head:
     2Ud^2 (A) + 2Ud^2 (B) + d^3 (solve) + 2 * 2d^3 (two scan directions)
     + 2 * 2Ud^2 (forward and reverse reads; one read without window
-    exclusion); bytes: Q, K, V (16-bit), beta, alpha, O (16-bit).  Text
-    state once per head: 4 N_text d^2 + d^3 + 2d^3 FLOPs, k_T, v_T, beta_T."""
+    exclusion); bytes: Q, K, V (16-bit), beta, alpha, O (16-bit), plus the
+    gate logits with the epilogue (its few elementwise FLOPs are not
+    counted).  Text state once per head: 4 N_text d^2 + d^3 + 2d^3 FLOPs,
+    k_T, v_T, beta_T."""
     U, d, n, H, Nt = cfg.tokens, cfg.d, cfg.scanned, cfg.heads, cfg.text_tokens
     ib = 4 if cfg.in_dtype == "f32" else 2
     ob = {"f32": 4, "bf16": 2, "f16": 2}[cfg.out_dtype]
     reads = 2 if cfg.window >= 0 else 1
     fl_fh = 4 * U * d * d + d ** 3 + 4 * d ** 3 + reads * 2 * U * d * d
-    by_fh = 3 * U * d * ib + 4 * U + 4 * d + U * d * ob
+    by_fh = 3 * U * d * ib + 4 * U + 4 * d + U * d * ob + (U * d * ib if epilogue else 0)
     fl_text = (4 * Nt * d * d + 3 * d ** 3) if Nt else 0
     by_text = (2 * Nt * d * ib + 4 * Nt) if Nt else 0
     return H * (n * fl_fh + fl_text), H * (n * by_fh + by_text)
 
 
 def kernel_bytes(cfg):
-    """Algorithmic HBM bytes of one launch of the two HBM-bound kernels:
+    """Algorithmic HBM bytes of one launch of the HBM-bound kernels:
     statistics read K, V (16-bit) and beta of every scanned frame and the
     text tokens; the readout reads Q and alpha of every scanned frame and
-    writes every output row (anchor rows are zeros)."""
+    writes every output row (anchor rows are zeros); the gated readout also
+    reads the gate logits of every scanned frame."""
     U, d, n, H, Nt, T = cfg.tokens, cfg.d, cfg.scanned, cfg.heads, cfg.text_tokens, cfg.frames
     ib = 4 if cfg.in_dtype == "f32" else 2
     ob = {"f32": 4, "bf16": 2, "f16": 2}[cfg.out_dtype]
     stats = H * (n * (2 * U * d * ib + 4 * U) + (2 * Nt * d * ib + 4 * Nt))
     read = H * (n * (U * d * ib + 4 * d) + T * U * d * ob)
-    return {"stats_kernel": stats, "readout_kernel": read}
+    gated = read + H * n * U * d * ib + H * d * 4
+    return {"stats_kernel": stats, "readout_kernel": read, "readout_gated": gated}
 
 
 KERNEL_SRC = {"stats_kernel": "vda_prepare.hip", "gj_kernel": "vda_prepare.hip",
-              "scan_kernel": "vda_scan.hip", "readout_kernel": "vda_readout.hip"}
+              "scan_kernel": "vda_scan.hip", "readout_kernel": "vda_readout.hip",
+              "readout_gated": "vda_readout.hip"}
 
 
 def _src_hash(kernel):
@@ -121,6 +132,10 @@ def copy_calibration():
 
 
 def _short(name):
+    """Short name of a profiled kernel; the gated readout is the
+    readout_kernel instantiation with its last template argument true."""
+    if "readout_kernel" in name:
+        return "readout_gated" if ("ELb1E" in name or "true>" in name) else "readout_kernel"
     for k in KERNELS:
         if k in name:
             return k
@@ -151,9 +166,15 @@ def write_traffic(fetch_csv, write_csv, cal_fetch_csv, cal_write_csv):
     cw = _counter_means(cal_write_csv, "WRITE_SIZE")["copy"]
     ff = COPY_BYTES / (cf * 1024.0)
     wf = COPY_BYTES / (cw * 1024.0)
+    # kernels profiled in other runs (e.g. the gated readout) stay as they were
+    try:
+        with open(TRAFFIC_JSON) as fh:
+            kept = json.load(fh).get("kernels", {})
+    except (OSError, ValueError):
+        kept = {}
     out = {"calibration": {"copy_bytes": COPY_BYTES, "fetch_kib": cf, "write_kib": cw,
                            "fetch_factor": round(ff, 4), "write_factor": round(wf, 4)},
-           "kernels": {}}
+           "kernels": {k: v for k, v in kept.items() if k in KERNELS and not (k in f and k in w)}}
     for k in KERNELS:
         if k in f and k in w:
             fb, wb = f[k] * 1024.0 * ff, w[k] * 1024.0 * wf
@@ -167,9 +188,10 @@ def write_traffic(fetch_csv, write_csv, cal_fetch_csv, cal_write_csv):
 
 # ---------------------------------------------------------------- bench --
 
-def cpu_baseline(cfg, heads_in, out0, budget_s=15.0):
+def cpu_baseline(cfg, heads_in, out0, budget_s=15.0, epi_in=None):
     """The float64 oracle, as it stands, on whole heads of the same workload
-    until about budget_s seconds of CPU time are spent (at least one head)."""
+    until about budget_s seconds of CPU time are spent (at least one head);
+    with epi_in, followed by the oracle's readout epilogue."""
     from oracle import vda_oracle as orc
     try:
         from threadpoolctl import threadpool_info
@@ -184,6 +206,8 @@ def cpu_baseline(cfg, heads_in, out0, budget_s=15.0):
         args = [f(x) for x in ("q", "k", "v", "beta", "alpha")] + [f(x) if text else None for x in ("kt", "vt", "bt")]
         c0 = time.perf_counter()
         ref = orc.run_head(cfg.frames, cfg.chunk, cfg.window, cfg.anchors, *args)
+        if epi_in is not None:
+            ref["O"] = orc.rmsnorm_gate(ref["O"], epi_in[h].f64("weight"), epi_in[h].f64("gate"), EPS)
         t_cpu += time.perf_counter() - c0
         done += 1
         if h == 0:
@@ -195,7 +219,8 @@ def cpu_baseline(cfg, heads_in, out0, budget_s=15.0):
     return ({"value": round(cfg.frames * frac / t_cpu, 4), "unit": "frames/s", "cores": int(cores),
              "kind": "oracle",
              "sample": f"{done} of {cfg.heads} heads of the same workload (all {cfg.frames} frames of each), "
-                       f"float64 NumPy/LAPACK, {t_cpu:.1f} s; frames/s scaled by the fraction of heads"},
+                       f"float64 NumPy/LAPACK{' with the readout epilogue' if epi_in is not None else ''}, "
+                       f"{t_cpu:.1f} s; frames/s scaled by the fraction of heads"},
             rel)
 
 
@@ -208,6 +233,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="CPU time budget of the oracle baseline (whole heads)")
+    ap.add_argument("--epilogue", action="store_true",
+                    help="time the readout with the RMSNorm + sigmoid-gate epilogue (vda_readout_gated)")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--traffic", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"))
     args = ap.parse_args()
@@ -234,6 +261,10 @@ def main():
     desc = vda.desc_for(cfg)
     dev = runner.upload(cfg, heads_in, "cuda")
     bufs = runner.allocate(desc, cfg.out_dtype, "cuda")
+    epi_in, gate, norm_w = None, None, None
+    if args.epilogue:
+        epi_in = [inp.epilogue_inputs(cfg, h) for h in range(cfg.heads)]
+        gate, norm_w = runner.upload_epilogue(cfg, epi_in)
     main_s = torch.cuda.current_stream()
 
     # events around each call, on the stream they all run on
@@ -258,7 +289,11 @@ def main():
         vda.vda_scan_bidir(desc, b.ws, x.alpha, None, b.states_f, b.states_r, stream=main_s)
         mark("scans", 1)
         mark("readout", 0)
-        vda.vda_readout(desc, x.q, x.alpha, b.states_f, b.states_r, b.out, stream=main_s)
+        if args.epilogue:
+            vda.vda_readout_gated(desc, x.q, x.alpha, b.states_f, b.states_r, gate, norm_w, EPS, b.out,
+                                  stream=main_s)
+        else:
+            vda.vda_readout(desc, x.q, x.alpha, b.states_f, b.states_r, b.out, stream=main_s)
         mark("readout", 1)
         if record:
             for k in names:
@@ -278,10 +313,12 @@ def main():
     kms = {k: float(np.mean([a.elapsed_time(b) for a, b in ev[k]])) for k in names}
     print(f"[bench] {args.steps} steps: {ms_step:.3f} ms/step; calls {kms}", file=sys.stderr, flush=True)
 
-    flops, nbytes = algorithmic_work(cfg)
+    flops, nbytes = algorithmic_work(cfg, args.epilogue)
     t_s = ms_step / 1e3
     kb = kernel_bytes(cfg)
-    call_of = {"stats_kernel": "stats", "readout_kernel": "readout"}
+    rk = "readout_gated" if args.epilogue else "readout_kernel"
+    kb = {k: kb[k] for k in ("stats_kernel", rk)}
+    call_of = {"stats_kernel": "stats", rk: "readout"}
     dom = max(kb, key=lambda k: kms[call_of[k]])
     ach = kb[dom] / (kms[call_of[dom]] / 1e3) / 1e9
     roofline = {"kernel": dom, "bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
@@ -291,7 +328,7 @@ def main():
     cpu, rel = None, None
     if not args.no_cpu_baseline:
         out0 = bufs.out[0].float().cpu().numpy().astype(np.float64)
-        cpu, rel = cpu_baseline(cfg, heads_in, out0, args.cpu_seconds)
+        cpu, rel = cpu_baseline(cfg, heads_in, out0, args.cpu_seconds, epi_in)
 
     out = {
         "metric": "VDA scan+readout latent frames/s and % of MI355X bf16 MFMA peak",
@@ -308,7 +345,9 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{cfg.name}: {cfg.heads} heads, d={cfg.d}, {cfg.frames} latent frames "
                                f"({cfg.anchors * 2} anchors, chunks of {cfg.chunk}, window +-{cfg.window} "
-                               f"chunk), U={cfg.tokens}, {cfg.text_tokens} text tokens",
+                               f"chunk), U={cfg.tokens}, {cfg.text_tokens} text tokens"
+                               + (", readout epilogue (RMSNorm + sigmoid gate)" if args.epilogue else ""),
+                   "epilogue": bool(args.epilogue),
                    "heads": cfg.heads, "d": cfg.d, "frames": cfg.frames, "tokens": cfg.tokens,
                    "text_tokens": cfg.text_tokens, "in_dtype": cfg.in_dtype, "out_dtype": cfg.out_dtype,
                    "state_dtype": "f32", "global_batch": 1, "seq_len": cfg.frames * cfg.tokens,

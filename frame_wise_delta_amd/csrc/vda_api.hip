@@ -5,6 +5,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <cmath>
 #include <mutex>
 
 #include "vda.h"
@@ -118,6 +119,7 @@ const char* vda_status_string(int code) {
     case VDA_ERR_WORKSPACE: return "workspace too small";
     case VDA_ERR_HIP: return "HIP error";
     case VDA_ERR_DEVICE: return "no usable gfx950 device";
+    case VDA_ERR_VALUE: return "argument out of range";
     default: return "unknown status";
   }
 }
@@ -265,6 +267,9 @@ int read_args(const vda_desc* desc, const void* q, const float* alpha, const flo
   a.w = s.w;
   a.count = s.count;
   a.bridge = (desc->flags & VDA_NO_BRIDGE) ? 0 : 1;
+  a.gate = nullptr;
+  a.normw = nullptr;
+  a.eps = 0.f;
   return VDA_OK;
 }
 
@@ -378,6 +383,27 @@ int vda_readout(const vda_desc* desc, const void* q, const float* alpha, const f
   if (rc) return rc;
   if (!any) return ok();
   vda::launch_readout(a, s.d, desc->in_dtype, desc->out_dtype, static_cast<hipStream_t>(stream));
+  return launch_status();
+}
+
+int vda_readout_gated(const vda_desc* desc, const void* q, const float* alpha, const float* states_fwd,
+                      const float* states_rev, const void* gate, const float* norm_weight, float eps, void* out,
+                      void* stream) {
+  Shape s;
+  vda::ReadArgs a;
+  bool any = false;
+  int rc = read_args(desc, q, alpha, states_fwd, states_rev, out, s, a, any);
+  if (rc) return rc;
+  if (any && s.n > 0 && (!gate || !norm_weight)) return fail(VDA_ERR_NULL, "gate or norm_weight is NULL");
+  if (!aligned16(gate) || !aligned16(norm_weight)) return fail(VDA_ERR_ALIGN, "gate, norm_weight need 16-byte alignment");
+  if (!(eps > 0.f) || !std::isfinite(eps)) return fail(VDA_ERR_VALUE, "eps must be positive and finite");
+  rc = check_device();
+  if (rc) return rc;
+  if (!any) return ok();
+  a.gate = gate;
+  a.normw = norm_weight;
+  a.eps = eps;
+  vda::launch_readout_gated(a, s.d, desc->in_dtype, desc->out_dtype, static_cast<hipStream_t>(stream));
   return launch_status();
 }
 

@@ -45,6 +45,10 @@ struct ReadArgs {
   void* out;              // [H][T][U][d]
   int H, T, U, a, n, P, C, w, count;
   int bridge;
+  // readout epilogue (gated launches only): y = rmsnorm(o) * normw * sigmoid(gate)
+  const void* gate;       // [H][T][U][d] logits, input dtype
+  const float* normw;     // [H][d]
+  float eps;
 };
 
 int launch_stats(const PrepArgs& a, int d, bool in_f32, hipStream_t stream);
@@ -52,5 +56,7 @@ int launch_gj(const PrepArgs& a, int d, hipStream_t stream);
 void launch_clear_status(int* status, hipStream_t stream);
 int launch_scan(const ScanPair& p, int d, hipStream_t stream);
 int launch_readout(const ReadArgs& a, int d, int in_dtype, int out_dtype, hipStream_t stream);
+// The readout with the RMSNorm + sigmoid-gate epilogue (a.gate, a.normw, a.eps).
+int launch_readout_gated(const ReadArgs& a, int d, int in_dtype, int out_dtype, hipStream_t stream);
 
 }  // namespace vda

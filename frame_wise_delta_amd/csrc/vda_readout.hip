@@ -23,6 +23,17 @@
 // tile's loads are issued before the current tile's MFMAs) and each
 // wavefront computes O^T = W Q^T on MFMA (2 products per tile for bf16 Q,
 // 3 for float32 Q split hi/lo), accumulating in float32.
+//
+// The gated launch adds the epilogue of the linear branch (same page,
+// method-steps section, step (5): the read is RMS-normalised, then gated by a
+// sigmoid; core-method section, paragraph 1: the linear branch is normalised
+// before its gate):  y_c = o_c / sqrt(mean_c o_c^2 + eps) * w_c * sigmoid(g_c)
+// over the d value channels of each token.  A wavefront holds a quarter of a
+// token's channels, so each 64-token tile takes two passes over its MFMAs:
+// the first leaves per-token partial sums of squares in LDS, and after one
+// extra barrier the second recomputes the products (cheaper than keeping
+// them, which would cost a workgroup per CU) and stores the normalised,
+// gated outputs.  The tile's gate logits are loaded before its products.
 #include "vda_common.h"
 #include "vda_kernels.h"
 
@@ -30,7 +41,7 @@ namespace vda {
 
 namespace {
 
-constexpr int kQT = 128;  // tokens per LDS tile
+constexpr int kQT = 128;  // tokens per LDS tile (64 in the gated launch)
 
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
@@ -106,24 +117,87 @@ struct QFrag<InF32> {
   }
 };
 
+// N consecutive gate logits of one token, kept as loaded until used.
+template <class TIN, int N>
+struct GateRaw;
+template <>
+struct GateRaw<InBF16, 8> {
+  uint4 r;
+  __device__ __forceinline__ void load(const void* base, size_t idx) {
+    r = *reinterpret_cast<const uint4*>(static_cast<const u16*>(base) + idx);
+  }
+  __device__ __forceinline__ float get(int e) const {
+    const uint32_t w = (e >> 1) == 0 ? r.x : (e >> 1) == 1 ? r.y : (e >> 1) == 2 ? r.z : r.w;
+    return bf16_bits_to_f32((e & 1) ? (w >> 16) : (w & 0xffffu));
+  }
+};
+template <>
+struct GateRaw<InBF16, 4> {
+  uint2 r;
+  __device__ __forceinline__ void load(const void* base, size_t idx) {
+    r = *reinterpret_cast<const uint2*>(static_cast<const u16*>(base) + idx);
+  }
+  __device__ __forceinline__ float get(int e) const {
+    const uint32_t w = (e >> 1) == 0 ? r.x : r.y;
+    return bf16_bits_to_f32((e & 1) ? (w >> 16) : (w & 0xffffu));
+  }
+};
+template <>
+struct GateRaw<InF32, 8> {
+  float4 r[2];
+  __device__ __forceinline__ void load(const void* base, size_t idx) {
+    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(base) + idx);
+    r[0] = p[0];
+    r[1] = p[1];
+  }
+  __device__ __forceinline__ float get(int e) const {
+    const float4 v = r[e >> 2];
+    return (e & 3) == 0 ? v.x : (e & 3) == 1 ? v.y : (e & 3) == 2 ? v.z : v.w;
+  }
+};
+template <>
+struct GateRaw<InF32, 4> {
+  float4 r;
+  __device__ __forceinline__ void load(const void* base, size_t idx) {
+    r = *reinterpret_cast<const float4*>(static_cast<const float*>(base) + idx);
+  }
+  __device__ __forceinline__ float get(int e) const { return e == 0 ? r.x : e == 1 ? r.y : e == 2 ? r.z : r.w; }
+};
+
+// Sum of v over the four 16-lane rows of the wavefront, in every lane
+// (permlane32_swap pairs rows (0, 2) and (1, 3), permlane16_swap then (0, 1)).
+__device__ __forceinline__ float sum_rows4(float v) {
+  const unsigned b = __float_as_uint(v);
+  const auto p = __builtin_amdgcn_permlane32_swap(b, b, false, false);
+  const float s = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+  const unsigned c = __float_as_uint(s);
+  const auto q = __builtin_amdgcn_permlane16_swap(c, c, false, false);
+  return __uint_as_float(q[0]) + __uint_as_float(q[1]);
+}
+
+__device__ __forceinline__ float sigmoid_fast(float x) {
+  return __builtin_amdgcn_rcpf(1.f + __expf(-x));
+}
+
 }  // namespace
 
-template <int D, class TIN, int OUT>
-__global__ __launch_bounds__(kThreads, 2) void readout_kernel(ReadArgs a) {
+template <int D, class TIN, int OUT, bool GATED>
+__global__ __launch_bounds__(kThreads, GATED ? 3 : 2) void readout_kernel(ReadArgs a) {
   using T = typename TIN::T;
   constexpr int VT = D / 16;                         // value-channel tiles
   constexpr int NVT = (VT + 3) / 4;                  // tiles per wavefront
   constexpr int KS = D / 32 > 0 ? D / 32 : 1;        // MFMA k-steps
+  constexpr int QT = GATED ? 64 : kQT;               // tokens per LDS tile
   constexpr int PITCH = D * TIN::bytes + 16;         // LDS bytes per token row
   constexpr int CH = D * TIN::bytes / 16;            // 16-byte chunks per token row
-  constexpr int PER = (kQT * CH + kThreads - 1) / kThreads;  // chunks per thread per tile
+  constexpr int PER = (QT * CH + kThreads - 1) / kThreads;  // chunks per thread per tile
   // d = 128: the two tiles of wavefront w interleave its 32 value channels so
   // that a lane's outputs of one token are 8 consecutive channels
   constexpr bool kPair = VT == 8;
   auto chan = [](int w, int i, int r) {
     return kPair ? 32 * w + 8 * (r >> 2) + 4 * i + (r & 3) : 16 * (w + 4 * i) + r;
   };
-  __shared__ __attribute__((aligned(16))) char sQ[kQT * PITCH];
+  __shared__ __attribute__((aligned(16))) char sQ[QT * PITCH];
   __shared__ float sBf[D], sBr[D];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -151,7 +225,7 @@ __global__ __launch_bounds__(kThreads, 2) void readout_kernel(ReadArgs a) {
     for (int j = 0; j < PER; ++j) {
       const int i = tid + j * kThreads;
       const int r = i / CH, ch = i - r * CH;
-      pre[j] = (i < kQT * CH && u0 + r < a.U)
+      pre[j] = (i < QT * CH && u0 + r < a.U)
                    ? reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(qh + (size_t)(u0 + r) * D))[ch]
                    : make_uint4(0, 0, 0, 0);
     }
@@ -234,20 +308,122 @@ __global__ __launch_bounds__(kThreads, 2) void readout_kernel(ReadArgs a) {
     }
   }
 
+  // ---- gated epilogue: RMSNorm weights of this lane's channels
+  constexpr int GN = kPair ? 8 : 4;  // consecutive channels per gate / output access
+  constexpr int NG = kPair ? 1 : NVT;
+  constexpr int NSUB = QT / 16;
+  float nw[NVT][4];
+  if constexpr (GATED) {
+#pragma unroll
+    for (int i = 0; i < NVT; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        nw[i][e] = (wave + 4 * i < VT) ? a.normw[(size_t)h * D + chan(wave, i, 4 * lg + e)] : 0.f;
+  }
+  __shared__ float sSq[GATED ? 4 * QT : 1];  // per-wavefront partial sums of squares per token
+
+  // One tile with the epilogue: the per-token sums of squares of the four
+  // wavefronts meet in LDS, then y = o * rsqrt(mean o^2 + eps) * w *
+  // sigmoid(g) is stored.
+  auto gated_tile = [&](int u0) {
+    GateRaw<TIN, GN> graw[NSUB][NG];
+    // gate logits of the tile first: they arrive during the products
+#pragma unroll
+    for (int st = 0; st < NSUB; ++st) {
+      const int u = u0 + 16 * st + lr;
+      if (wave < VT && u < a.U) {
+        if constexpr (kPair) {
+          graw[st][0].load(a.gate, frame_off + (size_t)u * D + 32 * wave + 8 * lg);
+        } else {
+#pragma unroll
+          for (int i = 0; i < NVT; ++i)
+            if (wave + 4 * i < VT) graw[st][i].load(a.gate, frame_off + (size_t)u * D + 16 * (wave + 4 * i) + 4 * lg);
+        }
+      }
+    }
+    auto products = [&](int st, f32x4 (&acc)[NVT]) {
+      const int ul = 16 * st + lr;
+#pragma unroll
+      for (int i = 0; i < NVT; ++i) acc[i] = f32x4{0, 0, 0, 0};
+      if (wave < VT && u0 + 16 * st < a.U) {
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) {
+          const int k0 = 32 * kk + 8 * lg;
+          QFrag<TIN> qf;
+          qf.load(sQ + ul * PITCH, k0, k0 < D);
+#pragma unroll
+          for (int i = 0; i < NVT; ++i) {
+            if (wave + 4 * i < VT) {
+              acc[i] = mfma_bf16(wh[i][kk], qf.hi, acc[i]);
+              acc[i] = mfma_bf16(wl[i][kk], qf.hi, acc[i]);
+              if constexpr (TIN::bytes == 4) acc[i] = mfma_bf16(wh[i][kk], qf.lo, acc[i]);
+            }
+          }
+        }
+      }
+    };
+    // pass 1: per-token sums of squares of this wavefront's channels
+#pragma unroll
+    for (int st = 0; st < NSUB; ++st) {
+      f32x4 acc[NVT];
+      products(st, acc);
+      float ss = 0.f;
+#pragma unroll
+      for (int i = 0; i < NVT; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ss = fmaf(acc[i][e], acc[i][e], ss);
+      ss = sum_rows4(ss);
+      if (lg == 0) sSq[wave * QT + 16 * st + lr] = ss;
+    }
+    lds_barrier();
+    // pass 2: the products again, normalised, gated and stored
+    if (wave < VT) {
+#pragma unroll
+      for (int st = 0; st < NSUB; ++st) {
+        const int ul = 16 * st + lr;
+        const int u = u0 + ul;
+        f32x4 acc[NVT];
+        products(st, acc);
+        if (u >= a.U) continue;
+        const float tot = sSq[ul] + sSq[QT + ul] + sSq[2 * QT + ul] + sSq[3 * QT + ul];
+        const float rs = __builtin_amdgcn_rsqf(tot * (1.f / D) + a.eps);
+        f32x4 y[NVT];
+#pragma unroll
+        for (int i = 0; i < NVT; ++i)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float g = kPair ? graw[st][0].get(4 * i + e) : graw[st][i].get(e);
+            y[i][e] = acc[i][e] * rs * nw[i][e] * sigmoid_fast(g);
+          }
+        if constexpr (kPair) {
+          OutT<OUT>::store8(a.out, frame_off + (size_t)u * D + 32 * wave + 8 * lg, y[0], y[1]);
+        } else {
+#pragma unroll
+          for (int i = 0; i < NVT; ++i) {
+            const int vt = wave + 4 * i;
+            if (vt < VT) OutT<OUT>::store4(a.out, frame_off + (size_t)u * D + 16 * vt + 4 * lg, y[i]);
+          }
+        }
+      }
+    }
+  };
+
   // ---- token tiles: the next tile's loads are in flight during the MFMAs
-  for (int u0 = 0; u0 < a.U; u0 += kQT) {
+  for (int u0 = 0; u0 < a.U; u0 += QT) {
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
       const int i = tid + j * kThreads;
-      if (i < kQT * CH) {
+      if (i < QT * CH) {
         const int r = i / CH, ch = i - r * CH;
         *reinterpret_cast<uint4*>(sQ + r * PITCH + 16 * ch) = pre[j];
       }
     }
     lds_barrier();
-    if (u0 + kQT < a.U) fetch(u0 + kQT);
-    if (wave < VT) {
-      const int nsub = (a.U - u0) >= kQT ? kQT / 16 : (a.U - u0 + 15) / 16;
+    if (u0 + QT < a.U) fetch(u0 + QT);
+    if constexpr (GATED) {
+      gated_tile(u0);
+    } else if (wave < VT) {
+      const int nsub = (a.U - u0) >= QT ? QT / 16 : (a.U - u0 + 15) / 16;
       for (int st = 0; st < nsub; ++st) {
         const int ul = 16 * st + lr;  // token of this lane's operand column
         f32x4 acc[NVT];
@@ -285,11 +461,12 @@ __global__ __launch_bounds__(kThreads, 2) void readout_kernel(ReadArgs a) {
   }
 }
 
-int launch_readout(const ReadArgs& a, int d, int in_dtype, int out_dtype, hipStream_t stream) {
+template <bool GATED>
+static int launch_readout_impl(const ReadArgs& a, int d, int in_dtype, int out_dtype, hipStream_t stream) {
   if (a.H == 0 || a.T == 0) return 0;
   dim3 grid((unsigned)(a.H * a.T)), block(kThreads);
 #define VDA_RD3(DD, TI, OO) \
-  if (out_dtype == OO) { hipLaunchKernelGGL((readout_kernel<DD, TI, OO>), grid, block, 0, stream, a); return 0; }
+  if (out_dtype == OO) { hipLaunchKernelGGL((readout_kernel<DD, TI, OO, GATED>), grid, block, 0, stream, a); return 0; }
 #define VDA_RD(DD)                                                                 \
   if (d == DD) {                                                                   \
     if (in_dtype == VDA_F32) {                                                     \
@@ -303,6 +480,14 @@ int launch_readout(const ReadArgs& a, int d, int in_dtype, int out_dtype, hipStr
 #undef VDA_RD
 #undef VDA_RD3
   return -1;
+}
+
+int launch_readout(const ReadArgs& a, int d, int in_dtype, int out_dtype, hipStream_t stream) {
+  return launch_readout_impl<false>(a, d, in_dtype, out_dtype, stream);
+}
+
+int launch_readout_gated(const ReadArgs& a, int d, int in_dtype, int out_dtype, hipStream_t stream) {
+  return launch_readout_impl<true>(a, d, in_dtype, out_dtype, stream);
 }
 
 }  // namespace vda

@@ -127,3 +127,24 @@ def run(cfg: inp.Config, heads_in, device="cuda", s_init=None, fused=False, **de
 
 def out_f64(bufs: Buffers) -> np.ndarray:
     return bufs.out.float().cpu().numpy().astype(np.float64)
+
+
+def upload_epilogue(cfg: inp.Config, epi_in, device="cuda"):
+    """Stack per-head epilogue inputs (``inputs.epilogue_inputs``) into device
+    tensors: gate logits [H, T, U, d] in the input dtype, weights [H, d]."""
+    gate = _dev(np.stack([e.gate for e in epi_in]), device)
+    weight = _dev(np.stack([e.weight for e in epi_in]), device)
+    return gate, weight
+
+
+def readout_gated(desc: vda.vda_desc, dev: DeviceInputs, bufs: Buffers, gate, weight, eps: float,
+                  out_dtype: str, device="cuda"):
+    """Run vda_readout_gated on the states in ``bufs`` into a new output
+    tensor, synchronise and return it."""
+    import torch
+    out = torch.empty(tuple(bufs.out.shape), dtype=getattr(torch, _OUT_TORCH[out_dtype]), device=device)
+    d = vda.vda_desc.from_buffer_copy(desc)
+    d.out_dtype = vda.DTYPES[out_dtype]
+    vda.vda_readout_gated(d, dev.q, dev.alpha, bufs.states_f, bufs.states_r, gate, weight, eps, out)
+    torch.cuda.synchronize()
+    return out

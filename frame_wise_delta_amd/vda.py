@@ -23,6 +23,7 @@ VDA_ERR_ALIGN = -4
 VDA_ERR_WORKSPACE = -5
 VDA_ERR_HIP = -6
 VDA_ERR_DEVICE = -7
+VDA_ERR_VALUE = -8
 
 VDA_F32, VDA_BF16, VDA_F16 = 0, 1, 2
 VDA_NO_BRIDGE = 1
@@ -32,7 +33,8 @@ DTYPES = {"f32": VDA_F32, "bf16": VDA_BF16, "f16": VDA_F16}
 
 EXPORTS = ("vda_workspace_bytes", "vda_state_count", "vda_index_map", "vda_prepare_frames",
            "vda_frame_stats", "vda_factor_frames", "vda_scan_fwd", "vda_scan_rev", "vda_scan_bidir",
-           "vda_readout", "vda_forward", "vda_device_status", "vda_status_string", "vda_last_error")
+           "vda_readout", "vda_readout_gated", "vda_forward", "vda_device_status", "vda_status_string",
+           "vda_last_error")
 
 
 class vda_desc(ctypes.Structure):
@@ -77,6 +79,8 @@ def load(path: str | None = None):
         "vda_scan_rev": [D, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p],
         "vda_scan_bidir": [D, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p],
         "vda_readout": [D, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p],
+        "vda_readout_gated": [D, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_float,
+                              c_void_p, c_void_p],
         "vda_forward": [D, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                         c_void_p, c_void_p, c_size_t, c_void_p, c_void_p, c_void_p, c_void_p],
         "vda_device_status": [D, c_void_p, c_void_p, POINTER(c_int32)],
@@ -198,6 +202,12 @@ def vda_scan_bidir(desc, ws, alpha, s_init, states_fwd, states_rev, stream=None)
 def vda_readout(desc, q, alpha, states_fwd, states_rev, out, stream=None):
     _check(load().vda_readout(ctypes.byref(desc), _ptr(q), _ptr(alpha), _ptr(states_fwd),
                               _ptr(states_rev), _ptr(out), _stream(stream)))
+
+
+def vda_readout_gated(desc, q, alpha, states_fwd, states_rev, gate, norm_weight, eps, out, stream=None):
+    _check(load().vda_readout_gated(ctypes.byref(desc), _ptr(q), _ptr(alpha), _ptr(states_fwd),
+                                    _ptr(states_rev), _ptr(gate), _ptr(norm_weight), float(eps), _ptr(out),
+                                    _stream(stream)))
 
 
 def vda_forward(desc, q, k, v, beta, alpha, k_text, v_text, beta_text, ws, states_fwd, states_rev, out,

@@ -59,7 +59,8 @@ enum {
   VDA_ERR_ALIGN = -4,     /* a pointer is not 16-byte aligned */
   VDA_ERR_WORKSPACE = -5, /* workspace too small */
   VDA_ERR_HIP = -6,       /* a HIP runtime call or kernel launch failed */
-  VDA_ERR_DEVICE = -7     /* no usable gfx950 device */
+  VDA_ERR_DEVICE = -7,    /* no usable gfx950 device */
+  VDA_ERR_VALUE = -8      /* a scalar argument is out of range */
 };
 
 /* element types */
@@ -175,6 +176,21 @@ int vda_scan_bidir(const vda_desc* desc, const void* ws, const float* alpha, con
  *  q [H][T][U][d] in_dtype; out [H][T][U][d] out_dtype (every element written). */
 int vda_readout(const vda_desc* desc, const void* q, const float* alpha, const float* states_fwd,
                 const float* states_rev, void* out, void* stream);
+
+/* The readout followed by the epilogue of the linear branch [VDN 方法步骤详情
+ * step (5): the read is RMS-normalised and then passes a sigmoid gate;
+ * VDN 核心方法 para 1: the linear branch is normalised before its gate].  For
+ * every token of every scanned frame, over its d value channels c,
+ *   y_c = o_c / sqrt(mean_c' o_c'^2 + eps) * norm_weight[h][c] * sigmoid(gate_c)
+ * where o is what vda_readout computes from the same q, alpha and states.
+ *  gate [H][T][U][d] logits in in_dtype (a per-channel gate projection of the
+ *    layer input, computed by the caller); norm_weight [H][d] float32;
+ *  eps > 0 and finite, else VDA_ERR_VALUE;
+ *  out [H][T][U][d] out_dtype, every element written; anchor rows are zero.
+ * The other arguments, layouts and errors are those of vda_readout. */
+int vda_readout_gated(const vda_desc* desc, const void* q, const float* alpha, const float* states_fwd,
+                      const float* states_rev, const void* gate, const float* norm_weight, float eps, void* out,
+                      void* stream);
 
 /* The whole path in one call: vda_prepare_frames, vda_scan_bidir (S_init =
  * S^T from the text tokens, or zero) and vda_readout, with the same

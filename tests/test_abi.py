@@ -108,6 +108,16 @@ def test_null_and_workspace_checks_precede_any_device_call():
     assert rc == vda.VDA_ERR_NULL  # windowed readout needs the reverse states
     rc = lib.vda_device_status(ctypes.byref(d), None, None, None)
     assert rc == vda.VDA_ERR_NULL
+    # gated readout: its own pointers and eps are checked too
+    rc = lib.vda_readout_gated(ctypes.byref(d), fake, fake, fake, fake, None, fake, 1e-6, fake, None)
+    assert rc == vda.VDA_ERR_NULL
+    rc = lib.vda_readout_gated(ctypes.byref(d), fake, fake, fake, fake, fake, None, 1e-6, fake, None)
+    assert rc == vda.VDA_ERR_NULL
+    rc = lib.vda_readout_gated(ctypes.byref(d), fake, fake, fake, fake, fake + 8, fake, 1e-6, fake, None)
+    assert rc == vda.VDA_ERR_ALIGN
+    for eps in (0.0, -1e-6, float("nan"), float("inf")):
+        rc = lib.vda_readout_gated(ctypes.byref(d), fake, fake, fake, fake, fake, fake, eps, fake, None)
+        assert rc == vda.VDA_ERR_VALUE, eps
 
 
 def test_valid_call_without_gpu_reports_no_device():
@@ -124,10 +134,12 @@ def test_valid_call_without_gpu_reports_no_device():
     assert rc == vda.VDA_ERR_DEVICE
     rc = lib.vda_factor_frames(ctypes.byref(d), fake, wsb, None)
     assert rc == vda.VDA_ERR_DEVICE
+    rc = lib.vda_readout_gated(ctypes.byref(d), fake, fake, fake, fake, fake, fake, 1e-6, fake, None)
+    assert rc == vda.VDA_ERR_DEVICE
 
 
 def test_status_strings():
-    for code in range(0, -8, -1):
+    for code in range(0, -9, -1):
         assert vda.vda_status_string(code) not in ("", "unknown status")
     assert vda.vda_status_string(-99) == "unknown status"
 
