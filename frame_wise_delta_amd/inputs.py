@@ -20,6 +20,8 @@ these draws stand in for them:
 * alpha: lo + (1 - lo) * U(0, 1) per frame and channel (lo = 0.9, or 0.97 for
          the long-video configuration)
 * text tokens (k_T, v_T, beta_T) follow the same laws as video tokens.
+* raw projections for the fused prep (``raw_head_inputs``): the same draws
+  with q, k not normalised and beta, alpha stored as logits;
 * readout epilogue (``epilogue_inputs``): gate logits N(0, 1) per frame,
   token and channel; RMSNorm weight 1 + 0.1 N(0, 1) per channel.
 
@@ -212,6 +214,35 @@ def epilogue_inputs(cfg: Config, head: int) -> EpilogueInputs:
     gate = store(_rng(cfg, _GATE, head).standard_normal((T, U, d)), cfg.in_dtype)
     weight = (1.0 + 0.1 * _rng(cfg, _NORMW, head).standard_normal(d)).astype(np.float32)
     return EpilogueInputs(dtype=cfg.in_dtype, gate=gate, weight=weight)
+
+
+def raw_head_inputs(cfg: Config, head: int) -> HeadInputs:
+    """Raw projections for the fused prep: the same draws as head_inputs
+    but q, k and the text keys are not normalised, and beta, alpha and the
+    text beta are stored as logits (log(p / (1 - p)) of the usual gates,
+    computed in float64 and stored as float32)."""
+    T, U, d, nt = cfg.frames, cfg.tokens, cfg.d, cfg.text_tokens
+    dt = cfg.in_dtype
+    logit = lambda p: np.log(p / (1.0 - p))
+    lo = cfg.alpha_lo
+    out = dict(
+        dtype=dt,
+        q=store(_rng(cfg, _Q, head).standard_normal((T, U, d)), dt),
+        k=store(_rng(cfg, _K, head).standard_normal((T, U, d)), dt),
+        v=store(_rng(cfg, _V, head).standard_normal((T, U, d)), dt),
+        beta=_rng(cfg, _BETA, head).standard_normal((T, U)).astype(np.float32),
+        alpha=logit(lo + (1.0 - lo) * _rng(cfg, _ALPHA, head).random((T, d))).astype(np.float32),
+        kt=np.zeros((0, d), np.float32), vt=np.zeros((0, d), np.float32), bt=np.zeros((0,), np.float32))
+    if nt > 0:
+        out["kt"] = store(_rng(cfg, _KT, head).standard_normal((nt, d)), dt)
+        out["vt"] = store(_rng(cfg, _VT, head).standard_normal((nt, d)), dt)
+        out["bt"] = _rng(cfg, _BT, head).standard_normal((nt,)).astype(np.float32)
+    return HeadInputs(**out)
+
+
+def all_raw_heads(cfg: Config, heads=None):
+    heads = list(range(cfg.heads)) if heads is None else list(heads)
+    return [raw_head_inputs(cfg, h) for h in heads]
 
 
 def all_heads(cfg: Config, heads=None, workers: int | None = None,

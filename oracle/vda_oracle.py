@@ -40,6 +40,9 @@ Readings of points the page leaves open:
   read by the linear branch (their output rows are zero).
 * With ``window = -1`` (no exclusion) the readout of frame t is S^f_t q where
   S^f_t includes frame t's own write.
+* Prep: q and k are normalised as x / sqrt(||x||^2 + eps) per token
+  (eps = 1e-6); the write gate is beta = sigmoid(logit) per token and the
+  decay gate alpha = sigmoid(logit) per frame and channel.
 * Epilogue: RMSNorm over the d_v channels of each token with a per-head
   weight and epsilon, then an elementwise sigmoid gate on per-channel logits
   (which come from the layer input and are given here).
@@ -175,6 +178,29 @@ def readout_full(Q, states_f, frame_chunk, anchors):
             continue
         O[t] = Q[t] @ states_f[t - a + 1].T
     return O
+
+
+# ------------------------------------------------------------------ prep --
+
+def l2_normalise(X, eps):
+    """x / sqrt(||x||^2 + eps) over the last axis [VDN 方法步骤详情 step (2):
+    Q and K are L2-normalised]."""
+    return X / np.sqrt(np.sum(X * X, axis=-1, keepdims=True) + eps)
+
+
+def sigmoid(Z):
+    return 1.0 / (1.0 + np.exp(-Z))
+
+
+def prep(q, k, beta_logit, alpha_logit, kt=None, bt_logit=None, eps=1e-6):
+    """Inputs of the linear branch from raw projections [VDN 方法步骤详情
+    step (2): Q/K L2 normalisation, per-token write gate beta_{t,u} and
+    per-frame decay gate alpha_t]: q and k (and the text keys) normalised per
+    token, beta = sigmoid(beta logit) per token, alpha = sigmoid(alpha logit)
+    per frame and channel.  Returns (q, k, beta, alpha, kt, bt)."""
+    kt_n = None if kt is None else l2_normalise(kt, eps)
+    bt_n = None if bt_logit is None else sigmoid(bt_logit)
+    return l2_normalise(q, eps), l2_normalise(k, eps), sigmoid(beta_logit), sigmoid(alpha_logit), kt_n, bt_n
 
 
 # ------------------------------------------------------------- epilogue --

@@ -423,3 +423,61 @@ def test_epilogue_inputs_are_deterministic_per_head():
     c = inp.epilogue_inputs(cfg, 1) if cfg.heads > 1 else inp.epilogue_inputs(inp.scaled(cfg, seed=cfg.seed + 1), 0)
     assert not np.array_equal(a.gate, c.gate)
     assert a.gate.shape == (cfg.frames, cfg.tokens, cfg.d) and a.weight.shape == (cfg.d,)
+
+
+# ------------------------------------------------------------ prep (f2) --
+
+def test_prep_hand_worked_example():
+    """(3, 4) normalises to (0.6, 0.8) with eps = 0; sigmoid(0) = 1/2 and
+    sigmoid(log 3) = 3/4."""
+    q, k, b, a, _, _ = orc.prep(np.array([[3.0, 4.0]]), np.array([[0.0, 2.0]]), np.array([0.0]),
+                                np.array([np.log(3.0)]), eps=0.0)
+    np.testing.assert_allclose(q, [[0.6, 0.8]], rtol=1e-15)
+    np.testing.assert_allclose(k, [[0.0, 1.0]], rtol=1e-15)
+    np.testing.assert_allclose(b, [0.5], rtol=1e-15)
+    np.testing.assert_allclose(a, [0.75], rtol=1e-15)
+
+
+def test_prep_norms_and_gate_ranges():
+    g = np.random.default_rng(11)
+    X = g.standard_normal((5, 7, 16)) * 3
+    for eps in (0.0, 1e-6, 2.0):
+        Y = orc.l2_normalise(X, eps)
+        n2 = np.sum(X * X, axis=-1)
+        np.testing.assert_allclose(np.sum(Y * Y, axis=-1), n2 / (n2 + eps), rtol=1e-13)
+    z = g.standard_normal(100) * 5
+    s = orc.sigmoid(z)
+    assert np.all((s > 0) & (s < 1))
+    np.testing.assert_allclose(s + orc.sigmoid(-z), 1.0, rtol=1e-15)
+
+
+def test_prep_makes_the_branch_invariant_to_q_k_scale():
+    """With normalisation (eps = 0), rescaling the raw q and k rows by any
+    positive factors leaves the whole branch unchanged."""
+    cfg = inp.CONFIG_BY_NAME["tiny"]
+    h = inp.raw_head_inputs(cfg, 0)
+    f = h.f64
+    g = np.random.default_rng(12)
+    cq = np.exp(g.standard_normal((cfg.frames, cfg.tokens, 1)))
+    ck = np.exp(g.standard_normal((cfg.frames, cfg.tokens, 1)))
+    ckt = np.exp(g.standard_normal((cfg.text_tokens, 1)))
+    runs = []
+    for sq, sk, skt in ((1.0, 1.0, 1.0), (cq, ck, ckt)):
+        q, k, b, a, kt, bt = orc.prep(sq * f("q"), sk * f("k"), f("beta"), f("alpha"), skt * f("kt"), f("bt"),
+                                      eps=0.0)
+        runs.append(orc.run_head(cfg.frames, cfg.chunk, cfg.window, cfg.anchors, q, k, f("v"), b, a, kt, f("vt"),
+                                 bt)["O"])
+    np.testing.assert_allclose(runs[1], runs[0], rtol=1e-10, atol=1e-12)
+
+
+def test_raw_inputs_are_the_usual_draws_before_prep():
+    """raw_head_inputs draws the same numbers as head_inputs: after the
+    oracle's prep (eps = 0) the gates match to float32 rounding and the
+    normalised keys match the stored unit keys to their rounding."""
+    cfg = inp.CONFIG_BY_NAME["tiny"]
+    raw, ref = inp.raw_head_inputs(cfg, 0), inp.head_inputs(cfg, 0)
+    _, _, b, a, _, bt = orc.prep(raw.f64("q"), raw.f64("k"), raw.f64("beta"), raw.f64("alpha"),
+                                 raw.f64("kt"), raw.f64("bt"), eps=0.0)
+    np.testing.assert_allclose(b, ref.f64("beta"), rtol=1e-6)
+    np.testing.assert_allclose(a, ref.f64("alpha"), rtol=1e-6)
+    np.testing.assert_allclose(bt, ref.f64("bt"), rtol=1e-6)
