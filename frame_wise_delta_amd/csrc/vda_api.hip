@@ -55,7 +55,7 @@ int check_desc(const vda_desc* desc, Shape* s) {
   if (q.out_dtype != VDA_F32 && q.out_dtype != VDA_BF16 && q.out_dtype != VDA_F16)
     return fail(VDA_ERR_DTYPE, "out_dtype = %d (VDA_F32, VDA_BF16 or VDA_F16)", q.out_dtype);
   if (!(q.text_init_scale == q.text_init_scale)) return fail(VDA_ERR_SHAPE, "text_init_scale is NaN");
-  if (q.flags & ~(uint32_t)VDA_NO_BRIDGE) return fail(VDA_ERR_SHAPE, "unknown flags 0x%x", q.flags);
+  if (q.flags & ~(uint32_t)(VDA_NO_BRIDGE | VDA_PREP)) return fail(VDA_ERR_SHAPE, "unknown flags 0x%x", q.flags);
   s->H = q.heads;
   s->T = q.frames;
   s->U = q.tokens;
@@ -210,6 +210,7 @@ int prep_args(const vda_desc* desc, const void* k, const void* v, const float* b
   a.Nt = s.Nt;
   a.s0 = 0;
   a.cnt = s.n_eff;
+  a.prep = (desc->flags & VDA_PREP) ? 1 : 0;
   return VDA_OK;
 }
 
@@ -236,6 +237,7 @@ int scan_args(const vda_desc* desc, const void* ws, const float* alpha, const fl
   a.reverse = reverse;
   a.use_text = s.Nt > 0;
   a.scale = desc->text_init_scale;
+  a.prep = (desc->flags & VDA_PREP) ? 1 : 0;
   return VDA_OK;
 }
 
@@ -267,6 +269,7 @@ int read_args(const vda_desc* desc, const void* q, const float* alpha, const flo
   a.w = s.w;
   a.count = s.count;
   a.bridge = (desc->flags & VDA_NO_BRIDGE) ? 0 : 1;
+  a.prep = (desc->flags & VDA_PREP) ? 1 : 0;
   a.gate = nullptr;
   a.normw = nullptr;
   a.eps = 0.f;

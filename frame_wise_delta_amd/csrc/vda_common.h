@@ -77,6 +77,28 @@ __device__ __forceinline__ void split_bf16(float x, __bf16& hi, __bf16& lo) {
   lo = (__bf16)(x - (float)hi);
 }
 
+// Fused prep of raw inputs: x / sqrt(||x||^2 + kPrepEps) per token and
+// gate = sigmoid(logit).
+constexpr float kPrepEps = 1e-6f;
+__device__ __forceinline__ float sigmoid_gate(float z) { return __builtin_amdgcn_rcpf(1.f + __expf(-z)); }
+
+// Sum of v over each aligned group of W lanes (W a power of two <= 64), in
+// every lane of the group.  W = 16 uses DPP (two quad permutations, then row
+// rotations by 4 and 8); other widths use lane shuffles.
+template <int W>
+__device__ __forceinline__ float group_sum(float v) {
+  if constexpr (W == 16) {
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x124, 0xF, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xF, 0xF, false));
+  } else {
+#pragma unroll
+    for (int off = W / 2; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  }
+  return v;
+}
+
 // Element type tags for the input / output tensors.
 struct InF32 { typedef float T; static constexpr int bytes = 4; };
 struct InBF16 { typedef u16 T; static constexpr int bytes = 2; };

@@ -16,6 +16,7 @@ struct PrepArgs {
   int* status;
   int H, T, U, a, n, n_eff, Nt;
   int s0, cnt;    // frame slots [s0, s0 + cnt) of every head (slot n = text)
+  int prep;       // k, k_text raw (L2-normalised here), beta, beta_text logits
 };
 
 struct ScanArgs {
@@ -28,6 +29,7 @@ struct ScanArgs {
   int reverse;
   int use_text;         // S_init = S^T from the text slot (slot n) when s_init == nullptr
   float scale;
+  int prep;             // alpha holds logits (the gate is sigmoid(logit))
 };
 
 // One or two scans in one launch: blocks [0, H RB) run dir[0], the next
@@ -45,6 +47,7 @@ struct ReadArgs {
   void* out;              // [H][T][U][d]
   int H, T, U, a, n, P, C, w, count;
   int bridge;
+  int prep;               // q raw (L2-normalised here), alpha logits
   // readout epilogue (gated launches only): y = rmsnorm(o) * normw * sigmoid(gate)
   const void* gate;       // [H][T][U][d] logits, input dtype
   const float* normw;     // [H][d]

@@ -53,6 +53,16 @@ struct Stage8<InBF16> {
     const uint32_t w = (c >> 1) == 0 ? raw[s].x : (c >> 1) == 1 ? raw[s].y : (c >> 1) == 2 ? raw[s].z : raw[s].w;
     return bf16_bits_to_f32((c & 1) ? (w >> 16) : (w & 0xffffu));
   }
+  // sum of squares of token s's eight values, straight from the packed words
+  __device__ __forceinline__ float sumsq(int s) const {
+    typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+    float a = 0.f;
+    a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b2, raw[s].x), __builtin_bit_cast(b2, raw[s].x), a, false);
+    a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b2, raw[s].y), __builtin_bit_cast(b2, raw[s].y), a, false);
+    a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b2, raw[s].z), __builtin_bit_cast(b2, raw[s].z), a, false);
+    a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b2, raw[s].w), __builtin_bit_cast(b2, raw[s].w), a, false);
+    return a;
+  }
 };
 
 template <>
@@ -65,6 +75,12 @@ struct Stage8<InF32> {
   __device__ __forceinline__ float get(int s, int c) const {
     const float4 v = raw[s][c >> 2];
     return (c & 3) == 0 ? v.x : (c & 3) == 1 ? v.y : (c & 3) == 2 ? v.z : v.w;
+  }
+  __device__ __forceinline__ float sumsq(int s) const {
+    float a = 0.f;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) a = fmaf(get(s, c), get(s, c), a);
+    return a;
   }
 };
 
@@ -207,7 +223,7 @@ __device__ __forceinline__ void store_rows(const f32x4 (&acc)[NRW][D / 16], floa
   }
 }
 
-template <int D, class TIN>
+template <int D, class TIN, bool PREP>
 __global__ __launch_bounds__(kThreads, 2) void stats_kernel(PrepArgs args) {
   using T = typename TIN::T;
   constexpr int RT = D / 16;              // 16-row tiles
@@ -272,7 +288,30 @@ __global__ __launch_bounds__(kThreads, 2) void stats_kernel(PrepArgs args) {
   };
   if (U > 0) fetch(0);
   for (int u0 = 0; u0 < U; u0 += kRound) {
-    if (has_task) {
+    if (PREP && tensor == 0) {
+      // raw keys: 1 / ||k|| per token over the CG threads of its row, and
+      // beta = sigmoid(logit); the K operand becomes k / ||k||, beta*K beta k / ||k||
+      float rn[8];
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        rn[s] = __builtin_amdgcn_rsqf(group_sum<CG>(pre.sumsq(s)) + kPrepEps);
+        pbt[s] = sigmoid_gate(pbt[s]) * rn[s];
+      }
+      if (has_task) {
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          f16x8 pk, pb;
+#pragma unroll
+          for (int s = 0; s < 8; ++s) {
+            const float x = pre.get(s, c);
+            pk[s] = (_Float16)(x * rn[s]);
+            pb[s] = (_Float16)(pbt[s] * x);
+          }
+          *reinterpret_cast<f16x8*>(sK + tile_off(cg * 8 + c, tg)) = pk;
+          *reinterpret_cast<f16x8*>(sBK + tile_off(cg * 8 + c, tg)) = pb;
+        }
+      }
+    } else if (has_task) {
       _Float16* dst = tensor == 0 ? sK : sV;
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
@@ -483,10 +522,14 @@ int launch_stats(const PrepArgs& a, int d, bool in_f32, hipStream_t stream) {
   dim3 grid((unsigned)(a.H * a.cnt)), block(kThreads);
 #define VDA_STATS(DD)                                                                 \
   if (d == DD) {                                                                      \
-    if (in_f32)                                                                       \
-      hipLaunchKernelGGL((stats_kernel<DD, InF32>), grid, block, 0, stream, a);       \
+    if (in_f32 && a.prep)                                                             \
+      hipLaunchKernelGGL((stats_kernel<DD, InF32, true>), grid, block, 0, stream, a); \
+    else if (in_f32)                                                                  \
+      hipLaunchKernelGGL((stats_kernel<DD, InF32, false>), grid, block, 0, stream, a); \
+    else if (a.prep)                                                                  \
+      hipLaunchKernelGGL((stats_kernel<DD, InBF16, true>), grid, block, 0, stream, a); \
     else                                                                              \
-      hipLaunchKernelGGL((stats_kernel<DD, InBF16>), grid, block, 0, stream, a);      \
+      hipLaunchKernelGGL((stats_kernel<DD, InBF16, false>), grid, block, 0, stream, a); \
     return 0;                                                                         \
   }
   VDA_STATS(16) VDA_STATS(32) VDA_STATS(64) VDA_STATS(128)

@@ -164,6 +164,24 @@ struct GateRaw<InF32, 4> {
   __device__ __forceinline__ float get(int e) const { return e == 0 ? r.x : e == 1 ? r.y : e == 2 ? r.z : r.w; }
 };
 
+// Sum of squares of the 16 bytes of one token row chunk (8 bf16 or 4 float32).
+template <class TIN>
+__device__ __forceinline__ float chunk_sumsq(uint4 w) {
+  const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+  float ss = 0.f;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    if constexpr (TIN::bytes == 2) {
+      const float lo = __uint_as_float(u[q] << 16), hi = __uint_as_float(u[q] & 0xffff0000u);
+      ss = fmaf(lo, lo, fmaf(hi, hi, ss));
+    } else {
+      const float x = __uint_as_float(u[q]);
+      ss = fmaf(x, x, ss);
+    }
+  }
+  return ss;
+}
+
 // Sum of v over the four 16-lane rows of the wavefront, in every lane
 // (permlane32_swap pairs rows (0, 2) and (1, 3), permlane16_swap then (0, 1)).
 __device__ __forceinline__ float sum_rows4(float v) {
@@ -175,13 +193,9 @@ __device__ __forceinline__ float sum_rows4(float v) {
   return __uint_as_float(q[0]) + __uint_as_float(q[1]);
 }
 
-__device__ __forceinline__ float sigmoid_fast(float x) {
-  return __builtin_amdgcn_rcpf(1.f + __expf(-x));
-}
-
 }  // namespace
 
-template <int D, class TIN, int OUT, bool GATED>
+template <int D, class TIN, int OUT, bool GATED, bool PREP>
 __global__ __launch_bounds__(kThreads, GATED ? 3 : 2) void readout_kernel(ReadArgs a) {
   using T = typename TIN::T;
   constexpr int VT = D / 16;                         // value-channel tiles
@@ -199,6 +213,7 @@ __global__ __launch_bounds__(kThreads, GATED ? 3 : 2) void readout_kernel(ReadAr
   };
   __shared__ __attribute__((aligned(16))) char sQ[QT * PITCH];
   __shared__ float sBf[D], sBr[D];
+  __shared__ float sRq[PREP ? QT : 1];  // raw q: 1 / ||q|| of the tile's tokens
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, lg = lane >> 4;
@@ -256,6 +271,10 @@ __global__ __launch_bounds__(kThreads, GATED ? 3 : 2) void readout_kernel(ReadAr
           float v[16];
 #pragma unroll
           for (int j = 0; j < 16; ++j) v[j] = (rb + j <= r1) ? alpha_h[(size_t)(rb + j) * D + k] : 1.f;
+          if constexpr (PREP) {  // alpha given as logits
+#pragma unroll
+            for (int j = 0; j < 16; ++j) v[j] = (rb + j <= r1) ? sigmoid_gate(v[j]) : 1.f;
+          }
 #pragma unroll
           for (int j = 0; j < 16; ++j) prod *= v[j];
         }
@@ -360,6 +379,11 @@ __global__ __launch_bounds__(kThreads, GATED ? 3 : 2) void readout_kernel(ReadAr
             }
           }
         }
+        if constexpr (PREP) {
+          const float rq = sRq[ul];
+#pragma unroll
+          for (int i = 0; i < NVT; ++i) acc[i] *= rq;
+        }
       }
     };
     // pass 1: per-token sums of squares of this wavefront's channels
@@ -393,7 +417,7 @@ __global__ __launch_bounds__(kThreads, GATED ? 3 : 2) void readout_kernel(ReadAr
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const float g = kPair ? graw[st][0].get(4 * i + e) : graw[st][i].get(e);
-            y[i][e] = acc[i][e] * rs * nw[i][e] * sigmoid_fast(g);
+            y[i][e] = acc[i][e] * rs * nw[i][e] * sigmoid_gate(g);
           }
         if constexpr (kPair) {
           OutT<OUT>::store8(a.out, frame_off + (size_t)u * D + 32 * wave + 8 * lg, y[0], y[1]);
@@ -416,6 +440,15 @@ __global__ __launch_bounds__(kThreads, GATED ? 3 : 2) void readout_kernel(ReadAr
       if (i < QT * CH) {
         const int r = i / CH, ch = i - r * CH;
         *reinterpret_cast<uint4*>(sQ + r * PITCH + 16 * ch) = pre[j];
+      }
+    }
+    if constexpr (PREP) {  // raw q: the output of token u is scaled by 1 / ||q_u|| (o = S q / ||q||)
+#pragma unroll
+      for (int j = 0; j < PER; ++j) {
+        const int i = tid + j * kThreads;
+        const float ss = group_sum<CH>(chunk_sumsq<TIN>(pre[j]));
+        const int r = i / CH;
+        if (i < QT * CH && i - r * CH == 0) sRq[r] = __builtin_amdgcn_rsqf(ss + kPrepEps);
       }
     }
     lds_barrier();
@@ -444,6 +477,11 @@ __global__ __launch_bounds__(kThreads, GATED ? 3 : 2) void readout_kernel(ReadAr
           }
         }
         const int u = u0 + ul;
+        if constexpr (PREP) {
+          const float rq = sRq[ul];
+#pragma unroll
+          for (int i = 0; i < NVT; ++i) acc[i] *= rq;
+        }
         if (u < a.U) {
           if constexpr (kPair) {
             OutT<OUT>::store8(a.out, frame_off + (size_t)u * D + 32 * wave + 8 * lg, acc[0], acc[1]);
@@ -465,8 +503,14 @@ template <bool GATED>
 static int launch_readout_impl(const ReadArgs& a, int d, int in_dtype, int out_dtype, hipStream_t stream) {
   if (a.H == 0 || a.T == 0) return 0;
   dim3 grid((unsigned)(a.H * a.T)), block(kThreads);
-#define VDA_RD3(DD, TI, OO) \
-  if (out_dtype == OO) { hipLaunchKernelGGL((readout_kernel<DD, TI, OO, GATED>), grid, block, 0, stream, a); return 0; }
+#define VDA_RD3(DD, TI, OO)                                                                         \
+  if (out_dtype == OO) {                                                                            \
+    if (a.prep)                                                                                     \
+      hipLaunchKernelGGL((readout_kernel<DD, TI, OO, GATED, true>), grid, block, 0, stream, a);     \
+    else                                                                                            \
+      hipLaunchKernelGGL((readout_kernel<DD, TI, OO, GATED, false>), grid, block, 0, stream, a);    \
+    return 0;                                                                                       \
+  }
 #define VDA_RD(DD)                                                                 \
   if (d == DD) {                                                                   \
     if (in_dtype == VDA_F32) {                                                     \

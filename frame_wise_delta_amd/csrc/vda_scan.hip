@@ -103,13 +103,15 @@ __global__ __launch_bounds__(ScanShape<D>::NT) void scan_kernel(ScanPair p) {
   };
 
   // one frame write on the LDS state slice: S <- (S Diag(al) + B) N; a step
-  // with live == false leaves S unchanged (padding at the end of the chain)
-  auto step = [&](const FrameRegs<D>& fr, float* rec, bool live) {
+  // with live == false leaves S unchanged (padding at the end of the chain);
+  // with logits the decay is sigmoid(al)
+  auto step = [&](const FrameRegs<D>& fr, float* rec, bool live, bool logits) {
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
       const int row = xrow + 16 * q;
       const float4 s = *reinterpret_cast<const float4*>(sS + row * D + xc0);
-      const float4 al = fr.al;
+      float4 al = fr.al;
+      if (logits) al = make_float4(sigmoid_gate(al.x), sigmoid_gate(al.y), sigmoid_gate(al.z), sigmoid_gate(al.w));
       const f16x4 bb = fr.b[q];
       const float x[4] = {fmaf(s.x, al.x, (float)bb[0]), fmaf(s.y, al.y, (float)bb[1]),
                           fmaf(s.z, al.z, (float)bb[2]), fmaf(s.w, al.w, (float)bb[3])};
@@ -168,7 +170,7 @@ __global__ __launch_bounds__(ScanShape<D>::NT) void scan_kernel(ScanPair p) {
   if (!a.s_init && a.use_text) {
     FrameRegs<D> fr;
     load(fr, a.n, nullptr);
-    step(fr, nullptr, true);  // S^T = (0 + B_T) N_T
+    step(fr, nullptr, true, false);  // S^T = (0 + B_T) N_T
   }
   for (int i = tid; i < ROWS * D; i += SS::NT) {
     const float s0 = a.scale * sS[i];
@@ -200,7 +202,7 @@ __global__ __launch_bounds__(ScanShape<D>::NT) void scan_kernel(ScanPair p) {
     for (int j = 0; j <= PD; ++j) {
       const int i = i0 + j;
       load(fr[(j + PD) % (PD + 1)], slot_of(cl(i + PD)), alpha_of(cl(i + PD)));
-      step(fr[j], rec_of(i), i < n);
+      step(fr[j], rec_of(i), i < n, a.prep != 0);
     }
   }
 }

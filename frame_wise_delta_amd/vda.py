@@ -27,6 +27,7 @@ VDA_ERR_VALUE = -8
 
 VDA_F32, VDA_BF16, VDA_F16 = 0, 1, 2
 VDA_NO_BRIDGE = 1
+VDA_PREP = 2
 VDA_DEV_NONFINITE, VDA_DEV_PIVOT = 1, 2
 
 DTYPES = {"f32": VDA_F32, "bf16": VDA_BF16, "f16": VDA_F16}
@@ -123,10 +124,10 @@ def _stream(stream):
 
 
 def make_desc(heads, frames, tokens, d, chunk=5, anchors=1, window=1, text_tokens=0,
-              in_dtype="bf16", out_dtype="bf16", text_init_scale=0.5, bridge=True) -> vda_desc:
+              in_dtype="bf16", out_dtype="bf16", text_init_scale=0.5, bridge=True, prep=False) -> vda_desc:
     return vda_desc(heads, frames, tokens, d, d, chunk, anchors, window, text_tokens,
                     DTYPES[in_dtype], DTYPES[out_dtype], text_init_scale,
-                    0 if bridge else VDA_NO_BRIDGE)
+                    (0 if bridge else VDA_NO_BRIDGE) | (VDA_PREP if prep else 0))
 
 
 def desc_for(cfg, **over) -> vda_desc:

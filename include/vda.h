@@ -68,7 +68,12 @@ enum { VDA_F32 = 0, VDA_BF16 = 1, VDA_F16 = 2 };
 
 /* vda_desc.flags */
 enum {
-  VDA_NO_BRIDGE = 1u << 0 /* readout without the decay bridge (b_f = b_r = 1) */
+  VDA_NO_BRIDGE = 1u << 0, /* readout without the decay bridge (b_f = b_r = 1) */
+  VDA_PREP = 1u << 1       /* inputs are raw projections, prepared inside the kernels
+                              [VDN 方法步骤详情 step (2)]: q, k and k_text are
+                              L2-normalised per token, x / sqrt(||x||^2 + 1e-6), and
+                              beta, beta_text and alpha are logits whose gates are
+                              sigmoid(logit) */
 };
 
 /* bits of the device status word */
@@ -93,7 +98,7 @@ typedef struct vda_desc {
   int32_t out_dtype;   /* out: VDA_F32, VDA_BF16 or VDA_F16 */
   float text_init_scale; /* both scans start from text_init_scale * S^T;
                             1/2 reads the page's "initialised by halves" */
-  uint32_t flags;      /* VDA_NO_BRIDGE */
+  uint32_t flags;      /* VDA_NO_BRIDGE | VDA_PREP */
 } vda_desc;
 
 /* Bytes of device workspace vda_prepare_frames needs for `desc` (host only,

@@ -74,6 +74,9 @@ def test_bad_dtypes_and_flags():
     with pytest.raises(vda.VdaError) as e:
         vda.vda_state_count(d)
     assert e.value.code == vda.VDA_ERR_SHAPE
+    d = _desc(prep=True, bridge=False)  # both known flags are accepted
+    assert d.flags == vda.VDA_PREP | vda.VDA_NO_BRIDGE
+    vda.vda_state_count(d)
 
 
 def test_null_and_workspace_checks_precede_any_device_call():
