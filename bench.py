@@ -12,12 +12,13 @@ timing starts.  Prints one JSON line: latent frames/s, algorithmic TFLOP/s,
 a roofline entry for the dominant HBM-bound kernel timed with HIP events on
 the stream it runs on, and the float64 oracle timed on this host's cores.
 
-    python bench.py [--steps K] [--warmup W] [--config h3] [--no-cpu-baseline] [--epilogue]
+    python bench.py [--steps K] [--warmup W] [--config h3] [--no-cpu-baseline] [--epilogue] [--prep]
 
 --epilogue replaces the readout by vda_readout_gated (the readout followed by
 the RMSNorm + sigmoid-gate epilogue of the linear branch, with seeded gate
-logits and norm weights): a measurement of that next step of the path, not
-the default line.
+logits and norm weights); --prep feeds raw projections (q, k not normalised,
+beta and alpha as logits) and sets VDA_PREP, so the kernels normalise and
+gate them.  Both measure next steps of the path; neither is the default line.
 
 Measurement helpers (used to make the files under profiles/):
 
@@ -188,7 +189,7 @@ def write_traffic(fetch_csv, write_csv, cal_fetch_csv, cal_write_csv):
 
 # ---------------------------------------------------------------- bench --
 
-def cpu_baseline(cfg, heads_in, out0, budget_s=15.0, epi_in=None):
+def cpu_baseline(cfg, heads_in, out0, budget_s=15.0, epi_in=None, prep=False):
     """The float64 oracle, as it stands, on whole heads of the same workload
     until about budget_s seconds of CPU time are spent (at least one head);
     with epi_in, followed by the oracle's readout epilogue."""
@@ -205,6 +206,10 @@ def cpu_baseline(cfg, heads_in, out0, budget_s=15.0, epi_in=None):
         f = heads_in[h].f64
         args = [f(x) for x in ("q", "k", "v", "beta", "alpha")] + [f(x) if text else None for x in ("kt", "vt", "bt")]
         c0 = time.perf_counter()
+        if prep:
+            q, k, v, b, a, kt, vt, bt = args
+            q, k, b, a, kt, bt = orc.prep(q, k, b, a, kt, bt, eps=1e-6)
+            args = [q, k, v, b, a, kt, vt, bt]
         ref = orc.run_head(cfg.frames, cfg.chunk, cfg.window, cfg.anchors, *args)
         if epi_in is not None:
             ref["O"] = orc.rmsnorm_gate(ref["O"], epi_in[h].f64("weight"), epi_in[h].f64("gate"), EPS)
@@ -219,7 +224,8 @@ def cpu_baseline(cfg, heads_in, out0, budget_s=15.0, epi_in=None):
     return ({"value": round(cfg.frames * frac / t_cpu, 4), "unit": "frames/s", "cores": int(cores),
              "kind": "oracle",
              "sample": f"{done} of {cfg.heads} heads of the same workload (all {cfg.frames} frames of each), "
-                       f"float64 NumPy/LAPACK{' with the readout epilogue' if epi_in is not None else ''}, "
+                       f"float64 NumPy/LAPACK{' with the prep' if prep else ''}"
+                       f"{' with the readout epilogue' if epi_in is not None else ''}, "
                        f"{t_cpu:.1f} s; frames/s scaled by the fraction of heads"},
             rel)
 
@@ -235,6 +241,8 @@ def main():
                     help="CPU time budget of the oracle baseline (whole heads)")
     ap.add_argument("--epilogue", action="store_true",
                     help="time the readout with the RMSNorm + sigmoid-gate epilogue (vda_readout_gated)")
+    ap.add_argument("--prep", action="store_true",
+                    help="raw inputs prepared inside the kernels (VDA_PREP: L2 normalisation, sigmoid gates)")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--traffic", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"))
     args = ap.parse_args()
@@ -256,9 +264,9 @@ def main():
 
     cfg = inp.CONFIG_BY_NAME[args.config]
     t0 = time.time()
-    heads_in = inp.all_heads(cfg)
+    heads_in = inp.all_raw_heads(cfg) if args.prep else inp.all_heads(cfg)
     print(f"[bench] inputs for {cfg.name} drawn in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
-    desc = vda.desc_for(cfg)
+    desc = vda.desc_for(cfg, prep=args.prep)
     dev = runner.upload(cfg, heads_in, "cuda")
     bufs = runner.allocate(desc, cfg.out_dtype, "cuda")
     epi_in, gate, norm_w = None, None, None
@@ -322,13 +330,13 @@ def main():
     dom = max(kb, key=lambda k: kms[call_of[k]])
     ach = kb[dom] / (kms[call_of[dom]] / 1e3) / 1e9
     roofline = {"kernel": dom, "bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": _traffic(dom),
+                "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None if args.prep else _traffic(dom),
                 "algorithmic_bytes_per_launch": kb[dom], "avg_ms": round(kms[call_of[dom]], 4)}
 
     cpu, rel = None, None
     if not args.no_cpu_baseline:
         out0 = bufs.out[0].float().cpu().numpy().astype(np.float64)
-        cpu, rel = cpu_baseline(cfg, heads_in, out0, args.cpu_seconds, epi_in)
+        cpu, rel = cpu_baseline(cfg, heads_in, out0, args.cpu_seconds, epi_in, args.prep)
 
     out = {
         "metric": "VDA scan+readout latent frames/s and % of MI355X bf16 MFMA peak",
@@ -346,8 +354,9 @@ def main():
         "config": {"workload": f"{cfg.name}: {cfg.heads} heads, d={cfg.d}, {cfg.frames} latent frames "
                                f"({cfg.anchors * 2} anchors, chunks of {cfg.chunk}, window +-{cfg.window} "
                                f"chunk), U={cfg.tokens}, {cfg.text_tokens} text tokens"
-                               + (", readout epilogue (RMSNorm + sigmoid gate)" if args.epilogue else ""),
-                   "epilogue": bool(args.epilogue),
+                               + (", readout epilogue (RMSNorm + sigmoid gate)" if args.epilogue else "")
+                               + (", raw inputs prepared in the kernels" if args.prep else ""),
+                   "epilogue": bool(args.epilogue), "prep": bool(args.prep),
                    "heads": cfg.heads, "d": cfg.d, "frames": cfg.frames, "tokens": cfg.tokens,
                    "text_tokens": cfg.text_tokens, "in_dtype": cfg.in_dtype, "out_dtype": cfg.out_dtype,
                    "state_dtype": "f32", "global_batch": 1, "seq_len": cfg.frames * cfg.tokens,
