@@ -40,6 +40,9 @@ Readings of points the page leaves open:
   read by the linear branch (their output rows are zero).
 * With ``window = -1`` (no exclusion) the readout of frame t is S^f_t q where
   S^f_t includes frame t's own write.
+* Softmax branch: scores are scaled by 1/sqrt(d); the query and key
+  projections arrive after the branch's QK normalisation and rotary
+  position encoding, which need weights and positions and are not part of it.
 * Prep: q and k are normalised as x / sqrt(||x||^2 + eps) per token
   (eps = 1e-6); the write gate is beta = sigmoid(logit) per token and the
   decay gate alpha = sigmoid(logit) per frame and channel.
@@ -177,6 +180,55 @@ def readout_full(Q, states_f, frame_chunk, anchors):
         if frame_chunk[t] < 0:
             continue
         O[t] = Q[t] @ states_f[t - a + 1].T
+    return O
+
+
+# -------------------------------------------------------- softmax branch --
+
+def softmax_key_frames(frames: int, chunk: int, window: int, anchors: int):
+    """Visible video key frames of every query frame in the softmax branch
+    [VDN 核心方法 ¶1: exact softmax attention inside each query chunk's
+    chunk-aligned window, plus the first and last anchor frames, which every
+    frame sees and which see the whole sequence; VDN 方法步骤详情 step (1)].
+    Built from sets: the frames of the window chunks, plus the anchors.
+    Returns a list of sorted frame lists, one per query frame."""
+    T = frames
+    a = 1 if anchors else 0
+    n = T - 2 * a
+    C = -(-n // chunk)
+    anchor_frames = {0, T - 1} if a else set()
+    chunk_frames = [set(range(a + chunk * c, min(a + chunk * (c + 1), T - a))) for c in range(C)]
+    out = []
+    for t in range(T):
+        if t in anchor_frames:
+            keys = set(range(T))
+        else:
+            c = (t - a) // chunk
+            keys = set().union(*(chunk_frames[j] for j in range(C) if abs(j - c) <= window)) | anchor_frames
+        out.append(sorted(keys))
+    return out
+
+
+def softmax_branch(q, k, v, kt, vt, frames, chunk, window, anchors, scale=None):
+    """Softmax branch of the hybrid attention for one head [VDN 核心方法 ¶1;
+    方法步骤详情 step (1)]: every query token of frame t attends with
+    softmax(q K^T * scale) to the tokens of its visible key frames
+    (``softmax_key_frames``) and to all text tokens, which are always
+    visible.  q, k, v [T, U, d]; kt, vt [N_text, d] or None; scale defaults
+    to 1 / sqrt(d).  Row by row, in float64."""
+    T, U, d = q.shape
+    scale = 1.0 / np.sqrt(d) if scale is None else scale
+    O = np.zeros((T, U, v.shape[-1]))
+    for t, fr in enumerate(softmax_key_frames(frames, chunk, window, anchors)):
+        K = k[fr].reshape(-1, d)
+        V = v[fr].reshape(-1, v.shape[-1])
+        if kt is not None and len(kt):
+            K = np.concatenate([K, kt])
+            V = np.concatenate([V, vt])
+        S = (q[t] @ K.T) * scale
+        S -= S.max(axis=1, keepdims=True)
+        P = np.exp(S)
+        O[t] = (P @ V) / P.sum(axis=1, keepdims=True)
     return O
 
 

@@ -481,3 +481,66 @@ def test_raw_inputs_are_the_usual_draws_before_prep():
     np.testing.assert_allclose(b, ref.f64("beta"), rtol=1e-6)
     np.testing.assert_allclose(a, ref.f64("alpha"), rtol=1e-6)
     np.testing.assert_allclose(bt, ref.f64("bt"), rtol=1e-6)
+
+
+# ------------------------------------------------------ softmax branch (f3) --
+
+def test_softmax_key_frames_match_hand_derived_tiny_table():
+    table = {}
+    with open(os.path.join(GOLDEN, "tiny_softmax_keys.txt")) as f:
+        for line in f:
+            if line.startswith("#") or not line.strip():
+                continue
+            xs = [int(x) for x in line.split()]
+            table[xs[0]] = xs[1:]
+    keys = orc.softmax_key_frames(22, 5, 1, 1)
+    assert len(keys) == 22
+    for t in range(22):
+        assert keys[t] == table[t], t
+
+
+def test_softmax_key_frames_without_anchors_and_wide_window():
+    """No anchors: every frame is a query of some chunk and nothing is seen
+    globally; a window wider than the sequence sees every frame."""
+    keys = orc.softmax_key_frames(20, 5, 0, 0)
+    assert keys[0] == list(range(5)) and keys[19] == list(range(15, 20))
+    keys = orc.softmax_key_frames(22, 5, 9, 1)
+    assert all(kf == list(range(22)) for kf in keys)
+
+
+def test_softmax_branch_uniform_scores_average_the_visible_values():
+    """q = 0 makes every score equal, so each output is the plain mean of the
+    visible values; with v = the key's frame number (and text v = -1) that
+    mean is fixed by the key sets: chunk 0 of the tiny layout sees frames
+    {0, ..., 10, 21} with 2 tokens each and 3 text tokens."""
+    T, U, d = 22, 2, 4
+    q = np.zeros((T, U, d))
+    k = np.random.default_rng(3).standard_normal((T, U, d))
+    v = np.broadcast_to(np.arange(T, dtype=np.float64)[:, None, None], (T, U, d)).copy()
+    kt = np.random.default_rng(4).standard_normal((3, d))
+    vt = -np.ones((3, d))
+    O = orc.softmax_branch(q, k, v, kt, vt, T, 5, 1, 1)
+    expect = (2 * (sum(range(11)) + 21) - 3) / (2 * 12 + 3)
+    np.testing.assert_allclose(O[1], expect, rtol=1e-14)
+    expect_anchor = (2 * sum(range(22)) - 3) / (2 * 22 + 3)
+    np.testing.assert_allclose(O[0], expect_anchor, rtol=1e-14)
+
+
+def test_softmax_branch_dominant_key_and_shift_invariance():
+    """A key far more aligned with the query than the others takes all the
+    weight; adding one vector c to every key (video and text) shifts all
+    scores of a query by the same q.c and leaves the output unchanged."""
+    g = np.random.default_rng(5)
+    T, U, d = 7, 3, 8
+    q = g.standard_normal((T, U, d))
+    k = g.standard_normal((T, U, d)) * 0.01
+    v = g.standard_normal((T, U, d))
+    k[3, 1] = 500 * q[4, 0] / np.linalg.norm(q[4, 0])   # frame 3 is in frame 4's window (chunk 0)
+    O = orc.softmax_branch(q, k, v, None, None, T, 5, 1, 1)
+    np.testing.assert_allclose(O[4, 0], v[3, 1], rtol=1e-9)
+    k = g.standard_normal((T, U, d))
+    kt, vt = g.standard_normal((4, d)), g.standard_normal((4, d))
+    c = g.standard_normal(d)
+    O1 = orc.softmax_branch(q, k, v, kt, vt, T, 5, 1, 1)
+    O2 = orc.softmax_branch(q, k + c, v, kt + c, vt, T, 5, 1, 1)
+    np.testing.assert_allclose(O2, O1, rtol=1e-10, atol=1e-12)
