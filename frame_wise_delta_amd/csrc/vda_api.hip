@@ -410,6 +410,48 @@ int vda_readout_gated(const vda_desc* desc, const void* q, const float* alpha, c
   return launch_status();
 }
 
+int vda_softmax_branch(const vda_desc* desc, const void* q, const void* k, const void* v, const void* k_text,
+                       const void* v_text, float scale, void* out, void* stream) {
+  Shape s;
+  int rc = check_desc(desc, &s);
+  if (rc) return rc;
+  if (desc->in_dtype != VDA_BF16) return fail(VDA_ERR_DTYPE, "the softmax branch needs bf16 inputs");
+  if (s.d == 16) return fail(VDA_ERR_SHAPE, "the softmax branch needs d in {32, 64, 128}");
+  if (s.w < 0) return fail(VDA_ERR_SHAPE, "the softmax branch needs window >= 0");
+  if (!(scale > 0.f) || !std::isfinite(scale)) return fail(VDA_ERR_VALUE, "scale must be positive and finite");
+  const bool any = (size_t)s.H * s.T * s.U > 0;
+  if (any && (!q || !k || !v || !out)) return fail(VDA_ERR_NULL, "q, k, v or out is NULL");
+  if (any && s.Nt > 0 && (!k_text || !v_text)) return fail(VDA_ERR_NULL, "k_text or v_text is NULL with text_tokens = %d", s.Nt);
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(k_text) || !aligned16(v_text) || !aligned16(out))
+    return fail(VDA_ERR_ALIGN, "q, k, v, k_text, v_text, out need 16-byte alignment");
+  rc = check_device();
+  if (rc) return rc;
+  if (!any) return ok();
+  vda::AttnArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.kt = k_text;
+  a.vt = v_text;
+  a.out = out;
+  a.H = s.H;
+  a.T = s.T;
+  a.U = s.U;
+  a.a = s.a;
+  a.P = s.P;
+  a.C = s.C;
+  a.w = s.w;
+  a.Nt = s.Nt;
+  a.scale = scale;
+  const int qb = 128;  // queries per workgroup
+  a.anchor_tiles = s.a ? (s.U + qb - 1) / qb : 0;
+  a.chunk_tiles = (s.P * s.U + qb - 1) / qb;
+  a.tiles_per_head = 2 * a.anchor_tiles + s.C * a.chunk_tiles;
+  if ((double)s.H * a.tiles_per_head > 2.0e9) return fail(VDA_ERR_SHAPE, "grid too large");
+  vda::launch_attn(a, s.d, desc->out_dtype, static_cast<hipStream_t>(stream));
+  return launch_status();
+}
+
 int vda_forward(const vda_desc* desc, const void* q, const void* k, const void* v, const float* beta,
                 const float* alpha, const void* k_text, const void* v_text, const float* beta_text, void* ws,
                 size_t ws_size, float* states_fwd, float* states_rev, void* out, void* stream) {

@@ -1,0 +1,328 @@
+// Softmax branch of the hybrid attention: exact softmax attention of every
+// query token over its visible keys ("Video DeltaNet: A Video-Native Hybrid
+// Attention for Livestream Video Generation", core-method section, paragraph
+// 1, and method-steps section, step (1)):
+//
+//   query frames of chunk c   see the frames of chunks c-w .. c+w (clipped),
+//                             the two anchor frames and the text tokens;
+//   anchor frames (0, T-1)    see every frame and the text tokens;
+//
+//   o = softmax(q K^T * scale) V  over those keys.
+//
+// Flash-attention style: one 256-thread workgroup per 128 query tokens of
+// one query block (a chunk's frames, or one anchor frame), four wavefronts of
+// 32 queries.  Keys stream through LDS in 64-key tiles, segment by segment
+// (window frames, anchor frames, text), with the next tile's loads in flight
+// during the current tile's work.  The scores are formed transposed,
+// S^T = K Q^T (16x16x32 bf16 MFMA), so that a wavefront's accumulator lane
+// holds four consecutive keys of one query: exactly the B operand of a
+// 16x16x16 MFMA.  The output is accumulated transposed as well,
+// O^T += V^T P^T, with P rounded to f16, V converted to f16 in LDS and V^T
+// read with the LDS transposing load.  The softmax is online (running max and
+// sum per query, in float32, base 2).
+#include "vda_common.h"
+#include "vda_kernels.h"
+
+namespace vda {
+
+namespace {
+
+constexpr int kQB = 128;  // queries per workgroup
+constexpr int kKT = 64;   // keys per LDS tile
+
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
+
+__device__ __forceinline__ f32x4 mfma16_f16(f16x4 a, f16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+}
+
+// max / sum over the four 16-lane rows (lanes n, n+16, n+32, n+48), in
+// every lane: permlane32_swap pairs rows (0, 2) and (1, 3), permlane16_swap
+// then rows (0, 1).
+__device__ __forceinline__ float rows4_max(float v) {
+  const unsigned b = __float_as_uint(v);
+  const auto p = __builtin_amdgcn_permlane32_swap(b, b, false, false);
+  const float s = fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+  const unsigned c = __float_as_uint(s);
+  const auto q = __builtin_amdgcn_permlane16_swap(c, c, false, false);
+  return fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
+}
+__device__ __forceinline__ float rows4_sum(float v) {
+  const unsigned b = __float_as_uint(v);
+  const auto p = __builtin_amdgcn_permlane32_swap(b, b, false, false);
+  const float s = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+  const unsigned c = __float_as_uint(s);
+  const auto q = __builtin_amdgcn_permlane16_swap(c, c, false, false);
+  return __uint_as_float(q[0]) + __uint_as_float(q[1]);
+}
+
+template <int OUT>
+__device__ __forceinline__ void store_out4(void* base, size_t idx, f32x4 v) {
+  if constexpr (OUT == VDA_F32) {
+    *reinterpret_cast<float4*>(static_cast<float*>(base) + idx) = make_float4(v[0], v[1], v[2], v[3]);
+  } else if constexpr (OUT == VDA_BF16) {
+    bf16x4 b = {(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
+    *reinterpret_cast<bf16x4*>(static_cast<u16*>(base) + idx) = b;
+  } else {
+    f16x4 h = {(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
+    *reinterpret_cast<f16x4*>(static_cast<_Float16*>(base) + idx) = h;
+  }
+}
+
+}  // namespace
+
+// Query blocks of one head, in this order: [anchor frame 0], the C chunks,
+// [anchor frame T-1]; block b has nq(b) query tokens starting at token
+// q0(b) of the head and ceil(nq / kQB) workgroups.
+template <int D, int OUT>
+__global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
+  static_assert(D % 32 == 0 && D <= 128, "head size must be 32, 64 or 128");
+  constexpr int KS = D / 32;   // k-steps of the score product
+  constexpr int DT = D / 16;   // 16-wide output tiles
+  constexpr int KP = D + 16;   // LDS row pitch (halves): rows 32 bytes apart modulo 256
+  constexpr int CPR = D / 8;   // 16-byte chunks per key row
+  constexpr int LPT = kKT * CPR / kThreads;  // chunks per thread per tile (K and V each)
+  static_assert(LPT >= 1, "tile too small");
+  __shared__ __attribute__((aligned(16))) u16 sK[kKT * KP];
+  __shared__ __attribute__((aligned(16))) _Float16 sV[kKT * KP];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int ln = lane & 15, lg = lane >> 4;
+
+  // ---- which head, query block and 128-query tile
+  int L = xcd_block(blockIdx.x, gridDim.x);
+  const int h = L / a.tiles_per_head;
+  L -= h * a.tiles_per_head;
+  const int ta = a.anchor_tiles;  // tiles per anchor frame (0 without anchors)
+  const int tc = a.chunk_tiles;   // tiles per chunk
+  int qb, tile;                   // query block (-1: first anchor, C: last anchor), tile in it
+  if (L < ta) {
+    qb = -1;
+    tile = L;
+  } else if (L < ta + a.C * tc) {
+    qb = (L - ta) / tc;
+    tile = L - ta - qb * tc;
+  } else {
+    qb = a.C;
+    tile = L - ta - a.C * tc;
+  }
+  const bool anchor_q = qb < 0 || qb >= a.C;
+  const int qf0 = qb < 0 ? 0 : (anchor_q ? a.T - 1 : a.a + a.P * qb);  // first query frame
+  const int nq = (anchor_q ? 1 : a.P) * a.U;                           // query tokens in the block
+  const int q0 = qf0 * a.U + tile * kQB;                                 // first query token of the tile
+  const int nq_tile = nq - tile * kQB < kQB ? nq - tile * kQB : kQB;
+
+  // ---- key segments: [start, end) tokens of the head's video keys, then text
+  int seg_s[3], seg_e[3], nseg = 0;
+  if (anchor_q) {
+    seg_s[0] = 0;
+    seg_e[0] = a.T * a.U;
+    nseg = 1;
+  } else {
+    const int lo = qb - a.w > 0 ? qb - a.w : 0;
+    const int hi = qb + a.w < a.C - 1 ? qb + a.w : a.C - 1;
+    seg_s[0] = (a.a + a.P * lo) * a.U;
+    seg_e[0] = (a.a + a.P * (hi + 1)) * a.U;
+    nseg = 1;
+    if (a.a) {
+      seg_s[1] = 0;
+      seg_e[1] = a.U;
+      seg_s[2] = (a.T - 1) * a.U;
+      seg_e[2] = a.T * a.U;
+      nseg = 3;
+    }
+  }
+  int ntiles = 0;
+  for (int s = 0; s < nseg; ++s) ntiles += (seg_e[s] - seg_s[s] + kKT - 1) / kKT;
+  const int text_tiles = (a.Nt + kKT - 1) / kKT;
+  const int all_tiles = ntiles + text_tiles;
+
+  const size_t hoff = (size_t)h * a.T * a.U * D;
+  const u16* qh = static_cast<const u16*>(a.q) + hoff;
+  const u16* kh = static_cast<const u16*>(a.k) + hoff;
+  const u16* vh = static_cast<const u16*>(a.v) + hoff;
+  const u16* kth = static_cast<const u16*>(a.kt) + (size_t)h * a.Nt * D;
+  const u16* vth = static_cast<const u16*>(a.vt) + (size_t)h * a.Nt * D;
+
+  // ---- Q fragments (B operand of S^T = K Q^T): lane (n, g) holds query n's
+  // channels 32 kk + 8g .. +7, for its wavefront's two 16-query tiles
+  bf16x8 qf[2][KS];
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) {
+    const int qi = wave * 32 + qt * 16 + ln;
+    const bool ok = qi < nq_tile;
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+      const uint4 w = ok ? *reinterpret_cast<const uint4*>(qh + (size_t)(q0 + qi) * D + 32 * kk + 8 * lg)
+                         : make_uint4(0, 0, 0, 0);
+      qf[qt][kk] = __builtin_bit_cast(bf16x8, w);
+    }
+  }
+
+  // ---- key tile j: its source rows and valid count
+  auto tile_src = [&](int j, const u16*& kb, const u16*& vb, int& n) {
+    if (j >= ntiles) {  // text
+      const int t0 = (j - ntiles) * kKT;
+      kb = kth + (size_t)t0 * D;
+      vb = vth + (size_t)t0 * D;
+      n = a.Nt - t0 < kKT ? a.Nt - t0 : kKT;
+      return;
+    }
+    for (int s = 0; s < nseg; ++s) {
+      const int nt = (seg_e[s] - seg_s[s] + kKT - 1) / kKT;
+      if (j < nt) {
+        const int t0 = seg_s[s] + j * kKT;
+        kb = kh + (size_t)t0 * D;
+        vb = vh + (size_t)t0 * D;
+        n = seg_e[s] - t0 < kKT ? seg_e[s] - t0 : kKT;
+        return;
+      }
+      j -= nt;
+    }
+    kb = kh;
+    vb = vh;
+    n = 0;
+  };
+
+  uint4 pk[LPT], pv[LPT];
+  auto fetch = [&](int j) {
+    const u16* kb;
+    const u16* vb;
+    int n;
+    tile_src(j, kb, vb, n);
+#pragma unroll
+    for (int i = 0; i < LPT; ++i) {
+      const int c = tid + i * kThreads;
+      const int r = c / CPR, ch = c - r * CPR;
+      const bool ok = r < n;
+      pk[i] = ok ? *reinterpret_cast<const uint4*>(kb + (size_t)r * D + 8 * ch) : make_uint4(0, 0, 0, 0);
+      pv[i] = ok ? *reinterpret_cast<const uint4*>(vb + (size_t)r * D + 8 * ch) : make_uint4(0, 0, 0, 0);
+    }
+    return n;
+  };
+
+  f32x4 o[2][DT];
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) o[qt][dt] = f32x4{0, 0, 0, 0};
+  float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
+  const float sc = a.scale * 1.4426950408889634f;  // scores in base-2 units
+
+  // V^T fragment addressing (transposing load): lane j of 16-lane block g
+  // reads key row 4g + (j >> 2) of the 16-key sub-tile, channels
+  // 16 dt + 4 (j & 3) .. +3
+  const int vrow = 4 * lg + (ln >> 2), vcol = 4 * (ln & 3);
+
+  int n_cur = all_tiles > 0 ? fetch(0) : 0;
+  for (int j = 0; j < all_tiles; ++j) {
+    // ---- stage tile j: K as loaded, V converted to f16
+#pragma unroll
+    for (int i = 0; i < LPT; ++i) {
+      const int c = tid + i * kThreads;
+      const int r = c / CPR, ch = c - r * CPR;
+      *reinterpret_cast<uint4*>(sK + r * KP + 8 * ch) = pk[i];
+      const uint4 w = pv[i];
+      const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+      f16x8 hv;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        hv[2 * e] = (_Float16)__uint_as_float(u[e] << 16);
+        hv[2 * e + 1] = (_Float16)__uint_as_float(u[e] & 0xffff0000u);
+      }
+      *reinterpret_cast<f16x8*>(sV + r * KP + 8 * ch) = hv;
+    }
+    const int n_tile = n_cur;
+    lds_barrier();
+    if (j + 1 < all_tiles) n_cur = fetch(j + 1);
+
+    // ---- S^T = K Q^T: 4 key sub-tiles x 2 query tiles
+    f32x4 s[4][2];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      s[kt][0] = f32x4{0, 0, 0, 0};
+      s[kt][1] = f32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) {
+        const bf16x8 kf = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(sK + (16 * kt + ln) * KP + 32 * kk + 8 * lg));
+        s[kt][0] = mfma_bf16(kf, qf[0][kk], s[kt][0]);
+        s[kt][1] = mfma_bf16(kf, qf[1][kk], s[kt][1]);
+      }
+    }
+    // ---- online softmax; lane (n, g) holds keys 16 kt + 4g + e of query n
+    f16x4 p[4][2];
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const bool valid = 16 * kt + 4 * lg + e < n_tile;
+          const float v = valid ? s[kt][qt][e] * sc : -INFINITY;
+          s[kt][qt][e] = v;
+          mx = fmaxf(mx, v);
+        }
+      mx = rows4_max(mx);
+      const float m_new = fmaxf(m_run[qt], mx);
+      const float corr = __builtin_amdgcn_exp2f(m_run[qt] - m_new);  // 0 on the first tile (m_run = -inf)
+      float rs = 0.f;
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+        f16x4 pp;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float pe = __builtin_amdgcn_exp2f(s[kt][qt][e] - m_new);
+          rs += pe;
+          pp[e] = (_Float16)pe;
+        }
+        p[kt][qt] = pp;
+      }
+      rs = rows4_sum(rs);
+      l_run[qt] = l_run[qt] * corr + rs;
+      m_run[qt] = m_new;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) o[qt][dt] *= corr;
+    }
+    // ---- O^T += V^T P^T
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const _Float16* src = sV + (16 * kt + vrow) * KP + 16 * dt + vcol;
+        const f16x4 vf = __builtin_bit_cast(f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)src));
+        o[0][dt] = mfma16_f16(vf, p[kt][0], o[0][dt]);
+        o[1][dt] = mfma16_f16(vf, p[kt][1], o[1][dt]);
+      }
+    }
+    lds_barrier();
+  }
+
+  // ---- O = O^T / l: lane (n, g) holds channels 16 dt + 4g + e of query n
+  const size_t obase = (size_t)h * a.T * a.U * D;
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) {
+    const int qi = wave * 32 + qt * 16 + ln;
+    if (qi >= nq_tile) continue;
+    const float inv = l_run[qt] > 0.f ? 1.f / l_run[qt] : 0.f;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) store_out4<OUT>(a.out, obase + (size_t)(q0 + qi) * D + 16 * dt + 4 * lg, o[qt][dt] * inv);
+  }
+}
+
+int launch_attn(const AttnArgs& a, int d, int out_dtype, hipStream_t stream) {
+  if (a.H == 0 || a.tiles_per_head == 0) return 0;
+  dim3 grid((unsigned)(a.H * a.tiles_per_head)), block(kThreads);
+#define VDA_AT(DD)                                                                                 \
+  if (d == DD) {                                                                                   \
+    if (out_dtype == VDA_F32) hipLaunchKernelGGL((attn_kernel<DD, VDA_F32>), grid, block, 0, stream, a); \
+    else if (out_dtype == VDA_BF16) hipLaunchKernelGGL((attn_kernel<DD, VDA_BF16>), grid, block, 0, stream, a); \
+    else hipLaunchKernelGGL((attn_kernel<DD, VDA_F16>), grid, block, 0, stream, a);               \
+    return 0;                                                                                      \
+  }
+  VDA_AT(32) VDA_AT(64) VDA_AT(128)
+#undef VDA_AT
+  return -1;
+}
+
+}  // namespace vda

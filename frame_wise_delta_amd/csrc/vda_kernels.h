@@ -54,6 +54,18 @@ struct ReadArgs {
   float eps;
 };
 
+struct AttnArgs {
+  const void* q;          // [H][T][U][d] bf16 (after the branch's QK normalisation and rotary encoding)
+  const void* k;          // [H][T][U][d] bf16
+  const void* v;          // [H][T][U][d] bf16
+  const void* kt;         // [H][Nt][d] bf16 or nullptr (Nt = 0)
+  const void* vt;         // [H][Nt][d] bf16 or nullptr
+  void* out;              // [H][T][U][d]
+  int H, T, U, a, P, C, w, Nt;
+  float scale;
+  int tiles_per_head, anchor_tiles, chunk_tiles;  // 128-query workgroups
+};
+
 int launch_stats(const PrepArgs& a, int d, bool in_f32, hipStream_t stream);
 int launch_gj(const PrepArgs& a, int d, hipStream_t stream);
 void launch_clear_status(int* status, hipStream_t stream);
@@ -61,5 +73,6 @@ int launch_scan(const ScanPair& p, int d, hipStream_t stream);
 int launch_readout(const ReadArgs& a, int d, int in_dtype, int out_dtype, hipStream_t stream);
 // The readout with the RMSNorm + sigmoid-gate epilogue (a.gate, a.normw, a.eps).
 int launch_readout_gated(const ReadArgs& a, int d, int in_dtype, int out_dtype, hipStream_t stream);
+int launch_attn(const AttnArgs& a, int d, int out_dtype, hipStream_t stream);
 
 }  // namespace vda

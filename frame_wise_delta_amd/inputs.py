@@ -22,6 +22,8 @@ these draws stand in for them:
 * text tokens (k_T, v_T, beta_T) follow the same laws as video tokens.
 * raw projections for the fused prep (``raw_head_inputs``): the same draws
   with q, k not normalised and beta, alpha stored as logits;
+* softmax branch (``softmax_inputs``): q, k, v and text k, v with N(0, 1)
+  entries, bf16;
 * readout epilogue (``epilogue_inputs``): gate logits N(0, 1) per frame,
   token and channel; RMSNorm weight 1 + 0.1 N(0, 1) per channel.
 
@@ -40,7 +42,7 @@ from concurrent.futures import ThreadPoolExecutor
 import numpy as np
 
 # tensor ids for the per-tensor generators
-_Q, _K, _V, _BETA, _ALPHA, _KT, _VT, _BT, _GATE, _NORMW = range(10)
+_Q, _K, _V, _BETA, _ALPHA, _KT, _VT, _BT, _GATE, _NORMW, _SQ, _SK, _SV, _SKT, _SVT = range(15)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -214,6 +216,31 @@ def epilogue_inputs(cfg: Config, head: int) -> EpilogueInputs:
     gate = store(_rng(cfg, _GATE, head).standard_normal((T, U, d)), cfg.in_dtype)
     weight = (1.0 + 0.1 * _rng(cfg, _NORMW, head).standard_normal(d)).astype(np.float32)
     return EpilogueInputs(dtype=cfg.in_dtype, gate=gate, weight=weight)
+
+
+@dataclasses.dataclass
+class SoftmaxInputs:
+    """Inputs of the softmax branch of one head, as bf16 bits: q, k, v
+    [T, U, d] and the text keys / values kt, vt [N_text, d]."""
+
+    q: np.ndarray
+    k: np.ndarray
+    v: np.ndarray
+    kt: np.ndarray
+    vt: np.ndarray
+
+    def f64(self, name: str) -> np.ndarray:
+        return to_f64(getattr(self, name), "bf16")
+
+
+def softmax_inputs(cfg: Config, head: int) -> SoftmaxInputs:
+    """q, k, v and the text keys / values of the softmax branch: N(0, 1)
+    entries (the scale of projections after a QK RMS normalisation, so that
+    q.k / sqrt(d) is about N(0, 1)), stored as bf16."""
+    T, U, d, nt = cfg.frames, cfg.tokens, cfg.d, cfg.text_tokens
+    n = lambda tid, shape: store(_rng(cfg, tid, head).standard_normal(shape), "bf16")
+    return SoftmaxInputs(q=n(_SQ, (T, U, d)), k=n(_SK, (T, U, d)), v=n(_SV, (T, U, d)),
+                         kt=n(_SKT, (nt, d)), vt=n(_SVT, (nt, d)))
 
 
 def raw_head_inputs(cfg: Config, head: int) -> HeadInputs:

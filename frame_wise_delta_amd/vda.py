@@ -34,8 +34,8 @@ DTYPES = {"f32": VDA_F32, "bf16": VDA_BF16, "f16": VDA_F16}
 
 EXPORTS = ("vda_workspace_bytes", "vda_state_count", "vda_index_map", "vda_prepare_frames",
            "vda_frame_stats", "vda_factor_frames", "vda_scan_fwd", "vda_scan_rev", "vda_scan_bidir",
-           "vda_readout", "vda_readout_gated", "vda_forward", "vda_device_status", "vda_status_string",
-           "vda_last_error")
+           "vda_readout", "vda_readout_gated", "vda_softmax_branch", "vda_forward", "vda_device_status",
+           "vda_status_string", "vda_last_error")
 
 
 class vda_desc(ctypes.Structure):
@@ -82,6 +82,7 @@ def load(path: str | None = None):
         "vda_readout": [D, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p],
         "vda_readout_gated": [D, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_float,
                               c_void_p, c_void_p],
+        "vda_softmax_branch": [D, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_float, c_void_p, c_void_p],
         "vda_forward": [D, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                         c_void_p, c_void_p, c_size_t, c_void_p, c_void_p, c_void_p, c_void_p],
         "vda_device_status": [D, c_void_p, c_void_p, POINTER(c_int32)],
@@ -209,6 +210,11 @@ def vda_readout_gated(desc, q, alpha, states_fwd, states_rev, gate, norm_weight,
     _check(load().vda_readout_gated(ctypes.byref(desc), _ptr(q), _ptr(alpha), _ptr(states_fwd),
                                     _ptr(states_rev), _ptr(gate), _ptr(norm_weight), float(eps), _ptr(out),
                                     _stream(stream)))
+
+
+def vda_softmax_branch(desc, q, k, v, k_text, v_text, scale, out, stream=None):
+    _check(load().vda_softmax_branch(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(k_text), _ptr(v_text),
+                                     float(scale), _ptr(out), _stream(stream)))
 
 
 def vda_forward(desc, q, k, v, beta, alpha, k_text, v_text, beta_text, ws, states_fwd, states_rev, out,
