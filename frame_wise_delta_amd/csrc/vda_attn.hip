@@ -15,10 +15,10 @@
 // (window frames, anchor frames, text), with the next tile's loads in flight
 // during the current tile's work.  The scores are formed transposed,
 // S^T = K Q^T (16x16x32 bf16 MFMA), so that a wavefront's accumulator lane
-// holds four consecutive keys of one query: exactly the B operand of a
-// 16x16x16 MFMA.  The output is accumulated transposed as well,
+// holds four consecutive keys of one query; two such tiles make the B
+// operand of a 16x16x32 MFMA.  The output is accumulated transposed as well,
 // O^T += V^T P^T, with P rounded to f16, V converted to f16 in LDS and V^T
-// read with the LDS transposing load.  The softmax is online (running max and
+// read with the LDS transposing load in the same key order.  The softmax is online (running max and
 // sum per query, in float32, base 2).
 #include "vda_common.h"
 #include "vda_kernels.h"
@@ -32,9 +32,6 @@ constexpr int kKT = 64;   // keys per LDS tile
 
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
 
-__device__ __forceinline__ f32x4 mfma16_f16(f16x4 a, f16x4 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
-}
 
 // max / sum over the four 16-lane rows (lanes n, n+16, n+32, n+48), in
 // every lane: permlane32_swap pairs rows (0, 2) and (1, 3), permlane16_swap
@@ -207,7 +204,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) o[qt][dt] = f32x4{0, 0, 0, 0};
   float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
-  const float sc = a.scale * 1.4426950408889634f;  // scores in base-2 units
+  const float sc = a.scale * 1.4426950408889634f;  // scale to base-2 units
 
   // V^T fragment addressing (transposing load): lane j of 16-lane block g
   // reads key row 4g + (j >> 2) of the 16-key sub-tile, channels
@@ -249,50 +246,63 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
         s[kt][1] = mfma_bf16(kf, qf[1][kk], s[kt][1]);
       }
     }
-    // ---- online softmax; lane (n, g) holds keys 16 kt + 4g + e of query n
-    f16x4 p[4][2];
+    // ---- online softmax; lane (n, g) holds keys 16 kt + 4g + e of query n.
+    // Scores stay unscaled; the running max is kept in scaled base-2 units.
+    if (n_tile < kKT) {  // last tile of a segment: keys past its end get no weight
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (16 * kt + 4 * lg + e >= n_tile) s[kt][0][e] = s[kt][1][e] = -INFINITY;
+    }
+    f16x8 p[2][2];  // [key pair kp][query tile]: keys 32 kp + 4g + e, then 32 kp + 16 + 4g + e
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt) {
       float mx = -INFINITY;
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const bool valid = 16 * kt + 4 * lg + e < n_tile;
-          const float v = valid ? s[kt][qt][e] * sc : -INFINITY;
-          s[kt][qt][e] = v;
-          mx = fmaxf(mx, v);
-        }
-      mx = rows4_max(mx);
-      const float m_new = fmaxf(m_run[qt], mx);
-      const float corr = __builtin_amdgcn_exp2f(m_run[qt] - m_new);  // 0 on the first tile (m_run = -inf)
+        for (int e = 0; e < 4; ++e) mx = fmaxf(mx, s[kt][qt][e]);
+      mx = rows4_max(mx) * sc;
+      // The reference point m_run moves only when a score exceeds it by more
+      // than 8 (base 2), so the weights stay below 2^8 (exact enough in f16)
+      // and O is rescaled only on the rare tiles where some query's
+      // reference moves (always on the first tile, where m_run = -inf).
+      const bool move = mx > m_run[qt] + 8.f;
+      const float m_new = move ? mx : m_run[qt];
+      if (__builtin_amdgcn_ballot_w64(move)) {
+        const float corr = __builtin_amdgcn_exp2f(m_run[qt] - m_new);  // 0 when m_run = -inf, 1 when kept
+        l_run[qt] *= corr;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) o[qt][dt] *= corr;
+        m_run[qt] = m_new;
+      }
       float rs = 0.f;
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) {
-        f16x4 pp;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float pe = __builtin_amdgcn_exp2f(s[kt][qt][e] - m_new);
+          const float pe = __builtin_amdgcn_exp2f(fmaf(s[kt][qt][e], sc, -m_new));
           rs += pe;
-          pp[e] = (_Float16)pe;
+          p[kt >> 1][qt][4 * (kt & 1) + e] = (_Float16)pe;
         }
-        p[kt][qt] = pp;
       }
-      rs = rows4_sum(rs);
-      l_run[qt] = l_run[qt] * corr + rs;
-      m_run[qt] = m_new;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) o[qt][dt] *= corr;
+      l_run[qt] += rows4_sum(rs);
     }
-    // ---- O^T += V^T P^T
+    // ---- O^T += V^T P^T on 16x16x32 MFMA: the k order of a 32-key pair is
+    // (16-key sub-tile 2kp, keys 4g .. 4g+3; sub-tile 2kp+1, keys 4g .. 4g+3)
+    // in lane group g, the same for the V^T operand (two transposing loads)
+    // and for P (two score accumulators)
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
+    for (int kp = 0; kp < 2; ++kp) {
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        const _Float16* src = sV + (16 * kt + vrow) * KP + 16 * dt + vcol;
-        const f16x4 vf = __builtin_bit_cast(f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)src));
-        o[0][dt] = mfma16_f16(vf, p[kt][0], o[0][dt]);
-        o[1][dt] = mfma16_f16(vf, p[kt][1], o[1][dt]);
+        const _Float16* src = sV + (32 * kp + vrow) * KP + 16 * dt + vcol;
+        const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)src);
+        const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(src + 16 * KP));
+        const f16x8 vf = __builtin_bit_cast(f16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+        o[0][dt] = mfma_f16(vf, p[kp][0], o[0][dt]);
+        o[1][dt] = mfma_f16(vf, p[kp][1], o[1][dt]);
       }
     }
     lds_barrier();
