@@ -411,11 +411,13 @@ int vda_readout_gated(const vda_desc* desc, const void* q, const float* alpha, c
 }
 
 int vda_softmax_branch(const vda_desc* desc, const void* q, const void* k, const void* v, const void* k_text,
-                       const void* v_text, float scale, void* out, void* stream) {
+                       const void* v_text, int32_t v_dtype, float scale, void* out, void* stream) {
   Shape s;
   int rc = check_desc(desc, &s);
   if (rc) return rc;
-  if (desc->in_dtype != VDA_BF16) return fail(VDA_ERR_DTYPE, "the softmax branch needs bf16 inputs");
+  if (desc->in_dtype != VDA_BF16) return fail(VDA_ERR_DTYPE, "the softmax branch needs bf16 q and k");
+  if (v_dtype != VDA_BF16 && v_dtype != VDA_F16)
+    return fail(VDA_ERR_DTYPE, "v_dtype = %d (VDA_BF16 or VDA_F16)", v_dtype);
   if (s.d == 16) return fail(VDA_ERR_SHAPE, "the softmax branch needs d in {32, 64, 128}");
   if (s.w < 0) return fail(VDA_ERR_SHAPE, "the softmax branch needs window >= 0");
   if (!(scale > 0.f) || !std::isfinite(scale)) return fail(VDA_ERR_VALUE, "scale must be positive and finite");
@@ -443,6 +445,7 @@ int vda_softmax_branch(const vda_desc* desc, const void* q, const void* k, const
   a.w = s.w;
   a.Nt = s.Nt;
   a.scale = scale;
+  a.v_f16 = v_dtype == VDA_F16;
   const int qb = 128;  // queries per workgroup
   a.anchor_tiles = s.a ? (s.U + qb - 1) / qb : 0;
   a.chunk_tiles = (s.P * s.U + qb - 1) / qb;

@@ -17,8 +17,10 @@
 // S^T = K Q^T (16x16x32 bf16 MFMA), so that a wavefront's accumulator lane
 // holds four consecutive keys of one query; two such tiles make the B
 // operand of a 16x16x32 MFMA.  The output is accumulated transposed as well,
-// O^T += V^T P^T, with P rounded to f16, V converted to f16 in LDS and V^T
-// read with the LDS transposing load in the same key order.  The softmax is online (running max and
+// O^T += V^T P^T on f16 operands (P rounded once; V given as f16, or bf16
+// converted while it is staged in LDS), with V^T read with the LDS
+// transposing load in the same key order; the softmax denominators come out
+// of the same MFMAs (an all-ones row block in place of V^T).  The softmax is online (running max and
 // sum per query, in float32, base 2).
 #include "vda_common.h"
 #include "vda_kernels.h"
@@ -33,7 +35,7 @@ constexpr int kKT = 64;   // keys per LDS tile
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
 
 
-// max / sum over the four 16-lane rows (lanes n, n+16, n+32, n+48), in
+// max over the four 16-lane rows (lanes n, n+16, n+32, n+48), in
 // every lane: permlane32_swap pairs rows (0, 2) and (1, 3), permlane16_swap
 // then rows (0, 1).
 __device__ __forceinline__ float rows4_max(float v) {
@@ -43,14 +45,6 @@ __device__ __forceinline__ float rows4_max(float v) {
   const unsigned c = __float_as_uint(s);
   const auto q = __builtin_amdgcn_permlane16_swap(c, c, false, false);
   return fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
-}
-__device__ __forceinline__ float rows4_sum(float v) {
-  const unsigned b = __float_as_uint(v);
-  const auto p = __builtin_amdgcn_permlane32_swap(b, b, false, false);
-  const float s = __uint_as_float(p[0]) + __uint_as_float(p[1]);
-  const unsigned c = __float_as_uint(s);
-  const auto q = __builtin_amdgcn_permlane16_swap(c, c, false, false);
-  return __uint_as_float(q[0]) + __uint_as_float(q[1]);
 }
 
 template <int OUT>
@@ -71,7 +65,7 @@ __device__ __forceinline__ void store_out4(void* base, size_t idx, f32x4 v) {
 // Query blocks of one head, in this order: [anchor frame 0], the C chunks,
 // [anchor frame T-1]; block b has nq(b) query tokens starting at token
 // q0(b) of the head and ceil(nq / kQB) workgroups.
-template <int D, int OUT>
+template <int D, int OUT, bool VF16>
 __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
   static_assert(D % 32 == 0 && D <= 128, "head size must be 32, 64 or 128");
   constexpr int KS = D / 32;   // k-steps of the score product
@@ -203,7 +197,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
   for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) o[qt][dt] = f32x4{0, 0, 0, 0};
-  float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
+  float m_run[2] = {-INFINITY, -INFINITY};
+  // row sums of P on the MFMA: an all-ones A operand makes every row of the
+  // product the sum over the keys (every lane of a query holds it)
+  f32x4 lsum[2] = {f32x4{0, 0, 0, 0}, f32x4{0, 0, 0, 0}};
+  f16x8 ones;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ones[e] = (_Float16)1.0f;
   const float sc = a.scale * 1.4426950408889634f;  // scale to base-2 units
 
   // V^T fragment addressing (transposing load): lane j of 16-lane block g
@@ -219,15 +219,18 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
       const int c = tid + i * kThreads;
       const int r = c / CPR, ch = c - r * CPR;
       *reinterpret_cast<uint4*>(sK + r * KP + 8 * ch) = pk[i];
-      const uint4 w = pv[i];
-      const uint32_t u[4] = {w.x, w.y, w.z, w.w};
-      f16x8 hv;
+      if constexpr (VF16) {
+        *reinterpret_cast<uint4*>(sV + r * KP + 8 * ch) = pv[i];
+      } else {  // bf16 V -> f16
+        const uint32_t u[4] = {pv[i].x, pv[i].y, pv[i].z, pv[i].w};
+        f16x8 hv;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        hv[2 * e] = (_Float16)__uint_as_float(u[e] << 16);
-        hv[2 * e + 1] = (_Float16)__uint_as_float(u[e] & 0xffff0000u);
+        for (int e = 0; e < 4; ++e) {
+          hv[2 * e] = (_Float16)__uint_as_float(u[e] << 16);
+          hv[2 * e + 1] = (_Float16)__uint_as_float(u[e] & 0xffff0000u);
+        }
+        *reinterpret_cast<f16x8*>(sV + r * KP + 8 * ch) = hv;
       }
-      *reinterpret_cast<f16x8*>(sV + r * KP + 8 * ch) = hv;
     }
     const int n_tile = n_cur;
     lds_barrier();
@@ -272,22 +275,16 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
       const float m_new = move ? mx : m_run[qt];
       if (__builtin_amdgcn_ballot_w64(move)) {
         const float corr = __builtin_amdgcn_exp2f(m_run[qt] - m_new);  // 0 when m_run = -inf, 1 when kept
-        l_run[qt] *= corr;
+        lsum[qt] *= corr;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) o[qt][dt] *= corr;
         m_run[qt] = m_new;
       }
-      float rs = 0.f;
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
+      for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float pe = __builtin_amdgcn_exp2f(fmaf(s[kt][qt][e], sc, -m_new));
-          rs += pe;
-          p[kt >> 1][qt][4 * (kt & 1) + e] = (_Float16)pe;
-        }
-      }
-      l_run[qt] += rows4_sum(rs);
+        for (int e = 0; e < 4; ++e)
+          p[kt >> 1][qt][4 * (kt & 1) + e] = (_Float16)__builtin_amdgcn_exp2f(fmaf(s[kt][qt][e], sc, -m_new));
     }
     // ---- O^T += V^T P^T on 16x16x32 MFMA: the k order of a 32-key pair is
     // (16-key sub-tile 2kp, keys 4g .. 4g+3; sub-tile 2kp+1, keys 4g .. 4g+3)
@@ -304,6 +301,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
         o[0][dt] = mfma_f16(vf, p[kp][0], o[0][dt]);
         o[1][dt] = mfma_f16(vf, p[kp][1], o[1][dt]);
       }
+      lsum[0] = mfma_f16(ones, p[kp][0], lsum[0]);
+      lsum[1] = mfma_f16(ones, p[kp][1], lsum[1]);
     }
     lds_barrier();
   }
@@ -314,25 +313,33 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
   for (int qt = 0; qt < 2; ++qt) {
     const int qi = wave * 32 + qt * 16 + ln;
     if (qi >= nq_tile) continue;
-    const float inv = l_run[qt] > 0.f ? 1.f / l_run[qt] : 0.f;
+    const float inv = lsum[qt][0] > 0.f ? 1.f / lsum[qt][0] : 0.f;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) store_out4<OUT>(a.out, obase + (size_t)(q0 + qi) * D + 16 * dt + 4 * lg, o[qt][dt] * inv);
   }
 }
 
-int launch_attn(const AttnArgs& a, int d, int out_dtype, hipStream_t stream) {
-  if (a.H == 0 || a.tiles_per_head == 0) return 0;
+template <bool VF16>
+static int launch_attn_v(const AttnArgs& a, int d, int out_dtype, hipStream_t stream) {
   dim3 grid((unsigned)(a.H * a.tiles_per_head)), block(kThreads);
-#define VDA_AT(DD)                                                                                 \
-  if (d == DD) {                                                                                   \
-    if (out_dtype == VDA_F32) hipLaunchKernelGGL((attn_kernel<DD, VDA_F32>), grid, block, 0, stream, a); \
-    else if (out_dtype == VDA_BF16) hipLaunchKernelGGL((attn_kernel<DD, VDA_BF16>), grid, block, 0, stream, a); \
-    else hipLaunchKernelGGL((attn_kernel<DD, VDA_F16>), grid, block, 0, stream, a);               \
-    return 0;                                                                                      \
+#define VDA_AT(DD)                                                                                         \
+  if (d == DD) {                                                                                           \
+    if (out_dtype == VDA_F32)                                                                              \
+      hipLaunchKernelGGL((attn_kernel<DD, VDA_F32, VF16>), grid, block, 0, stream, a);                     \
+    else if (out_dtype == VDA_BF16)                                                                        \
+      hipLaunchKernelGGL((attn_kernel<DD, VDA_BF16, VF16>), grid, block, 0, stream, a);                    \
+    else                                                                                                   \
+      hipLaunchKernelGGL((attn_kernel<DD, VDA_F16, VF16>), grid, block, 0, stream, a);                     \
+    return 0;                                                                                              \
   }
   VDA_AT(32) VDA_AT(64) VDA_AT(128)
 #undef VDA_AT
   return -1;
+}
+
+int launch_attn(const AttnArgs& a, int d, int out_dtype, hipStream_t stream) {
+  if (a.H == 0 || a.tiles_per_head == 0) return 0;
+  return a.v_f16 ? launch_attn_v<true>(a, d, out_dtype, stream) : launch_attn_v<false>(a, d, out_dtype, stream);
 }
 
 }  // namespace vda

@@ -57,12 +57,13 @@ struct ReadArgs {
 struct AttnArgs {
   const void* q;          // [H][T][U][d] bf16 (after the branch's QK normalisation and rotary encoding)
   const void* k;          // [H][T][U][d] bf16
-  const void* v;          // [H][T][U][d] bf16
+  const void* v;          // [H][T][U][d] bf16 or f16 (v_f16)
   const void* kt;         // [H][Nt][d] bf16 or nullptr (Nt = 0)
-  const void* vt;         // [H][Nt][d] bf16 or nullptr
+  const void* vt;         // [H][Nt][d] like v, or nullptr
   void* out;              // [H][T][U][d]
   int H, T, U, a, P, C, w, Nt;
   float scale;
+  int v_f16;              // v, vt are f16 (else bf16)
   int tiles_per_head, anchor_tiles, chunk_tiles;  // 128-query workgroups
 };
 

@@ -82,7 +82,8 @@ def load(path: str | None = None):
         "vda_readout": [D, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p],
         "vda_readout_gated": [D, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_float,
                               c_void_p, c_void_p],
-        "vda_softmax_branch": [D, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_float, c_void_p, c_void_p],
+        "vda_softmax_branch": [D, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_float, c_void_p,
+                               c_void_p],
         "vda_forward": [D, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                         c_void_p, c_void_p, c_size_t, c_void_p, c_void_p, c_void_p, c_void_p],
         "vda_device_status": [D, c_void_p, c_void_p, POINTER(c_int32)],
@@ -212,9 +213,9 @@ def vda_readout_gated(desc, q, alpha, states_fwd, states_rev, gate, norm_weight,
                                     _stream(stream)))
 
 
-def vda_softmax_branch(desc, q, k, v, k_text, v_text, scale, out, stream=None):
+def vda_softmax_branch(desc, q, k, v, k_text, v_text, scale, out, v_dtype="bf16", stream=None):
     _check(load().vda_softmax_branch(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(k_text), _ptr(v_text),
-                                     float(scale), _ptr(out), _stream(stream)))
+                                     DTYPES[v_dtype], float(scale), _ptr(out), _stream(stream)))
 
 
 def vda_forward(desc, q, k, v, beta, alpha, k_text, v_text, beta_text, ws, states_fwd, states_rev, out,

@@ -204,15 +204,18 @@ int vda_readout_gated(const vda_desc* desc, const void* q, const float* alpha, c
  *  - a frame of chunk c sees the frames of chunks c-w .. c+w (clipped to
  *    [0, C-1]) and the two anchor frames;
  *  - an anchor frame (0 or T-1) sees every frame.
- * q, k, v [H][T][U][d] and k_text, v_text [H][N_text][d] are bf16 (the
- * projections after the branch's QK normalisation and rotary encoding);
- * out [H][T][U][d] out_dtype, every row written (anchor rows included).
+ * q, k [H][T][U][d] and k_text [H][N_text][d] are bf16 (the projections
+ * after the branch's QK normalisation and rotary encoding); v [H][T][U][d]
+ * and v_text [H][N_text][d] are v_dtype, VDA_BF16 or VDA_F16 (f16 values
+ * are used as given; bf16 ones are converted to f16 in the kernel, which
+ * costs some throughput); out [H][T][U][d] out_dtype, every row written
+ * (anchor rows included).
  * Needs in_dtype == VDA_BF16 (else VDA_ERR_DTYPE), d in {32, 64, 128} and
  * window >= 0 (else VDA_ERR_SHAPE), scale > 0 and finite (else
  * VDA_ERR_VALUE; 1/sqrt(d) is the usual choice).  VDA_PREP and VDA_NO_BRIDGE
  * do not apply.  k_text and v_text may be NULL when text_tokens == 0. */
 int vda_softmax_branch(const vda_desc* desc, const void* q, const void* k, const void* v, const void* k_text,
-                       const void* v_text, float scale, void* out, void* stream);
+                       const void* v_text, int32_t v_dtype, float scale, void* out, void* stream);
 
 /* The whole path in one call: vda_prepare_frames, vda_scan_bidir (S_init =
  * S^T from the text tokens, or zero) and vda_readout, with the same

@@ -123,21 +123,23 @@ def test_null_and_workspace_checks_precede_any_device_call():
         assert rc == vda.VDA_ERR_VALUE, eps
     # softmax branch: bf16 inputs, d >= 32, window >= 0, positive scale, pointers
     db = _desc(in_dtype="bf16", d=32)
-    rc = lib.vda_softmax_branch(ctypes.byref(d), fake, fake, fake, fake, fake, 0.1, fake, None)
+    rc = lib.vda_softmax_branch(ctypes.byref(d), fake, fake, fake, fake, fake, 1, 0.1, fake, None)
     assert rc == vda.VDA_ERR_DTYPE  # f32 inputs
-    rc = lib.vda_softmax_branch(ctypes.byref(_desc(in_dtype="bf16")), fake, fake, fake, fake, fake, 0.1, fake, None)
+    rc = lib.vda_softmax_branch(ctypes.byref(_desc(in_dtype="bf16")), fake, fake, fake, fake, fake, 1, 0.1, fake, None)
     assert rc == vda.VDA_ERR_SHAPE  # d = 16
     rc = lib.vda_softmax_branch(ctypes.byref(_desc(in_dtype="bf16", d=32, window=-1)), fake, fake, fake, fake,
-                                fake, 0.1, fake, None)
+                                fake, 1, 0.1, fake, None)
     assert rc == vda.VDA_ERR_SHAPE
+    rc = lib.vda_softmax_branch(ctypes.byref(db), fake, fake, fake, fake, fake, 0, 0.1, fake, None)
+    assert rc == vda.VDA_ERR_DTYPE  # v as f32
     for sc in (0.0, -1.0, float("nan"), float("inf")):
-        rc = lib.vda_softmax_branch(ctypes.byref(db), fake, fake, fake, fake, fake, sc, fake, None)
+        rc = lib.vda_softmax_branch(ctypes.byref(db), fake, fake, fake, fake, fake, 1, sc, fake, None)
         assert rc == vda.VDA_ERR_VALUE, sc
-    rc = lib.vda_softmax_branch(ctypes.byref(db), None, fake, fake, fake, fake, 0.1, fake, None)
+    rc = lib.vda_softmax_branch(ctypes.byref(db), None, fake, fake, fake, fake, 1, 0.1, fake, None)
     assert rc == vda.VDA_ERR_NULL
-    rc = lib.vda_softmax_branch(ctypes.byref(db), fake, fake, fake, None, fake, 0.1, fake, None)
+    rc = lib.vda_softmax_branch(ctypes.byref(db), fake, fake, fake, None, fake, 1, 0.1, fake, None)
     assert rc == vda.VDA_ERR_NULL  # text tokens without k_text
-    rc = lib.vda_softmax_branch(ctypes.byref(db), fake, fake, fake + 2, fake, fake, 0.1, fake, None)
+    rc = lib.vda_softmax_branch(ctypes.byref(db), fake, fake, fake + 2, fake, fake, 1, 0.1, fake, None)
     assert rc == vda.VDA_ERR_ALIGN
 
 
@@ -157,7 +159,7 @@ def test_valid_call_without_gpu_reports_no_device():
     assert rc == vda.VDA_ERR_DEVICE
     rc = lib.vda_readout_gated(ctypes.byref(d), fake, fake, fake, fake, fake, fake, 1e-6, fake, None)
     assert rc == vda.VDA_ERR_DEVICE
-    rc = lib.vda_softmax_branch(ctypes.byref(_desc(in_dtype="bf16", d=32)), fake, fake, fake, fake, fake, 0.1,
+    rc = lib.vda_softmax_branch(ctypes.byref(_desc(in_dtype="bf16", d=32)), fake, fake, fake, fake, fake, 1, 0.1,
                                 fake, None)
     assert rc == vda.VDA_ERR_DEVICE
 

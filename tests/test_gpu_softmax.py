@@ -14,7 +14,7 @@ pytestmark = pytest.mark.gpu
 TOL = 2e-3   # relative L2; P is rounded to f16 and a bf16 output adds its own rounding
 
 
-def _run(cfg, out_dtype="bf16", scale=None):
+def _run(cfg, out_dtype="bf16", scale=None, v_dtype="bf16"):
     import torch
     print(f"[softmax] {cfg.name} H={cfg.heads} T={cfg.frames} U={cfg.tokens} d={cfg.d} window={cfg.window} "
           f"anchors={cfg.anchors} text={cfg.text_tokens} out={out_dtype}", flush=True)
@@ -22,17 +22,20 @@ def _run(cfg, out_dtype="bf16", scale=None):
     dev = lambda name: runner._dev(np.stack([getattr(x, name) for x in ins]), "cuda")
     q, k, v = dev("q"), dev("k"), dev("v")
     kt, vt = (dev("kt"), dev("vt")) if cfg.text_tokens else (None, None)
+    if v_dtype == "f16":  # the same bf16 values, stored as f16 (exact)
+        v = v.view(torch.bfloat16).to(torch.float16)
+        vt = None if vt is None else vt.view(torch.bfloat16).to(torch.float16)
     desc = vda.desc_for(cfg, in_dtype="bf16", out_dtype=out_dtype)
     out = torch.empty((cfg.heads, cfg.frames, cfg.tokens, cfg.d), device="cuda",
                       dtype={"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[out_dtype])
     scale = 1.0 / np.sqrt(cfg.d) if scale is None else scale
-    vda.vda_softmax_branch(desc, q, k, v, kt, vt, scale, out)
+    vda.vda_softmax_branch(desc, q, k, v, kt, vt, scale, out, v_dtype=v_dtype)
     torch.cuda.synchronize()
     return ins, out.float().cpu().numpy().astype(np.float64), scale
 
 
-def _check(cfg, out_dtype="bf16", heads=None, frames=None, scale=None):
-    ins, O, scale = _run(cfg, out_dtype, scale)
+def _check(cfg, out_dtype="bf16", heads=None, frames=None, scale=None, v_dtype="bf16"):
+    ins, O, scale = _run(cfg, out_dtype, scale, v_dtype)
     for h in (range(cfg.heads) if heads is None else heads):
         x = ins[h]
         text = cfg.text_tokens > 0
@@ -63,6 +66,16 @@ def test_softmax_branch_output_dtypes(out_dtype):
     _check(inp.scaled(inp.CONFIG_BY_NAME["h3"], heads=1, frames=12, tokens=70, text_tokens=20), out_dtype)
 
 
+@pytest.mark.parametrize("over", [
+    dict(heads=2, frames=12, tokens=100, text_tokens=64),
+    dict(heads=1, frames=22, tokens=64, d=64, text_tokens=100),
+])
+def test_softmax_branch_f16_values(over):
+    """V given as f16 (the bf16 draws, exactly representable) skips the
+    conversion in the kernel and gives the same result."""
+    _check(inp.scaled(inp.CONFIG_BY_NAME["h3"], **over), v_dtype="f16")
+
+
 def test_softmax_branch_other_scale():
     _check(inp.scaled(inp.CONFIG_BY_NAME["h3"], heads=1, frames=12, tokens=70, text_tokens=20), "f32", scale=0.3)
 
@@ -73,7 +86,7 @@ def test_softmax_branch_h3_full_size_sampled_frames():
     512 text tokens); the oracle checks head 5 on an anchor frame, the first
     and a middle chunk's frames and the last anchor."""
     cfg = inp.CONFIG_BY_NAME["h3"]
-    ins, O, scale = _run(cfg)
+    ins, O, scale = _run(cfg, v_dtype="f16")
     x = ins[5]
     f = x.f64
     keys = orc.softmax_key_frames(cfg.frames, cfg.chunk, cfg.window, cfg.anchors)
