@@ -13,12 +13,16 @@ a roofline entry for the dominant HBM-bound kernel timed with HIP events on
 the stream it runs on, and the float64 oracle timed on this host's cores.
 
     python bench.py [--steps K] [--warmup W] [--config h3] [--no-cpu-baseline] [--epilogue] [--prep]
+    python bench.py --softmax [--steps K] [--warmup W]
 
 --epilogue replaces the readout by vda_readout_gated (the readout followed by
 the RMSNorm + sigmoid-gate epilogue of the linear branch, with seeded gate
 logits and norm weights); --prep feeds raw projections (q, k not normalised,
 beta and alpha as logits) and sets VDA_PREP, so the kernels normalise and
 gate them.  Both measure next steps of the path; neither is the default line.
+--softmax times the softmax window + anchor + text branch (vda_softmax_branch)
+on the same workload instead: an MFMA-bound kernel, reported against the
+bf16 MFMA peak.
 
 Measurement helpers (used to make the files under profiles/):
 
@@ -230,6 +234,79 @@ def cpu_baseline(cfg, heads_in, out0, budget_s=15.0, epi_in=None, prep=False):
             rel)
 
 
+def softmax_work(cfg):
+    """Algorithmic FLOPs and HBM bytes of the softmax branch: 4d FLOPs per
+    (query, visible key) pair (q.k and p.v), and Q, K, V (bf16), text K, V
+    and O (bf16) once."""
+    T, P, w = cfg.frames, cfg.chunk, cfg.window
+    a = 1 if cfg.anchors else 0
+    n = T - 2 * a
+    C = -(-n // P)
+    visible = 0
+    for t in range(T):
+        if a and t in (0, T - 1):
+            visible += T                       # an anchor frame sees every frame
+        else:
+            c = (t - a) // P                   # window: chunks c-w .. c+w, clipped
+            lo, hi = max(c - w, 0), min(c + w, C - 1)
+            visible += min(a + P * (hi + 1), T - a) - (a + P * lo) + 2 * a
+    pairs = (visible * cfg.tokens + T * cfg.text_tokens) * cfg.tokens
+    flops = 4 * cfg.d * pairs * cfg.heads
+    nbytes = cfg.heads * (4 * cfg.frames * cfg.tokens * cfg.d * 2 + 2 * cfg.text_tokens * cfg.d * 2)
+    return flops, nbytes
+
+
+def softmax_bench(args):
+    """The softmax branch on the H3-shaped workload: seeded bf16 q, k, f16 v
+    (the same draws, exactly representable), resident in HBM; K timed calls."""
+    import torch
+    from frame_wise_delta_amd import inputs as inp
+    from frame_wise_delta_amd import runner, vda
+    cfg = inp.CONFIG_BY_NAME[args.config]
+    if cfg.window < 0:
+        sys.exit(f"bench.py --softmax: config {cfg.name} has no window (the softmax branch needs one)")
+    t0 = time.time()
+    ins = [inp.softmax_inputs(cfg, h) for h in range(cfg.heads)]
+    dev = lambda name: runner._dev(np.stack([getattr(x, name) for x in ins]), "cuda")
+    q, k = dev("q"), dev("k")
+    v = dev("v").view(torch.bfloat16).to(torch.float16)
+    kt, vt = dev("kt"), dev("vt").view(torch.bfloat16).to(torch.float16)
+    print(f"[bench] softmax inputs drawn in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+    out = torch.empty((cfg.heads, cfg.frames, cfg.tokens, cfg.d), dtype=torch.bfloat16, device="cuda")
+    desc = vda.desc_for(cfg)
+    scale = 1.0 / np.sqrt(cfg.d)
+    st = torch.cuda.current_stream()
+    call = lambda: vda.vda_softmax_branch(desc, q, k, v, kt, vt, scale, out, v_dtype="f16", stream=st)
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(st)
+    for _ in range(args.steps):
+        call()
+    e1.record(st)
+    torch.cuda.synchronize()
+    ms = 1e3 * (time.perf_counter() - t0) / args.steps
+    ms_ev = e0.elapsed_time(e1) / args.steps
+    flops, nbytes = softmax_work(cfg)
+    tf = flops / (ms_ev / 1e3) / 1e12
+    res = {
+        "metric": "softmax window + anchor + text branch TFLOP/s and % of MI355X bf16 MFMA peak",
+        "value": round(tf, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: {cfg.heads} heads, d={cfg.d}, {cfg.frames} latent frames, "
+                               f"U={cfg.tokens}, window +-{cfg.window} chunk of {cfg.chunk}, 2 anchors, "
+                               f"{cfg.text_tokens} text tokens; q, k bf16, v f16, bf16 out"},
+        "roofline": {"kernel": "attn_kernel", "bound": "mfma", "achieved": round(tf, 1), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "algorithmic_flops_per_launch": flops, "avg_ms": round(ms_ev, 4)},
+        "hbm_bytes_algorithmic": nbytes,
+    }
+    print(json.dumps(res))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -243,6 +320,8 @@ def main():
                     help="time the readout with the RMSNorm + sigmoid-gate epilogue (vda_readout_gated)")
     ap.add_argument("--prep", action="store_true",
                     help="raw inputs prepared inside the kernels (VDA_PREP: L2 normalisation, sigmoid gates)")
+    ap.add_argument("--softmax", action="store_true",
+                    help="time the softmax window + anchor + text branch instead of the linear branch")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--traffic", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"))
     args = ap.parse_args()
@@ -256,6 +335,9 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.softmax:
+        softmax_bench(args)
         return
 
     import torch
