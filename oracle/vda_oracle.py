@@ -27,6 +27,9 @@ the section heading of that page:
 * [VDN 方法步骤详情 step (4)]        S^T initialises the two scans "by halves".
 * [VDN 方法步骤详情 step (5)]        window-boundary states are carried to the
   query through the decay bridge prod(alpha_r).
+* [VDN 方法步骤详情 step (3)-(4)]    per-frame transition M_t and injection J_t
+  from I + A_t, composed over each chunk and scanned at chunk level,
+  S_out = S_in M_chunk + J_chunk.
 
 Readings of points the page leaves open:
 
@@ -46,12 +49,18 @@ Readings of points the page leaves open:
 * Prep: q and k are normalised as x / sqrt(||x||^2 + eps) per token
   (eps = 1e-6); the write gate is beta = sigmoid(logit) per token and the
   decay gate alpha = sigmoid(logit) per frame and channel.
+* Chunk maps: M_t = Diag(alpha_t)(I + A_t)^{-1} and J_t = B_t (I + A_t)^{-1},
+  so that S_t = S_{t-1} M_t + J_t is the frame write; a chunk's map is the
+  composition of its frames' affine maps in scan order (the reverse scan
+  composes them last frame first).
 * Epilogue: RMSNorm over the d_v channels of each token with a per-head
   weight and epsilon, then an elementwise sigmoid gate on per-channel logits
   (which come from the layer input and are given here).
 
 Everything is float64; matrix products and linear solves are NumPy/LAPACK
-calls used as single steps.  No blocking, chunk composition or reordering.
+calls used as single steps.  No blocking or reordering; the chunk-level scan
+(``scan_chunked``) is kept apart from the frame-level ``scan`` that the rest
+of the oracle uses.
 """
 from __future__ import annotations
 
@@ -136,6 +145,48 @@ def scan(order, K, V, beta, alpha, S0, record_every: int):
         S = frame_update(S, K[t], V[t], beta[t], alpha[t])
         if (i + 1) % record_every == 0 or i + 1 == len(order):
             states.append(S.copy())
+    return np.stack(states)
+
+
+def frame_map(K: np.ndarray, V: np.ndarray, beta: np.ndarray, alpha: np.ndarray):
+    """The frame write as an affine map S -> S M_t + J_t [VDN 方法步骤详情
+    step (3): transition M_t and injection J_t from the factorised I + A_t]:
+    M_t = Diag(alpha_t)(I + A_t)^{-1}, J_t = B_t (I + A_t)^{-1}.  Both come
+    from solves with the symmetric I + A_t (M_t^T = (I+A_t)^{-1} Diag(alpha_t),
+    J_t^T = (I+A_t)^{-1} B_t^T); no inverse is formed."""
+    A, B = frame_stats(K, V, beta)
+    G = np.eye(A.shape[0]) + A
+    M = np.linalg.solve(G, np.diag(alpha)).T
+    J = np.linalg.solve(G, B.T).T
+    return M, J
+
+
+def chunk_map(frames_in_order, K, V, beta, alpha):
+    """Affine map of a run of frames [VDN 方法步骤详情 step (4): chunk-level
+    scan S_out = S_in M_chunk + J_chunk]: starting from the identity map,
+    each frame t (in scan order) composes as (M, J) -> (M M_t, J M_t + J_t),
+    which is applying S -> S M + J and then S -> S M_t + J_t."""
+    d_k, d_v = K.shape[-1], V.shape[-1]
+    M = np.eye(d_k)
+    J = np.zeros((d_v, d_k))
+    for t in frames_in_order:
+        Mt, Jt = frame_map(K[t], V[t], beta[t], alpha[t])
+        M = M @ Mt
+        J = J @ Mt + Jt
+    return M, J
+
+
+def scan_chunked(order, K, V, beta, alpha, S0, chunk: int):
+    """The scan at chunk level [VDN 方法步骤详情 step (4)]: the frames in
+    ``order`` are taken ``chunk`` at a time (the last run may be shorter);
+    each run's map is composed by ``chunk_map`` and applied once,
+    S <- S M_chunk + J_chunk.  Returns the states after 0, 1, 2, ... runs."""
+    S = S0.copy()
+    states = [S.copy()]
+    for i in range(0, len(order), chunk):
+        M, J = chunk_map(order[i:i + chunk], K, V, beta, alpha)
+        S = S @ M + J
+        states.append(S.copy())
     return np.stack(states)
 
 

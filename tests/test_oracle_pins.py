@@ -215,6 +215,65 @@ def test_scan_records_every_chunk_boundary():
     assert np.array_equal(per_chunk, per_frame[::5])
 
 
+# ------------------------------------------------ chunk composition (a3) --
+
+@pytest.mark.parametrize("P", [1, 3, 5, 7])
+def test_chunk_scan_equals_frame_scan_at_every_boundary(P):
+    """S_out = S_in M_chunk + J_chunk (方法步骤详情 step (4)) reaches the
+    frame-by-frame states at each chunk boundary, forward and reverse,
+    including a shorter last run (20 frames in runs of 3 or 7)."""
+    q, k, v, beta, alpha, kt, vt, bt = _small_cfg_inputs(T=22)
+    order = list(range(1, 21))
+    S0 = 0.5 * orc.text_state(kt, vt, bt, 8, 8)
+    for o in (order, order[::-1]):
+        ref = orc.scan(o, k, v, beta, alpha, S0, P)
+        got = orc.scan_chunked(o, k, v, beta, alpha, S0, P)
+        assert got.shape == ref.shape
+        assert np.abs(got - ref).max() <= 1e-12 * np.abs(ref).max()
+
+
+def test_frame_map_satisfies_the_normal_equations():
+    """M_t (I + A_t) = Diag(alpha_t) and J_t (I + A_t) = B_t, with A_t and
+    B_t summed token by token (方法步骤详情 step (3))."""
+    g = np.random.default_rng(21)
+    for U, d in ((1, 4), (9, 6), (50, 16)):
+        _, K, V, beta, alpha = _frame(g, U, d)
+        A = sum(beta[u] * np.outer(K[u], K[u]) for u in range(U))
+        B = sum(beta[u] * np.outer(V[u], K[u]) for u in range(U))
+        M, J = orc.frame_map(K, V, beta, alpha)
+        G = np.eye(d) + A
+        assert np.abs(M @ G - np.diag(alpha)).max() <= 1e-12
+        assert np.abs(J @ G - B).max() <= 1e-12 * max(1.0, np.abs(B).max())
+
+
+def test_chunk_map_without_writes_is_pure_decay_and_non_expansive():
+    """beta = 0: M_chunk = Diag(prod alpha) and J_chunk = 0.  With writes,
+    ||M_chunk||_2 <= 1 (a product of non-expansive transitions, 核心方法
+    para 2)."""
+    q, k, v, beta, alpha, *_ = _small_cfg_inputs(T=12)
+    frames = [3, 4, 5, 6, 7]
+    M, J = orc.chunk_map(frames, k, v, np.zeros_like(beta), alpha)
+    assert np.abs(M - np.diag(np.prod(alpha[frames], axis=0))).max() <= 1e-15
+    assert np.abs(J).max() == 0.0
+    for fr in (frames, frames[::-1], [2]):
+        M, _ = orc.chunk_map(fr, k, v, beta, alpha)
+        assert np.linalg.norm(M, 2) <= 1 + 1e-12
+
+
+def test_chunk_map_order_matters_and_reverse_matches_reversed_time():
+    """The reverse scan composes a chunk last frame first; on time-reversed
+    input it is the forward composition."""
+    q, k, v, beta, alpha, *_ = _small_cfg_inputs(T=12)
+    fr = [3, 4, 5, 6, 7]
+    Mf, Jf = orc.chunk_map(fr, k, v, beta, alpha)
+    Mr, Jr = orc.chunk_map(fr[::-1], k, v, beta, alpha)
+    assert np.abs(Mf - Mr).max() > 1e-6  # the transitions do not commute
+    T = k.shape[0]
+    rev = [T - 1 - t for t in fr[::-1]]
+    M2, J2 = orc.chunk_map(rev, k[::-1], v[::-1], beta[::-1], alpha[::-1])
+    assert np.array_equal(M2, Mr) and np.array_equal(J2, Jr)
+
+
 # ---------------------------------------------------------------- maps ----
 
 def _closed_form_rows(T, P, w, anchors):
