@@ -13,6 +13,7 @@ a roofline entry for the dominant HBM-bound kernel timed with HIP events on
 the stream it runs on, and the float64 oracle timed on this host's cores.
 
     python bench.py [--steps K] [--warmup W] [--config h3] [--no-cpu-baseline] [--epilogue] [--prep]
+                    [--chunk-scan]
     python bench.py --softmax [--steps K] [--warmup W]
 
 --epilogue replaces the readout by vda_readout_gated (the readout followed by
@@ -20,6 +21,8 @@ the RMSNorm + sigmoid-gate epilogue of the linear branch, with seeded gate
 logits and norm weights); --prep feeds raw projections (q, k not normalised,
 beta and alpha as logits) and sets VDA_PREP, so the kernels normalise and
 gate them.  Both measure next steps of the path; neither is the default line.
+--chunk-scan sets VDA_CHUNK_SCAN: vda_compose_chunks after the factorisation,
+then the scans at chunk level (S <- S M_c + J_c once per chunk).
 --softmax times the softmax window + anchor + text branch (vda_softmax_branch)
 on the same workload instead: an MFMA-bound kernel, reported against the
 bf16 MFMA peak.
@@ -52,7 +55,7 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16/f16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 COPY_BYTES = 512 * 1024 * 1024
-KERNELS = ("stats_kernel", "gj_kernel", "scan_kernel", "readout_kernel", "readout_gated")
+KERNELS = ("stats_kernel", "gj_kernel", "scan_kernel", "compose_kernel", "readout_kernel", "readout_gated")
 EPS = 1e-6  # RMSNorm epsilon of the epilogue
 
 
@@ -91,7 +94,7 @@ def kernel_bytes(cfg):
 
 
 KERNEL_SRC = {"stats_kernel": "vda_prepare.hip", "gj_kernel": "vda_prepare.hip",
-              "scan_kernel": "vda_scan.hip", "readout_kernel": "vda_readout.hip",
+              "scan_kernel": "vda_scan.hip", "compose_kernel": "vda_scan.hip", "readout_kernel": "vda_readout.hip",
               "readout_gated": "vda_readout.hip"}
 
 
@@ -320,6 +323,8 @@ def main():
                     help="time the readout with the RMSNorm + sigmoid-gate epilogue (vda_readout_gated)")
     ap.add_argument("--prep", action="store_true",
                     help="raw inputs prepared inside the kernels (VDA_PREP: L2 normalisation, sigmoid gates)")
+    ap.add_argument("--chunk-scan", action="store_true",
+                    help="scans at chunk level from composed chunk maps (VDA_CHUNK_SCAN)")
     ap.add_argument("--softmax", action="store_true",
                     help="time the softmax window + anchor + text branch instead of the linear branch")
     ap.add_argument("--copy-calibration", action="store_true")
@@ -348,7 +353,7 @@ def main():
     t0 = time.time()
     heads_in = inp.all_raw_heads(cfg) if args.prep else inp.all_heads(cfg)
     print(f"[bench] inputs for {cfg.name} drawn in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
-    desc = vda.desc_for(cfg, prep=args.prep)
+    desc = vda.desc_for(cfg, prep=args.prep, chunk_scan=args.chunk_scan)
     dev = runner.upload(cfg, heads_in, "cuda")
     bufs = runner.allocate(desc, cfg.out_dtype, "cuda")
     epi_in, gate, norm_w = None, None, None
@@ -358,7 +363,7 @@ def main():
     main_s = torch.cuda.current_stream()
 
     # events around each call, on the stream they all run on
-    names = ["stats", "factor", "scans", "readout"]
+    names = ["stats", "factor"] + (["compose"] if args.chunk_scan else []) + ["scans", "readout"]
     ev = {k: [] for k in names}
 
     def step(record):
@@ -375,6 +380,10 @@ def main():
         mark("factor", 0)
         vda.vda_factor_frames(desc, b.ws, b.ws_bytes, stream=main_s)
         mark("factor", 1)
+        if args.chunk_scan:
+            mark("compose", 0)
+            vda.vda_compose_chunks(desc, b.ws, x.alpha, ws_bytes=b.ws_bytes, stream=main_s)
+            mark("compose", 1)
         mark("scans", 0)
         vda.vda_scan_bidir(desc, b.ws, x.alpha, None, b.states_f, b.states_r, stream=main_s)
         mark("scans", 1)
@@ -437,8 +446,9 @@ def main():
                                f"({cfg.anchors * 2} anchors, chunks of {cfg.chunk}, window +-{cfg.window} "
                                f"chunk), U={cfg.tokens}, {cfg.text_tokens} text tokens"
                                + (", readout epilogue (RMSNorm + sigmoid gate)" if args.epilogue else "")
-                               + (", raw inputs prepared in the kernels" if args.prep else ""),
-                   "epilogue": bool(args.epilogue), "prep": bool(args.prep),
+                               + (", raw inputs prepared in the kernels" if args.prep else "")
+                               + (", chunk-level scans from composed chunk maps" if args.chunk_scan else ""),
+                   "epilogue": bool(args.epilogue), "prep": bool(args.prep), "chunk_scan": bool(args.chunk_scan),
                    "heads": cfg.heads, "d": cfg.d, "frames": cfg.frames, "tokens": cfg.tokens,
                    "text_tokens": cfg.text_tokens, "in_dtype": cfg.in_dtype, "out_dtype": cfg.out_dtype,
                    "state_dtype": "f32", "global_batch": 1, "seq_len": cfg.frames * cfg.tokens,

@@ -31,6 +31,7 @@ int ok() {
 
 struct Shape {
   int H, T, U, d, P, a, n, C, w, Nt, n_eff, count;
+  bool chunked;  // VDA_CHUNK_SCAN
 };
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -55,7 +56,10 @@ int check_desc(const vda_desc* desc, Shape* s) {
   if (q.out_dtype != VDA_F32 && q.out_dtype != VDA_BF16 && q.out_dtype != VDA_F16)
     return fail(VDA_ERR_DTYPE, "out_dtype = %d (VDA_F32, VDA_BF16 or VDA_F16)", q.out_dtype);
   if (!(q.text_init_scale == q.text_init_scale)) return fail(VDA_ERR_SHAPE, "text_init_scale is NaN");
-  if (q.flags & ~(uint32_t)(VDA_NO_BRIDGE | VDA_PREP)) return fail(VDA_ERR_SHAPE, "unknown flags 0x%x", q.flags);
+  if (q.flags & ~(uint32_t)(VDA_NO_BRIDGE | VDA_PREP | VDA_CHUNK_SCAN))
+    return fail(VDA_ERR_SHAPE, "unknown flags 0x%x", q.flags);
+  if ((q.flags & VDA_CHUNK_SCAN) && q.window < 0)
+    return fail(VDA_ERR_SHAPE, "VDA_CHUNK_SCAN needs window >= 0 (states at chunk boundaries)");
   s->H = q.heads;
   s->T = q.frames;
   s->U = q.tokens;
@@ -70,6 +74,7 @@ int check_desc(const vda_desc* desc, Shape* s) {
   if (s->w >= 0 && s->n % s->P != 0)
     return fail(VDA_ERR_SHAPE, "windowed readout needs n %% chunk == 0 (n = %d, chunk = %d)", s->n, s->P);
   s->count = (s->w >= 0 ? s->C : s->n) + 1;
+  s->chunked = (q.flags & VDA_CHUNK_SCAN) != 0;
   // 64-bit sizes must not overflow and grids must fit
   const double elems = (double)s->H * s->T * (double)s->U * s->d;
   if (elems > 9.0e15) return fail(VDA_ERR_SHAPE, "tensor too large");
@@ -77,8 +82,13 @@ int check_desc(const vda_desc* desc, Shape* s) {
   return VDA_OK;
 }
 
-size_t ws_bytes(const Shape& s) {
+size_t ws_frames_bytes(const Shape& s) {
   return vda::kWsHeader + (size_t)s.H * s.n_eff * vda::ws_slot_floats(s.d) * sizeof(float);
+}
+
+// the chunk maps follow the frame slots: [H][2 directions][C] x 4 d^2 bytes
+size_t ws_bytes(const Shape& s) {
+  return ws_frames_bytes(s) + (s.chunked ? (size_t)s.H * 2 * s.C * 4 * s.d * s.d : 0);
 }
 
 // One-time check per device that it is a gfx950 GPU.
@@ -215,11 +225,11 @@ int prep_args(const vda_desc* desc, const void* k, const void* v, const float* b
 }
 
 int scan_args(const vda_desc* desc, const void* ws, const float* alpha, const float* s_init, float* states,
-              int reverse, Shape& s, vda::ScanArgs& a) {
+              int reverse, Shape& s, vda::ScanArgs& a, bool need_states = true) {
   int rc = check_desc(desc, &s);
   if (rc) return rc;
   if (!ws) return fail(VDA_ERR_NULL, "ws is NULL");
-  if (!states) return fail(VDA_ERR_NULL, "states is NULL");
+  if (need_states && !states) return fail(VDA_ERR_NULL, "states is NULL");
   if (s.H * (size_t)s.n > 0 && !alpha) return fail(VDA_ERR_NULL, "alpha is NULL");
   if (!aligned16(alpha) || !aligned16(s_init) || !aligned16(states) || ((uintptr_t)ws & 255u))
     return fail(VDA_ERR_ALIGN, "alpha, s_init, states need 16-byte and ws 256-byte alignment");
@@ -238,8 +248,13 @@ int scan_args(const vda_desc* desc, const void* ws, const float* alpha, const fl
   a.use_text = s.Nt > 0;
   a.scale = desc->text_init_scale;
   a.prep = (desc->flags & VDA_PREP) ? 1 : 0;
+  a.chunks = const_cast<char*>(static_cast<const char*>(ws)) + ws_frames_bytes(s);
+  a.C = s.C;
+  a.P = s.P;
   return VDA_OK;
 }
+
+int scan_mode(const Shape& s) { return s.chunked ? vda::kChunkScan : vda::kFrameScan; }
 
 int read_args(const vda_desc* desc, const void* q, const float* alpha, const float* states_fwd,
               const float* states_rev, void* out, Shape& s, vda::ReadArgs& a, bool& any) {
@@ -343,7 +358,7 @@ int vda_scan_fwd(const vda_desc* desc, const void* ws, const float* alpha, const
   if (rc) return rc;
   rc = check_device();
   if (rc) return rc;
-  vda::ScanPair p = {{a, a}, 1};
+  vda::ScanPair p = {{a, a}, 1, scan_mode(s)};
   vda::launch_scan(p, s.d, static_cast<hipStream_t>(stream));
   return launch_status();
 }
@@ -356,7 +371,23 @@ int vda_scan_rev(const vda_desc* desc, const void* ws, const float* alpha, const
   if (rc) return rc;
   rc = check_device();
   if (rc) return rc;
-  vda::ScanPair p = {{a, a}, 1};
+  vda::ScanPair p = {{a, a}, 1, scan_mode(s)};
+  vda::launch_scan(p, s.d, static_cast<hipStream_t>(stream));
+  return launch_status();
+}
+
+int vda_compose_chunks(const vda_desc* desc, void* ws, size_t ws_size, const float* alpha, void* stream) {
+  Shape s;
+  vda::ScanPair p;
+  int rc = scan_args(desc, ws, alpha, nullptr, nullptr, 0, s, p.dir[0], false);
+  if (rc) return rc;
+  if (!s.chunked) return fail(VDA_ERR_SHAPE, "vda_compose_chunks needs VDA_CHUNK_SCAN in desc.flags");
+  if (ws_size < ws_bytes(s)) return fail(VDA_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_size, ws_bytes(s));
+  scan_args(desc, ws, alpha, nullptr, nullptr, 1, s, p.dir[1], false);
+  rc = check_device();
+  if (rc) return rc;
+  p.ndir = 2;
+  p.mode = vda::kCompose;
   vda::launch_scan(p, s.d, static_cast<hipStream_t>(stream));
   return launch_status();
 }
@@ -371,6 +402,7 @@ int vda_scan_bidir(const vda_desc* desc, const void* ws, const float* alpha, con
   rc = check_device();
   if (rc) return rc;
   p.ndir = 2;
+  p.mode = scan_mode(s);
   vda::launch_scan(p, s.d, static_cast<hipStream_t>(stream));
   return launch_status();
 }
@@ -477,6 +509,15 @@ int vda_forward(const vda_desc* desc, const void* q, const void* k, const void* 
   vda::launch_clear_status(pa.status, st);
   vda::launch_stats(pa, s.d, f32, st);
   vda::launch_gj(pa, s.d, st);
+  if (s.chunked) {
+    vda::ScanPair cp = sp;  // both directions' chunk maps in one launch
+    cp.dir[1] = sp.dir[0];
+    cp.dir[1].reverse = 1;
+    cp.ndir = 2;
+    cp.mode = vda::kCompose;
+    vda::launch_scan(cp, s.d, st);
+  }
+  sp.mode = scan_mode(s);
   vda::launch_scan(sp, s.d, st);  // both directions in one launch
   if (any) vda::launch_readout(qa, s.d, desc->in_dtype, desc->out_dtype, st);
   return launch_status();

@@ -30,13 +30,27 @@ struct ScanArgs {
   int use_text;         // S_init = S^T from the text slot (slot n) when s_init == nullptr
   float scale;
   int prep;             // alpha holds logits (the gate is sigmoid(logit))
+  // chunk maps (compose and chunk-scan launches): per head, direction and
+  // chunk, 4 d^2 bytes: M_c (f16, the fragment order of N) then J_c (f16,
+  // accumulator order, see vda_scan.hip)
+  void* chunks;
+  int C, P;
+};
+
+// What a scan launch runs.
+enum ScanMode {
+  kFrameScan = 0,  // S_t = (S_{t-1} Diag(alpha_t) + B_t) N_t over the frames
+  kCompose = 1,    // the chunk maps (M_c, J_c) of every chunk, in parallel
+  kChunkScan = 2,  // S_c = S_{c-1} M_c + J_c over the chunks
 };
 
 // One or two scans in one launch: blocks [0, H RB) run dir[0], the next
-// H RB blocks (when ndir == 2) run dir[1].
+// H RB blocks (when ndir == 2) run dir[1] (compose: H C 2RB blocks per
+// direction).
 struct ScanPair {
   ScanArgs dir[2];
   int ndir;
+  int mode;  // ScanMode
 };
 
 struct ReadArgs {

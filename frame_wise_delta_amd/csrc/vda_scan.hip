@@ -22,6 +22,23 @@
 // The chain is bound by the latency of these per-frame operand loads, so
 // frames are prefetched three or four steps ahead into registers; the barriers wait
 // for LDS traffic only, so the global loads stay in flight across them.
+//
+// The same kernel also runs the scan at chunk level (method-steps section,
+// step (4): S_out = S_in M_chunk + J_chunk), in two launches:
+//  * compose (compose_kernel): the frame write is the affine map
+//    S -> S M_t + J_t with M_t = Diag(alpha_t) N_t and J_t = B_t N_t, so
+//    running the frame step over a chunk's frames on the stacked 2d x d
+//    state [Y; X] from [I; 0] (B zero on the Y rows) leaves Y = M_c and
+//    X = J_c.  Every (head, chunk, direction) is an independent chain of P
+//    steps, so all of them run at once; the reverse direction takes the
+//    chunk's frames last first.  M_c is stored as f16 in the fragment order
+//    of N (column j's k-slices, since M_c is not symmetric) and J_c as f16 in
+//    accumulator order: the f16x4 at index (R * d/16 + ct) * 64 + l holds
+//    J_c[16R + 4(l/16) + e][16ct + l%16].
+//  * chunk scan: C steps of S <- S M_c + J_c, the product on the same MFMA
+//    path as a frame step (S as an f16 hi/lo pair, M_c as the B operand) with
+//    the accumulators starting from J_c; the state is recorded after every
+//    chunk, which is where the windowed readout needs it.
 #include "vda_common.h"
 #include "vda_kernels.h"
 
@@ -53,10 +70,12 @@ struct FrameRegs {
 
 }  // namespace
 
-template <int D>
+template <int D, int MODE>
 __global__ __launch_bounds__(ScanShape<D>::NT) void scan_kernel(ScanPair p) {
+  static_assert(MODE == kFrameScan || MODE == kChunkScan, "compose runs in compose_kernel");
   using SS = ScanShape<D>;
   constexpr int ROWS = SS::ROWS, NQ = SS::NQ, PD = SS::PD;
+  static_assert(NQ == SS::RTS, "one B / J register per 16-row tile");
   __shared__ __attribute__((aligned(16))) float sS[ROWS * D];
   __shared__ __attribute__((aligned(16))) _Float16 sXh[ROWS * SS::XP];
   __shared__ __attribute__((aligned(16))) _Float16 sXl[ROWS * SS::XP];
@@ -80,7 +99,10 @@ __global__ __launch_bounds__(ScanShape<D>::NT) void scan_kernel(ScanPair p) {
   const float* frames = a.frames + (size_t)h * a.n_eff * slot_floats;
   const float* alpha_h = a.alpha + (size_t)h * a.T * D;
   float* states_h = a.states + (size_t)h * a.count * D * D;
-
+  // chunk maps of (head, direction, chunk c): 4 d^2 bytes
+  auto chunk_map = [&](int c) {
+    return static_cast<char*>(a.chunks) + ((size_t)(2 * h + a.reverse) * a.C + c) * (size_t)(4 * D * D);
+  };
   auto load = [&](FrameRegs<D>& fr, int slot, const float* alpha_row) {
     const float* base = frames + (size_t)slot * slot_floats;
     const _Float16* nf = reinterpret_cast<const _Float16*>(base);
@@ -102,10 +124,32 @@ __global__ __launch_bounds__(ScanShape<D>::NT) void scan_kernel(ScanPair p) {
     fr.al = alpha_row ? *reinterpret_cast<const float4*>(alpha_row + xc0) : make_float4(1.f, 1.f, 1.f, 1.f);
   };
 
+  // chunk scan: M_c as the B operand (fragment order, like N) and this
+  // lane's accumulator-order J_c entries
+  auto load_map = [&](FrameRegs<D>& fr, int c) {
+    const char* base = chunk_map(c);
+    const _Float16* mf = reinterpret_cast<const _Float16*>(base);
+    const f16x4* jf = reinterpret_cast<const f16x4*>(base + 2 * D * D);
+#pragma unroll
+    for (int kk = 0; kk < SS::KS; ++kk) {
+      if (lg < SS::LG) {
+        const int chunk = ((ct * SS::KS + kk) * SS::LG + lg) * 16 + lr;
+        fr.nk[kk] = reinterpret_cast<const f16x8*>(mf)[chunk];
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) fr.nk[kk][e] = (_Float16)0.f;
+      }
+    }
+#pragma unroll
+    for (int rt = 0; rt < SS::RTS; ++rt) fr.b[rt] = jf[((r0 / 16 + rt) * SS::NW + ct) * 64 + lane];
+    fr.al = make_float4(1.f, 1.f, 1.f, 1.f);
+  };
+
   // one frame write on the LDS state slice: S <- (S Diag(al) + B) N; a step
   // with live == false leaves S unchanged (padding at the end of the chain);
-  // with logits the decay is sigmoid(al)
-  auto step = [&](const FrameRegs<D>& fr, float* rec, bool live, bool logits) {
+  // with logits the decay is sigmoid(al).  With post, one chunk step
+  // S <- S M_c + J_c instead (fr from load_map).
+  auto step = [&](const FrameRegs<D>& fr, float* rec, bool live, bool logits, bool post) {
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
       const int row = xrow + 16 * q;
@@ -113,8 +157,13 @@ __global__ __launch_bounds__(ScanShape<D>::NT) void scan_kernel(ScanPair p) {
       float4 al = fr.al;
       if (logits) al = make_float4(sigmoid_gate(al.x), sigmoid_gate(al.y), sigmoid_gate(al.z), sigmoid_gate(al.w));
       const f16x4 bb = fr.b[q];
-      const float x[4] = {fmaf(s.x, al.x, (float)bb[0]), fmaf(s.y, al.y, (float)bb[1]),
-                          fmaf(s.z, al.z, (float)bb[2]), fmaf(s.w, al.w, (float)bb[3])};
+      float x[4] = {s.x, s.y, s.z, s.w};
+      if (!post) {
+        x[0] = fmaf(s.x, al.x, (float)bb[0]);
+        x[1] = fmaf(s.y, al.y, (float)bb[1]);
+        x[2] = fmaf(s.z, al.z, (float)bb[2]);
+        x[3] = fmaf(s.w, al.w, (float)bb[3]);
+      }
       f16x4 hi, lo;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -127,7 +176,12 @@ __global__ __launch_bounds__(ScanShape<D>::NT) void scan_kernel(ScanPair p) {
     lds_barrier();
     f32x4 acc[SS::RTS];
 #pragma unroll
-    for (int rt = 0; rt < SS::RTS; ++rt) acc[rt] = f32x4{0, 0, 0, 0};
+    for (int rt = 0; rt < SS::RTS; ++rt) {
+      if (post)
+        acc[rt] = f32x4{(float)fr.b[rt][0], (float)fr.b[rt][1], (float)fr.b[rt][2], (float)fr.b[rt][3]};
+      else
+        acc[rt] = f32x4{0, 0, 0, 0};
+    }
 #pragma unroll
     for (int kk = 0; kk < SS::KS; ++kk) {
       const int k0 = 32 * kk + 8 * lg;
@@ -170,7 +224,7 @@ __global__ __launch_bounds__(ScanShape<D>::NT) void scan_kernel(ScanPair p) {
   if (!a.s_init && a.use_text) {
     FrameRegs<D> fr;
     load(fr, a.n, nullptr);
-    step(fr, nullptr, true, false);  // S^T = (0 + B_T) N_T
+    step(fr, nullptr, true, false, false);  // S^T = (0 + B_T) N_T
   }
   for (int i = tid; i < ROWS * D; i += SS::NT) {
     const float s0 = a.scale * sS[i];
@@ -178,6 +232,27 @@ __global__ __launch_bounds__(ScanShape<D>::NT) void scan_kernel(ScanPair p) {
     states_h[(size_t)r0 * D + i] = s0;
   }
   lds_barrier();
+
+  if constexpr (MODE == kChunkScan) {
+    // ---- C chunk steps S <- S M_c + J_c, maps prefetched PD chunks ahead;
+    // the state is recorded after every chunk
+    const int n = a.C;
+    if (n == 0) return;
+    auto slot_of = [&](int i) { return a.reverse ? n - 1 - i : i; };
+    auto cl = [&](int i) { return i < n ? i : n - 1; };
+    FrameRegs<D> fr[PD + 1];
+#pragma unroll
+    for (int j = 0; j < PD; ++j) load_map(fr[j], slot_of(cl(j)));
+    for (int i0 = 0; i0 < n; i0 += PD + 1) {
+#pragma unroll
+      for (int j = 0; j <= PD; ++j) {
+        const int i = i0 + j;
+        load_map(fr[(j + PD) % (PD + 1)], slot_of(cl(i + PD)));
+        step(fr[j], i < n ? states_h + (size_t)(i + 1) * D * D : nullptr, i < n, false, true);
+      }
+    }
+    return;
+  }
 
   // ---- the chain, operands prefetched PD frames ahead (PD + 1 register sets).
   // Loads past the last frame re-read the last frame, so every step issues
@@ -202,21 +277,251 @@ __global__ __launch_bounds__(ScanShape<D>::NT) void scan_kernel(ScanPair p) {
     for (int j = 0; j <= PD; ++j) {
       const int i = i0 + j;
       load(fr[(j + PD) % (PD + 1)], slot_of(cl(i + PD)), alpha_of(cl(i + PD)));
-      step(fr[j], rec_of(i), i < n, a.prep != 0);
+      step(fr[j], rec_of(i), i < n, a.prep != 0, false);
     }
   }
+}
+
+namespace {
+
+template <int D>
+struct ComposeShape {
+  static constexpr int NTW = D == 128 ? 2 : 1;         // 16-row tiles of Z per wavefront
+  static constexpr int NWV = D / (16 * NTW);            // wavefronts: one workgroup holds a d x d half of Z
+  static constexpr int NTH = 64 * NWV;                  // threads
+  static constexpr int MT = D / 16;                     // 16-column tiles of Z
+  static constexpr int KS = D >= 32 ? D / 32 : 1;       // MFMA k-steps (D = 16: one, zero padded)
+  static constexpr int NCH = 2 * D * D / 16;            // 16-byte chunks of N
+  static constexpr int CPT = (NCH + NTH - 1) / NTH;     // chunks staged per thread
+  static constexpr int TP = D + 8;                      // LDS pitch (halves) of the output tile
+};
+
+}  // namespace
+
+// The chunk maps of every (head, chunk, direction).  One workgroup runs one
+// half of the stacked state of one chain: the d rows of Y (part 0, from I)
+// or of X (part 1, from 0, with B).  The product is taken transposed,
+// Z^T <- N X^T (N is symmetric), so that a lane's accumulators hold four
+// consecutive columns of one row of Z: the next step's X = Z Diag(alpha) + B
+// is then formed in registers and is already the B operand of the next
+// MFMAs, with the k order permuted so that k-slot group g covers columns
+// 32kk + 4g .. +3 and 32kk + 16 + 4g .. +3 (both operands agree on it).  N's
+// fragment order serves that order as two 8-byte LDS reads per operand.  N
+// and alpha of the next frame are fetched during the current frame's MFMAs
+// and staged into the other LDS buffer; one barrier per frame.  X enters the
+// MFMA as an f16 hi/lo pair on the X rows (J_c keeps float32 accuracy) and
+// as f16 on the Y rows (M_c: the product of contractions, whose rounding the
+// f16 store of M_c dominates).
+template <int D>
+struct ComposeLds {
+  _Float16 n[2 * D * D + (D == 16 ? D * 8 : 0)];  // N of two frames; then the output tile
+  float al[2][D];                                  // alpha of two frames
+};
+
+template <int D, bool JPART>
+__device__ __forceinline__ void compose_half(const ScanArgs& a, int h, int cc, ComposeLds<D>& lds) {
+  using CS = ComposeShape<D>;
+  constexpr int MT = CS::MT, NTW = CS::NTW, KS = CS::KS, TP = CS::TP;
+  static_assert(2 * D * D >= D * TP || D == 16, "output tile fits the two N buffers");
+  _Float16* sN = lds.n;
+  float (*sA)[D] = lds.al;
+  constexpr bool jpart = JPART;  // rows of J_c (else of M_c)
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lr = lane & 15, lg = lane >> 4;
+  const int P = a.P;
+  const size_t slot_floats = ws_slot_floats(D);
+  const float* frames = a.frames + (size_t)h * a.n_eff * slot_floats;
+  const float* alpha_h = a.alpha + (size_t)h * a.T * D;
+  auto slot_of = [&](int i) { return P * cc + (a.reverse ? P - 1 - i : i); };
+  const int n0 = 16 * NTW * wave;  // this wavefront's first row of Z (within its half)
+
+  f16x8 nreg[CS::CPT];
+  float areg = 0.f;
+  f16x4 breg[NTW][MT];
+  auto fetch = [&](int i) {
+    const float* base = frames + (size_t)slot_of(i) * slot_floats;
+    const f16x8* src = reinterpret_cast<const f16x8*>(base);
+#pragma unroll
+    for (int j = 0; j < CS::CPT; ++j) {
+      const int c = tid + j * CS::NTH;
+      if (c < CS::NCH) nreg[j] = src[c];
+    }
+    if (tid < D) areg = alpha_h[(size_t)(a.a + slot_of(i)) * D + tid];
+    if (jpart) {
+      const _Float16* bm = reinterpret_cast<const _Float16*>(base + D * D);
+#pragma unroll
+      for (int nt = 0; nt < NTW; ++nt)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+          breg[nt][mt] = *reinterpret_cast<const f16x4*>(bm + (size_t)(n0 + 16 * nt + lr) * D + 16 * mt + 4 * lg);
+    }
+  };
+  auto stage = [&](int buf) {
+    f16x8* dst = reinterpret_cast<f16x8*>(sN + buf * D * D);
+#pragma unroll
+    for (int j = 0; j < CS::CPT; ++j) {
+      const int c = tid + j * CS::NTH;
+      if (c < CS::NCH) dst[c] = nreg[j];
+    }
+    if (tid < D) sA[buf][tid] = a.prep ? sigmoid_gate(areg) : areg;
+  };
+
+  // Z (this half) in accumulators: acc[mt][nt][e] = Z[n0 + 16nt + lr][16mt + 4lg + e]
+  f32x4 acc[MT][NTW];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < NTW; ++nt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[mt][nt][e] = (!jpart && n0 + 16 * nt + lr == 16 * mt + 4 * lg + e) ? 1.f : 0.f;
+
+  fetch(0);
+  stage(0);
+  lds_barrier();
+  for (int i = 0; i < P; ++i) {
+    const int buf = i & 1;
+    // X = Z Diag(alpha) (+ B) as the B operands of the k-steps
+    f16x8 xh[NTW][KS], xl[NTW][KS];
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk)
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const int mt = 2 * kk + half;
+        if (mt < MT) {
+          const float4 al = *reinterpret_cast<const float4*>(&sA[buf][16 * mt + 4 * lg]);
+          const float alv[4] = {al.x, al.y, al.z, al.w};
+#pragma unroll
+          for (int nt = 0; nt < NTW; ++nt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float x = jpart ? fmaf(acc[mt][nt][e], alv[e], (float)breg[nt][mt][e]) : acc[mt][nt][e] * alv[e];
+              const _Float16 hi = (_Float16)x;
+              xh[nt][kk][4 * half + e] = hi;
+              xl[nt][kk][4 * half + e] = (_Float16)(x - (float)hi);
+            }
+        } else {
+#pragma unroll
+          for (int nt = 0; nt < NTW; ++nt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) xh[nt][kk][4 * half + e] = xl[nt][kk][4 * half + e] = (_Float16)0.f;
+        }
+      }
+    if (i + 1 < P) fetch(i + 1);
+    // Z^T <- N X^T
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < NTW; ++nt) acc[mt][nt] = f32x4{0, 0, 0, 0};
+    const _Float16* nb = sN + buf * D * D;
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const int m = 16 * mt + lr;
+        const f16x4 lo4 = *reinterpret_cast<const f16x4*>(nb + ntile_chunk(D, m, 4 * kk + (lg >> 1)) * 8 + 4 * (lg & 1));
+        f16x4 hi4;
+        if (32 * kk + 16 < D) {
+          hi4 = *reinterpret_cast<const f16x4*>(nb + ntile_chunk(D, m, 4 * kk + 2 + (lg >> 1)) * 8 + 4 * (lg & 1));
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) hi4[e] = (_Float16)0.f;
+        }
+        const f16x8 av = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+#pragma unroll
+        for (int nt = 0; nt < NTW; ++nt) {
+          acc[mt][nt] = mfma_f16(av, xh[nt][kk], acc[mt][nt]);
+          if (jpart) acc[mt][nt] = mfma_f16(av, xl[nt][kk], acc[mt][nt]);
+        }
+      }
+    if (i + 1 < P) stage(buf ^ 1);
+    lds_barrier();
+  }
+
+  // ---- store the half through LDS (the N buffers are free now)
+  char* out = static_cast<char*>(a.chunks) + ((size_t)(2 * h + a.reverse) * a.C + cc) * (size_t)(4 * D * D);
+  _Float16* T = sN;
+  if (!jpart) {
+    // M_c: T[m][n] = M_c[n][m], read back as column chunks in the fragment order of N
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < NTW; ++nt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) T[(16 * mt + 4 * lg + e) * TP + n0 + 16 * nt + lr] = (_Float16)acc[mt][nt][e];
+    lds_barrier();
+    constexpr int LG = D >= 32 ? 4 : D / 8;
+    f16x8* mf = reinterpret_cast<f16x8*>(out);
+    for (int q = tid; q < D * D / 8; q += CS::NTH) {
+      const int t = q / (16 * LG);
+      const int c = 4 * (t % KS) + (q / 16) % LG;
+      const int j = 16 * (t / KS) + (q & 15);
+      mf[q] = *reinterpret_cast<const f16x8*>(T + j * TP + 8 * c);
+    }
+  } else {
+    // J_c: T[n][m] = J_c[n][m], read back in the chunk scan's accumulator order
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < NTW; ++nt) {
+        f16x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = (_Float16)acc[mt][nt][e];
+        *reinterpret_cast<f16x4*>(T + (n0 + 16 * nt + lr) * TP + 16 * mt + 4 * lg) = v;
+      }
+    lds_barrier();
+    f16x4* jf = reinterpret_cast<f16x4*>(out + 2 * D * D);
+    for (int q = tid; q < D * D / 4; q += CS::NTH) {
+      const int l = q & 63, t = q >> 6;
+      const int rt = t / MT, ct = t - rt * MT;
+      const int row = 16 * rt + 4 * (l >> 4), col = 16 * ct + (l & 15);
+      f16x4 v;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = T[(row + e) * TP + col];
+      jf[q] = v;
+    }
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(ComposeShape<D>::NTH, 2) void compose_kernel(ScanPair p) {
+  __shared__ __attribute__((aligned(16))) ComposeLds<D> lds;
+  int L = xcd_block(blockIdx.x, gridDim.x);
+  const int per_dir = p.dir[0].H * p.dir[0].C * 2;
+  const int dir = L >= per_dir ? 1 : 0;
+  L -= dir * per_dir;
+  const ScanArgs& a = p.dir[dir];
+  const int chain = L >> 1;
+  const int h = chain / a.C, cc = chain - h * a.C;
+  if (L & 1)
+    compose_half<D, true>(a, h, cc, lds);
+  else
+    compose_half<D, false>(a, h, cc, lds);
 }
 
 int launch_scan(const ScanPair& p, int d, hipStream_t stream) {
   const int H = p.dir[0].H;
   if (H == 0) return 0;
-#define VDA_SCAN(DD)                                                                              \
-  if (d == DD) {                                                                                  \
-    hipLaunchKernelGGL((scan_kernel<DD>), dim3((unsigned)(p.ndir * H * (DD / ScanShape<DD>::ROWS))), \
-                       dim3(ScanShape<DD>::NT), 0, stream, p);                                    \
-    return 0;                                                                                     \
+  if (p.mode == kCompose) {
+    if (p.dir[0].C == 0 || p.dir[0].P == 0) return 0;
+    const long blocks = (long)p.ndir * H * p.dir[0].C * 2;  // two halves of the stacked state per chain
+#define VDA_COMPOSE(DD)                                                                               \
+    if (d == DD) {                                                                                    \
+      hipLaunchKernelGGL((compose_kernel<DD>), dim3((unsigned)blocks), dim3(ComposeShape<DD>::NTH), 0, stream, p); \
+      return 0;                                                                                       \
+    }
+    VDA_COMPOSE(16) VDA_COMPOSE(32) VDA_COMPOSE(64) VDA_COMPOSE(128)
+#undef VDA_COMPOSE
+    return -1;
   }
-  VDA_SCAN(16) VDA_SCAN(32) VDA_SCAN(64) VDA_SCAN(128)
+#define VDA_SCAN(DD, MM)                                                                             \
+  if (d == DD && p.mode == MM) {                                                                     \
+    const long blocks = (long)p.ndir * H * (DD / ScanShape<DD>::ROWS);                               \
+    hipLaunchKernelGGL((scan_kernel<DD, MM>), dim3((unsigned)blocks), dim3(ScanShape<DD>::NT), 0, stream, p); \
+    return 0;                                                                                        \
+  }
+#define VDA_SCAN_D(DD) VDA_SCAN(DD, kFrameScan) VDA_SCAN(DD, kChunkScan)
+  VDA_SCAN_D(16) VDA_SCAN_D(32) VDA_SCAN_D(64) VDA_SCAN_D(128)
+#undef VDA_SCAN_D
 #undef VDA_SCAN
   return -1;
 }

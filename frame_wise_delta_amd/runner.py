@@ -100,6 +100,8 @@ class Path:
     def enqueue(self):
         d, x, b = self.desc, self.dev, self.bufs
         vda.vda_prepare_frames(d, x.k, x.v, x.beta, x.kt, x.vt, x.bt, b.ws, b.ws_bytes, stream=self.main)
+        if d.flags & vda.VDA_CHUNK_SCAN:
+            vda.vda_compose_chunks(d, b.ws, x.alpha, ws_bytes=b.ws_bytes, stream=self.main)
         self.ev_prep.record(self.main)
         self.side.wait_event(self.ev_prep)
         vda.vda_scan_rev(d, b.ws, x.alpha, self.s_init, b.states_r, stream=self.side)

@@ -28,12 +28,13 @@ VDA_ERR_VALUE = -8
 VDA_F32, VDA_BF16, VDA_F16 = 0, 1, 2
 VDA_NO_BRIDGE = 1
 VDA_PREP = 2
+VDA_CHUNK_SCAN = 4
 VDA_DEV_NONFINITE, VDA_DEV_PIVOT = 1, 2
 
 DTYPES = {"f32": VDA_F32, "bf16": VDA_BF16, "f16": VDA_F16}
 
 EXPORTS = ("vda_workspace_bytes", "vda_state_count", "vda_index_map", "vda_prepare_frames",
-           "vda_frame_stats", "vda_factor_frames", "vda_scan_fwd", "vda_scan_rev", "vda_scan_bidir",
+           "vda_frame_stats", "vda_factor_frames", "vda_compose_chunks", "vda_scan_fwd", "vda_scan_rev", "vda_scan_bidir",
            "vda_readout", "vda_readout_gated", "vda_softmax_branch", "vda_forward", "vda_device_status",
            "vda_status_string", "vda_last_error")
 
@@ -76,6 +77,7 @@ def load(path: str | None = None):
         "vda_frame_stats": [D, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                             c_void_p, c_size_t, c_void_p],
         "vda_factor_frames": [D, c_void_p, c_size_t, c_void_p],
+        "vda_compose_chunks": [D, c_void_p, c_size_t, c_void_p, c_void_p],
         "vda_scan_fwd": [D, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p],
         "vda_scan_rev": [D, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p],
         "vda_scan_bidir": [D, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p],
@@ -126,10 +128,12 @@ def _stream(stream):
 
 
 def make_desc(heads, frames, tokens, d, chunk=5, anchors=1, window=1, text_tokens=0,
-              in_dtype="bf16", out_dtype="bf16", text_init_scale=0.5, bridge=True, prep=False) -> vda_desc:
+              in_dtype="bf16", out_dtype="bf16", text_init_scale=0.5, bridge=True, prep=False,
+              chunk_scan=False) -> vda_desc:
     return vda_desc(heads, frames, tokens, d, d, chunk, anchors, window, text_tokens,
                     DTYPES[in_dtype], DTYPES[out_dtype], text_init_scale,
-                    (0 if bridge else VDA_NO_BRIDGE) | (VDA_PREP if prep else 0))
+                    (0 if bridge else VDA_NO_BRIDGE) | (VDA_PREP if prep else 0) |
+                    (VDA_CHUNK_SCAN if chunk_scan else 0))
 
 
 def desc_for(cfg, **over) -> vda_desc:
@@ -185,6 +189,12 @@ def vda_factor_frames(desc, ws, ws_bytes=None, stream=None):
     if ws_bytes is None:
         ws_bytes = ws.numel() * ws.element_size()
     _check(load().vda_factor_frames(ctypes.byref(desc), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def vda_compose_chunks(desc, ws, alpha, ws_bytes=None, stream=None):
+    if ws_bytes is None:
+        ws_bytes = ws.numel() * ws.element_size()
+    _check(load().vda_compose_chunks(ctypes.byref(desc), _ptr(ws), ws_bytes, _ptr(alpha), _stream(stream)))
 
 
 def vda_scan_fwd(desc, ws, alpha, s_init, states, stream=None):

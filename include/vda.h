@@ -69,11 +69,16 @@ enum { VDA_F32 = 0, VDA_BF16 = 1, VDA_F16 = 2 };
 /* vda_desc.flags */
 enum {
   VDA_NO_BRIDGE = 1u << 0, /* readout without the decay bridge (b_f = b_r = 1) */
-  VDA_PREP = 1u << 1       /* inputs are raw projections, prepared inside the kernels
+  VDA_PREP = 1u << 1,      /* inputs are raw projections, prepared inside the kernels
                               [VDN 方法步骤详情 step (2)]: q, k and k_text are
                               L2-normalised per token, x / sqrt(||x||^2 + 1e-6), and
                               beta, beta_text and alpha are logits whose gates are
                               sigmoid(logit) */
+  VDA_CHUNK_SCAN = 1u << 2 /* the scans run at chunk level [VDN 方法步骤详情 step (4)]:
+                              vda_compose_chunks turns each chunk's P frame writes
+                              into one affine map (M_c, J_c) and the scans apply
+                              S <- S M_c + J_c once per chunk; needs window >= 0
+                              and a larger workspace (vda_workspace_bytes) */
 };
 
 /* bits of the device status word */
@@ -98,13 +103,15 @@ typedef struct vda_desc {
   int32_t out_dtype;   /* out: VDA_F32, VDA_BF16 or VDA_F16 */
   float text_init_scale; /* both scans start from text_init_scale * S^T;
                             1/2 reads the page's "initialised by halves" */
-  uint32_t flags;      /* VDA_NO_BRIDGE | VDA_PREP */
+  uint32_t flags;      /* VDA_NO_BRIDGE | VDA_PREP | VDA_CHUNK_SCAN */
 } vda_desc;
 
 /* Bytes of device workspace vda_prepare_frames needs for `desc` (host only,
  * enqueues nothing).  The workspace carries, per head, the factor
  * (I + A_t)^{-1} and B_t of every scanned frame and of the text "frame", plus
- * the device status word, from vda_prepare_frames to the scans. */
+ * the device status word, from vda_prepare_frames to the scans.  With
+ * VDA_CHUNK_SCAN it also holds the chunk maps of both directions
+ * (4 d^2 bytes per head, direction and chunk). */
 int vda_workspace_bytes(const vda_desc* desc, size_t* bytes);
 
 /* Number of states each scan records per head (host only):
@@ -150,13 +157,29 @@ int vda_frame_stats(const vda_desc* desc, const void* k, const void* v, const fl
                     size_t ws_bytes, void* stream);
 int vda_factor_frames(const vda_desc* desc, void* ws, size_t ws_bytes, void* stream);
 
+/* Chunk composition [VDN 方法步骤详情 step (4): chunk-level scan
+ * S_out = S_in M_chunk + J_chunk], for descriptors with VDA_CHUNK_SCAN: with
+ * M_t = Diag(alpha_t) N_t and J_t = B_t N_t (so that the frame write is
+ * S_t = S_{t-1} M_t + J_t), stores for every head and chunk c the forward map
+ * (M_c, J_c) = the composition of the chunk's frame maps in increasing frame
+ * order, and the reverse map, composed in decreasing order.  M_c and J_c are
+ * kept as f16 in `ws`; every chunk is composed independently.
+ *  ws     holds the output of vda_prepare_frames for the same desc;
+ *         ws_bytes >= vda_workspace_bytes(desc)
+ *  alpha  [H][T][d] float32 (logits with VDA_PREP)
+ * Returns VDA_ERR_SHAPE when desc lacks VDA_CHUNK_SCAN. */
+int vda_compose_chunks(const vda_desc* desc, void* ws, size_t ws_bytes, const float* alpha, void* stream);
+
 /* Forward scan [VDN 核心方法 para 1; 方法步骤详情 step (4)]: starting from
  * S_0 = text_init_scale * S_init, applies S_t = (S_{t-1} Diag(alpha_t) + B_t) N_t
  * over the scanned frames in increasing order and records vda_state_count()
  * states per head into `states` [H][count][d][d] float32 (states[h][0] = S_0).
  *  S_init = s_init [H][d][d] float32 when s_init != NULL, else S^T built from
  *  the text tokens in ws (zero when text_tokens == 0).
- *  ws must hold the output of vda_prepare_frames for the same desc. */
+ *  ws must hold the output of vda_prepare_frames for the same desc.
+ * With VDA_CHUNK_SCAN the same states come from C chunk steps
+ * S <- S M_c + J_c; ws must then also hold the output of vda_compose_chunks,
+ * which already applied alpha (the alpha argument is checked but not read). */
 int vda_scan_fwd(const vda_desc* desc, const void* ws, const float* alpha, const float* s_init,
                  float* states, void* stream);
 
@@ -217,7 +240,8 @@ int vda_readout_gated(const vda_desc* desc, const void* q, const float* alpha, c
 int vda_softmax_branch(const vda_desc* desc, const void* q, const void* k, const void* v, const void* k_text,
                        const void* v_text, int32_t v_dtype, float scale, void* out, void* stream);
 
-/* The whole path in one call: vda_prepare_frames, vda_scan_bidir (S_init =
+/* The whole path in one call: vda_prepare_frames, vda_compose_chunks (with
+ * VDA_CHUNK_SCAN only), vda_scan_bidir (S_init =
  * S^T from the text tokens, or zero) and vda_readout, with the same
  * arguments, layouts and results as those calls made in that order on
  * `stream`; everything is enqueued on `stream` alone.  states_rev may be

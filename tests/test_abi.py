@@ -70,13 +70,36 @@ def test_bad_dtypes_and_flags():
         vda.vda_state_count(d)
     assert e.value.code == vda.VDA_ERR_DTYPE
     d = _desc()
-    d.flags = 4
+    d.flags = 8
     with pytest.raises(vda.VdaError) as e:
         vda.vda_state_count(d)
     assert e.value.code == vda.VDA_ERR_SHAPE
-    d = _desc(prep=True, bridge=False)  # both known flags are accepted
-    assert d.flags == vda.VDA_PREP | vda.VDA_NO_BRIDGE
+    d = _desc(prep=True, bridge=False, chunk_scan=True)  # the known flags are accepted
+    assert d.flags == vda.VDA_PREP | vda.VDA_NO_BRIDGE | vda.VDA_CHUNK_SCAN
     vda.vda_state_count(d)
+    with pytest.raises(vda.VdaError) as e:  # chunk-level scans record chunk boundaries only
+        vda.vda_state_count(_desc(chunk_scan=True, window=-1))
+    assert e.value.code == vda.VDA_ERR_SHAPE
+
+
+def test_compose_chunks_validation():
+    lib = vda.load()
+    fake = 1 << 20
+    d = _desc()
+    wsb = vda.vda_workspace_bytes(d)
+    rc = lib.vda_compose_chunks(ctypes.byref(d), fake, wsb, fake, None)
+    assert rc == vda.VDA_ERR_SHAPE  # desc without VDA_CHUNK_SCAN
+    dc = _desc(chunk_scan=True)
+    wsc = vda.vda_workspace_bytes(dc)
+    assert wsc > wsb
+    assert lib.vda_compose_chunks(ctypes.byref(dc), None, wsc, fake, None) == vda.VDA_ERR_NULL
+    assert lib.vda_compose_chunks(ctypes.byref(dc), fake, wsc, None, None) == vda.VDA_ERR_NULL
+    assert lib.vda_compose_chunks(ctypes.byref(dc), fake, wsc - 1, fake, None) == vda.VDA_ERR_WORKSPACE
+    assert lib.vda_compose_chunks(ctypes.byref(dc), fake + 16, wsc, fake, None) == vda.VDA_ERR_ALIGN
+    assert lib.vda_compose_chunks(ctypes.byref(dc), fake, wsc, fake + 4, None) == vda.VDA_ERR_ALIGN
+    # the step calls size the workspace with the chunk maps included
+    rc = lib.vda_prepare_frames(ctypes.byref(dc), fake, fake, fake, fake, fake, fake, fake, wsb, None)
+    assert rc == vda.VDA_ERR_WORKSPACE
 
 
 def test_null_and_workspace_checks_precede_any_device_call():
@@ -157,6 +180,9 @@ def test_valid_call_without_gpu_reports_no_device():
     assert rc == vda.VDA_ERR_DEVICE
     rc = lib.vda_factor_frames(ctypes.byref(d), fake, wsb, None)
     assert rc == vda.VDA_ERR_DEVICE
+    dc = _desc(chunk_scan=True)
+    rc = lib.vda_compose_chunks(ctypes.byref(dc), fake, vda.vda_workspace_bytes(dc), fake, None)
+    assert rc == vda.VDA_ERR_DEVICE
     rc = lib.vda_readout_gated(ctypes.byref(d), fake, fake, fake, fake, fake, fake, 1e-6, fake, None)
     assert rc == vda.VDA_ERR_DEVICE
     rc = lib.vda_softmax_branch(ctypes.byref(_desc(in_dtype="bf16", d=32)), fake, fake, fake, fake, fake, 1, 0.1,
@@ -176,6 +202,10 @@ def test_workspace_and_state_count():
         n = cfg.scanned
         n_eff = n + (1 if cfg.text_tokens else 0)
         assert vda.vda_workspace_bytes(d) == 256 + cfg.heads * n_eff * 2 * cfg.d * cfg.d * 4
+        if cfg.window >= 0:  # chunk maps: 2 directions x C chunks x 4 d^2 bytes per head
+            dc = vda.desc_for(cfg, chunk_scan=True)
+            assert (vda.vda_workspace_bytes(dc) - vda.vda_workspace_bytes(d)
+                    == cfg.heads * 2 * cfg.n_chunks * 4 * cfg.d * cfg.d)
         assert vda.vda_state_count(d) == (cfg.n_chunks + 1 if cfg.window >= 0 else n + 1)
 
 

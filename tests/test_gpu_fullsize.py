@@ -28,12 +28,12 @@ def _oracle(cfg, h_in):
                         f("bt") if text else None)
 
 
-def _run_and_check(cfg, sample_heads):
-    print(f"[fullsize] {cfg.name}: H={cfg.heads} T={cfg.frames} U={cfg.tokens} d={cfg.d}: drawing inputs",
-          flush=True)
+def _run_and_check(cfg, sample_heads, chunk_scan=False):
+    print(f"[fullsize] {cfg.name}: H={cfg.heads} T={cfg.frames} U={cfg.tokens} d={cfg.d} "
+          f"chunk_scan={chunk_scan}: drawing inputs", flush=True)
     heads_in = inp.all_heads(cfg)
     print("[fullsize] running vda_forward", flush=True)
-    desc, dev, bufs = runner.run(cfg, heads_in, fused=True)
+    desc, dev, bufs = runner.run(cfg, heads_in, fused=True, chunk_scan=chunk_scan)
     assert vda.vda_device_status(desc, bufs.ws) == 0
     import torch
     a = cfg.anchors
@@ -70,3 +70,14 @@ def test_long_video_full_shape():
 @pytest.mark.timeout(900)
 def test_high_resolution_full_shape():
     _run_and_check(inp.scaled(inp.CONFIG_BY_NAME["hires"], heads=2), sample_heads=(0,))
+
+
+@pytest.mark.timeout(900)
+def test_h3_full_size_chunk_scan():
+    """The same workload with the scans at chunk level (VDA_CHUNK_SCAN)."""
+    _run_and_check(inp.CONFIG_BY_NAME["h3"], sample_heads=(0, 23), chunk_scan=True)
+
+
+@pytest.mark.timeout(900)
+def test_long_video_chunk_scan():
+    _run_and_check(inp.scaled(inp.CONFIG_BY_NAME["long"], heads=2), sample_heads=(0,), chunk_scan=True)
