@@ -53,6 +53,13 @@ Readings of points the page leaves open:
   so that S_t = S_{t-1} M_t + J_t is the frame write; a chunk's map is the
   composition of its frames' affine maps in scan order (the reverse scan
   composes them last frame first).
+* SANA-WM comparator: the batched additive update takes every token's
+  correction against the same decayed state, with the keys scaled by
+  1/sqrt(U) (U = tokens of the frame; N_text for the text write); in that
+  mode the text state is the same additive write into a zero state.
+* Newton iteration for (I + A)^{-1}: X_{k+1} = X_k (2I - G X_k) from
+  X_0 = c I, c = 2 / (1 + g) with g the largest absolute row sum of G, run
+  until the residual bound ((g-1)/(g+1))^(2^k) is at most a tolerance.
 * Epilogue: RMSNorm over the d_v channels of each token with a per-head
   weight and epsilon, then an elementwise sigmoid gate on per-channel logits
   (which come from the layer input and are given here).
@@ -125,24 +132,72 @@ def frame_update(S_prev: np.ndarray, K: np.ndarray, V: np.ndarray,
     return np.linalg.solve(G, (S_bar + B).T).T
 
 
-def text_state(Kt: np.ndarray, Vt: np.ndarray, bt: np.ndarray, d_v: int, d_k: int) -> np.ndarray:
+def sana_wm_update(S_prev: np.ndarray, K: np.ndarray, V: np.ndarray, beta: np.ndarray,
+                   alpha: np.ndarray, key_scale=None) -> np.ndarray:
+    """The batched additive frame update of SANA-WM, which the page sets
+    against VDA [VDN 核心方法 ¶2; 技术新颖性]: every token's residual is
+    taken against the same decayed state S_bar = S_prev Diag(alpha), with the
+    keys scaled by the frame-size factor key_scale (1/sqrt(U) by default),
+        S = S_bar + sum_u beta_u (v_u - S_bar k'_u) k'_u^T,   k'_u = key_scale k_u,
+    the residuals of all tokens formed first (rows of R), then summed as
+    R^T Diag(beta) K'.  Equal to S_bar (I - A') + B' in the page's notation."""
+    U = K.shape[0]
+    if U == 0:
+        return S_prev * alpha[None, :]
+    c = 1.0 / np.sqrt(U) if key_scale is None else key_scale
+    S_bar = S_prev * alpha[None, :]
+    Kp = c * K
+    R = V - Kp @ S_bar.T            # r_u = v_u - S_bar k'_u, one row per token
+    return S_bar + R.T @ (beta[:, None] * Kp)
+
+
+def text_state(Kt: np.ndarray, Vt: np.ndarray, bt: np.ndarray, d_v: int, d_k: int,
+               update=frame_update) -> np.ndarray:
     """S^T: all text tokens written jointly into a zero state with no decay
-    (reading of [VDN 核心方法 ¶1] "文本状态 S^T")."""
+    (reading of [VDN 核心方法 ¶1] "文本状态 S^T"), with the given frame
+    update rule."""
     if Kt.shape[0] == 0:
         return np.zeros((d_v, d_k))
-    return frame_update(np.zeros((d_v, d_k)), Kt, Vt, bt, np.ones(d_k))
+    return update(np.zeros((d_v, d_k)), Kt, Vt, bt, np.ones(d_k))
+
+
+def ns_iterations(g: float, tol: float) -> int:
+    """Smallest k with r^(2^k) <= tol, r = (g - 1) / (g + 1)."""
+    r = (g - 1.0) / (g + 1.0)
+    k = 0
+    while r ** (2 ** k) > tol:
+        k += 1
+    return k
+
+
+def newton_schulz_inverse(G: np.ndarray, tol: float = 1e-6):
+    """Newton iteration for the inverse of G = I + A, which the page names
+    as a replacement for the exact inverse [VDN 实验结果, the weaknesses
+    discussion]: X_{k+1} = X_k (2I - G X_k) from X_0 = c I.  G is symmetric
+    with eigenvalues in [1, g], g the largest absolute row sum (A is positive
+    semi-definite), so c = 2 / (1 + g) gives ||I - c G||_2 <= r = (g-1)/(g+1)
+    < 1, and the residual I - G X_k is (I - c G)^(2^k).  Runs
+    k = ns_iterations(g, tol) steps; returns (X_k, k)."""
+    d = G.shape[0]
+    g = float(np.abs(G).sum(axis=1).max())
+    k = ns_iterations(g, tol)
+    X = (2.0 / (1.0 + g)) * np.eye(d)
+    for _ in range(k):
+        X = X @ (2.0 * np.eye(d) - G @ X)
+    return X, k
 
 
 # ---------------------------------------------------------------- scans --
 
-def scan(order, K, V, beta, alpha, S0, record_every: int):
-    """Apply ``frame_update`` over the frames in ``order`` starting from S0;
-    return the states after 0, r, 2r, ... frames (r = ``record_every``) and
-    after the last frame.  [VDN 核心方法 ¶1, 方法步骤详情 step (4)]"""
+def scan(order, K, V, beta, alpha, S0, record_every: int, update=frame_update):
+    """Apply ``update`` (the VDA ``frame_update`` unless given) over the
+    frames in ``order`` starting from S0; return the states after 0, r, 2r,
+    ... frames (r = ``record_every``) and after the last frame.
+    [VDN 核心方法 ¶1, 方法步骤详情 step (4)]"""
     S = S0.copy()
     states = [S.copy()]
     for i, t in enumerate(order):
-        S = frame_update(S, K[t], V[t], beta[t], alpha[t])
+        S = update(S, K[t], V[t], beta[t], alpha[t])
         if (i + 1) % record_every == 0 or i + 1 == len(order):
             states.append(S.copy())
     return np.stack(states)
@@ -327,22 +382,24 @@ def rmsnorm_gate(O, weight, gate, eps):
 
 def run_head(frames, chunk, window, anchors, q, k, v, beta, alpha,
              kt=None, vt=None, bt=None, text_init_scale=0.5, bridge=True,
-             with_output=True):
+             with_output=True, update="vda"):
     """Whole linear branch for one head.  Arrays are float64:
     q, k, v [T, U, d]; beta [T, U]; alpha [T, d]; kt, vt [N_text, d]; bt
-    [N_text].  Returns a dict with the maps, S^T, forward/reverse recorded
-    states and the output O [T, U, d_v]."""
+    [N_text].  update = "vda" (the frame write) or "sana" (the SANA-WM
+    comparator, also for the text write).  Returns a dict with the maps,
+    S^T, forward/reverse recorded states and the output O [T, U, d_v]."""
     T, U, d = k.shape
+    upd = {"vda": frame_update, "sana": sana_wm_update}[update]
     rows, frame_chunk = index_maps(frames, chunk, window, anchors)
     order = scanned_frames(frames, anchors)
     if kt is None or len(kt) == 0:
         ST = np.zeros((d, d))
     else:
-        ST = text_state(kt, vt, bt, d, d)
+        ST = text_state(kt, vt, bt, d, d, upd)
     S0 = text_init_scale * ST
     every = chunk if window >= 0 else 1
-    states_f = scan(order, k, v, beta, alpha, S0, every)
-    states_r = scan(order[::-1], k, v, beta, alpha, S0, every)
+    states_f = scan(order, k, v, beta, alpha, S0, every, upd)
+    states_r = scan(order[::-1], k, v, beta, alpha, S0, every, upd)
     out = dict(rows=rows, frame_chunk=frame_chunk, S_text=ST,
                states_f=states_f, states_r=states_r)
     if with_output:

@@ -603,3 +603,113 @@ def test_softmax_branch_dominant_key_and_shift_invariance():
     O1 = orc.softmax_branch(q, k, v, kt, vt, T, 5, 1, 1)
     O2 = orc.softmax_branch(q, k + c, v, kt + c, vt, T, 5, 1, 1)
     np.testing.assert_allclose(O2, O1, rtol=1e-10, atol=1e-12)
+
+
+# ------------------------------------------- variants: SANA-WM and Newton --
+
+def test_sana_wm_single_token_hand_worked():
+    """One token, key scale 1 (U = 1): the explicit token delta rule.
+    S_prev = [[1, 2], [3, 4]], alpha = (1/2, 1), k = (1, 0), v = (1, 1),
+    beta = 1/2: S_bar = [[1/2, 2], [3/2, 4]], S_bar k = (1/2, 3/2), the
+    residual is (1/2, -1/2), so S = [[3/4, 2], [5/4, 4]]."""
+    S = orc.sana_wm_update(np.array([[1.0, 2.0], [3.0, 4.0]]), np.array([[1.0, 0.0]]),
+                           np.array([[1.0, 1.0]]), np.array([0.5]), np.array([0.5, 1.0]))
+    assert np.array_equal(S, np.array([[0.75, 2.0], [1.25, 4.0]]))
+
+
+def test_sana_wm_frame_size_key_scale_hand_worked():
+    """Four copies of one token at the default key scale 1/sqrt(4) = 1/2:
+    k' = (1/2, 0), S_bar = [[1/2, 2], [3/2, 4]] as above, beta = 1/2.  Each
+    residual is v - S_bar k' = (1, 1) - (1/4, 3/4) = (3/4, 1/4); the four
+    corrections sum to 4 * 1/2 * (3/4, 1/4) k'^T, i.e. (3/4, 1/4) in the
+    first column: S = [[5/4, 2], [7/4, 4]]."""
+    K = np.tile([1.0, 0.0], (4, 1))
+    V = np.tile([1.0, 1.0], (4, 1))
+    S = orc.sana_wm_update(np.array([[1.0, 2.0], [3.0, 4.0]]), K, V, np.full(4, 0.5), np.array([0.5, 1.0]))
+    assert np.array_equal(S, np.array([[1.25, 2.0], [1.75, 4.0]]))
+
+
+def test_sana_wm_orthonormal_keys_and_pure_decay():
+    """Orthonormal keys at key scale 1: each key direction moves to
+    (1 - beta_u) S_bar k_u + beta_u v_u independently; beta = 0 is decay."""
+    g = np.random.default_rng(31)
+    d = 6
+    Q, _ = np.linalg.qr(g.standard_normal((d, d)))
+    K = Q.T                                   # rows are orthonormal keys
+    V = g.standard_normal((d, d))
+    beta = g.random(d)
+    alpha = 0.9 + 0.1 * g.random(d)
+    S_prev = g.standard_normal((d, d))
+    S = orc.sana_wm_update(S_prev, K, V, beta, alpha, key_scale=1.0)
+    S_bar = S_prev * alpha[None, :]
+    for u in range(d):
+        expect = (1 - beta[u]) * (S_bar @ K[u]) + beta[u] * V[u]
+        assert np.abs(S @ K[u] - expect).max() <= 1e-13
+    S0 = orc.sana_wm_update(S_prev, K, V, np.zeros(d), alpha)
+    assert np.abs(S0 - S_bar).max() == 0.0
+
+
+def test_sana_wm_expands_where_vda_does_not():
+    """Ten aligned tokens with beta = 1/2 at key scale 1 give
+    lambda_max(A) = 5 > 2: the additive transition I - A maps the key
+    direction to -4 times itself, so the inherited state grows four-fold
+    (核心方法 para 2); the VDA write of the same frame does not expand.
+    With the frame-size scale 1/sqrt(U) and beta < 1 the additive update is
+    non-expansive too."""
+    g = np.random.default_rng(32)
+    d, U = 8, 10
+    k = _unit(g, (d,))
+    K = np.tile(k, (U, 1))
+    V = np.zeros((U, d))
+    beta = np.full(U, 0.5)
+    S_prev = np.outer(g.standard_normal(d), k)  # inherited state along k
+    one = np.ones(d)
+    S_sana = orc.sana_wm_update(S_prev, K, V, beta, one, key_scale=1.0)
+    assert np.linalg.norm(S_sana, 2) == pytest.approx(4.0 * np.linalg.norm(S_prev, 2), rel=1e-12)
+    S_vda = orc.frame_update(S_prev, K, V, beta, one)
+    assert np.linalg.norm(S_vda, 2) <= np.linalg.norm(S_prev, 2)
+    for trial in range(20):
+        S_prev, K, _, beta, alpha = _frame(g, 64, 16)
+        S = orc.sana_wm_update(S_prev, K, np.zeros((64, 16)), beta, alpha)
+        assert np.linalg.norm(S, 2) <= np.linalg.norm(S_prev * alpha[None, :], 2) * (1 + 1e-12)
+
+
+def test_sana_wm_branch_runs_the_additive_rule_everywhere():
+    """run_head(update="sana") applies the additive rule to the text write
+    and to every scanned frame; with beta = 0 on the video both rules give
+    the same (pure decay) states from their own text state."""
+    q, k, v, beta, alpha, kt, vt, bt = _small_cfg_inputs(T=12)
+    r = orc.run_head(12, 5, 1, 1, q, k, v, np.zeros_like(beta), alpha, kt, vt, bt, update="sana")
+    ST = orc.sana_wm_update(np.zeros((8, 8)), kt, vt, bt, np.ones(8))
+    assert np.abs(r["S_text"] - ST).max() == 0.0
+    decay = np.prod(alpha[1:6], axis=0)
+    assert np.abs(r["states_f"][1] - 0.5 * ST * decay[None, :]).max() <= 1e-15
+
+
+def test_newton_schulz_hand_worked():
+    """G = diag(1, 3): g = 3, c = 1/2, r = 1/2; X_1 = diag(3/4, 1/4),
+    X_2 = diag(15/16, 5/16); a tolerance of 0.1 needs k = 2 (r^4 = 1/16)."""
+    X, k = orc.newton_schulz_inverse(np.diag([1.0, 3.0]), tol=0.1)
+    assert k == 2
+    assert np.array_equal(X, np.diag([15 / 16, 5 / 16]))
+
+
+def test_newton_schulz_residual_is_a_power_of_the_start():
+    """From X_0 = c I the residual I - G X_k equals (I - c G)^(2^k), checked
+    through the eigendecomposition of G; it is within the tolerance, and
+    one step fewer would not be."""
+    g = np.random.default_rng(33)
+    for U, d in ((40, 16), (300, 32)):
+        _, K, _, beta, _ = _frame(g, U, d)
+        G = np.eye(d) + K.T @ (beta[:, None] * K)
+        tol = 1e-6
+        X, k = orc.newton_schulz_inverse(G, tol=tol)
+        gmax = np.abs(G).sum(axis=1).max()
+        c = 2 / (1 + gmax)
+        lam, Q = np.linalg.eigh(G)
+        R = (Q * (1 - c * lam) ** (2 ** k)) @ Q.T
+        assert np.abs((np.eye(d) - G @ X) - R).max() <= 1e-12
+        r = (gmax - 1) / (gmax + 1)
+        assert np.linalg.norm(np.eye(d) - G @ X, 2) <= r ** (2 ** k) * (1 + 1e-9) + 1e-12
+        assert r ** (2 ** k) <= tol < r ** (2 ** (k - 1))
+        assert np.abs(X - X.T).max() <= 1e-12
