@@ -13,7 +13,7 @@ a roofline entry for the dominant HBM-bound kernel timed with HIP events on
 the stream it runs on, and the float64 oracle timed on this host's cores.
 
     python bench.py [--steps K] [--warmup W] [--config h3] [--no-cpu-baseline] [--epilogue] [--prep]
-                    [--chunk-scan]
+                    [--chunk-scan] [--sana-wm]
     python bench.py --softmax [--steps K] [--warmup W]
 
 --epilogue replaces the readout by vda_readout_gated (the readout followed by
@@ -23,6 +23,8 @@ beta and alpha as logits) and sets VDA_PREP, so the kernels normalise and
 gate them.  Both measure next steps of the path; neither is the default line.
 --chunk-scan sets VDA_CHUNK_SCAN: vda_compose_chunks after the factorisation,
 then the scans at chunk level (S <- S M_c + J_c once per chunk).
+--sana-wm sets VDA_SANA_WM: the SANA-WM batched additive update as a
+comparator (the "factor" call then forms -A/U and B/sqrt(U)).
 --softmax times the softmax window + anchor + text branch (vda_softmax_branch)
 on the same workload instead: an MFMA-bound kernel, reported against the
 bf16 MFMA peak.
@@ -196,10 +198,11 @@ def write_traffic(fetch_csv, write_csv, cal_fetch_csv, cal_write_csv):
 
 # ---------------------------------------------------------------- bench --
 
-def cpu_baseline(cfg, heads_in, out0, budget_s=15.0, epi_in=None, prep=False):
+def cpu_baseline(cfg, heads_in, out0, budget_s=15.0, epi_in=None, prep=False, update="vda"):
     """The float64 oracle, as it stands, on whole heads of the same workload
     until about budget_s seconds of CPU time are spent (at least one head);
-    with epi_in, followed by the oracle's readout epilogue."""
+    with epi_in, followed by the oracle's readout epilogue; update selects
+    the frame update rule ("sana": the SANA-WM comparator)."""
     from oracle import vda_oracle as orc
     try:
         from threadpoolctl import threadpool_info
@@ -217,7 +220,7 @@ def cpu_baseline(cfg, heads_in, out0, budget_s=15.0, epi_in=None, prep=False):
             q, k, v, b, a, kt, vt, bt = args
             q, k, b, a, kt, bt = orc.prep(q, k, b, a, kt, bt, eps=1e-6)
             args = [q, k, v, b, a, kt, vt, bt]
-        ref = orc.run_head(cfg.frames, cfg.chunk, cfg.window, cfg.anchors, *args)
+        ref = orc.run_head(cfg.frames, cfg.chunk, cfg.window, cfg.anchors, *args, update=update)
         if epi_in is not None:
             ref["O"] = orc.rmsnorm_gate(ref["O"], epi_in[h].f64("weight"), epi_in[h].f64("gate"), EPS)
         t_cpu += time.perf_counter() - c0
@@ -232,6 +235,7 @@ def cpu_baseline(cfg, heads_in, out0, budget_s=15.0, epi_in=None, prep=False):
              "kind": "oracle",
              "sample": f"{done} of {cfg.heads} heads of the same workload (all {cfg.frames} frames of each), "
                        f"float64 NumPy/LAPACK{' with the prep' if prep else ''}"
+                       f"{' with the SANA-WM update' if update == 'sana' else ''}"
                        f"{' with the readout epilogue' if epi_in is not None else ''}, "
                        f"{t_cpu:.1f} s; frames/s scaled by the fraction of heads"},
             rel)
@@ -325,6 +329,8 @@ def main():
                     help="raw inputs prepared inside the kernels (VDA_PREP: L2 normalisation, sigmoid gates)")
     ap.add_argument("--chunk-scan", action="store_true",
                     help="scans at chunk level from composed chunk maps (VDA_CHUNK_SCAN)")
+    ap.add_argument("--sana-wm", action="store_true",
+                    help="the SANA-WM batched additive update in place of the VDA write (VDA_SANA_WM)")
     ap.add_argument("--softmax", action="store_true",
                     help="time the softmax window + anchor + text branch instead of the linear branch")
     ap.add_argument("--copy-calibration", action="store_true")
@@ -353,7 +359,7 @@ def main():
     t0 = time.time()
     heads_in = inp.all_raw_heads(cfg) if args.prep else inp.all_heads(cfg)
     print(f"[bench] inputs for {cfg.name} drawn in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
-    desc = vda.desc_for(cfg, prep=args.prep, chunk_scan=args.chunk_scan)
+    desc = vda.desc_for(cfg, prep=args.prep, chunk_scan=args.chunk_scan, sana_wm=args.sana_wm)
     dev = runner.upload(cfg, heads_in, "cuda")
     bufs = runner.allocate(desc, cfg.out_dtype, "cuda")
     epi_in, gate, norm_w = None, None, None
@@ -427,7 +433,8 @@ def main():
     cpu, rel = None, None
     if not args.no_cpu_baseline:
         out0 = bufs.out[0].float().cpu().numpy().astype(np.float64)
-        cpu, rel = cpu_baseline(cfg, heads_in, out0, args.cpu_seconds, epi_in, args.prep)
+        cpu, rel = cpu_baseline(cfg, heads_in, out0, args.cpu_seconds, epi_in, args.prep,
+                                "sana" if args.sana_wm else "vda")
 
     out = {
         "metric": "VDA scan+readout latent frames/s and % of MI355X bf16 MFMA peak",
@@ -447,8 +454,10 @@ def main():
                                f"chunk), U={cfg.tokens}, {cfg.text_tokens} text tokens"
                                + (", readout epilogue (RMSNorm + sigmoid gate)" if args.epilogue else "")
                                + (", raw inputs prepared in the kernels" if args.prep else "")
-                               + (", chunk-level scans from composed chunk maps" if args.chunk_scan else ""),
+                               + (", chunk-level scans from composed chunk maps" if args.chunk_scan else "")
+                               + (", SANA-WM batched additive update (comparator)" if args.sana_wm else ""),
                    "epilogue": bool(args.epilogue), "prep": bool(args.prep), "chunk_scan": bool(args.chunk_scan),
+                   "sana_wm": bool(args.sana_wm),
                    "heads": cfg.heads, "d": cfg.d, "frames": cfg.frames, "tokens": cfg.tokens,
                    "text_tokens": cfg.text_tokens, "in_dtype": cfg.in_dtype, "out_dtype": cfg.out_dtype,
                    "state_dtype": "f32", "global_batch": 1, "seq_len": cfg.frames * cfg.tokens,

@@ -32,6 +32,7 @@ int ok() {
 struct Shape {
   int H, T, U, d, P, a, n, C, w, Nt, n_eff, count;
   bool chunked;  // VDA_CHUNK_SCAN
+  bool sana;     // VDA_SANA_WM
 };
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -56,8 +57,10 @@ int check_desc(const vda_desc* desc, Shape* s) {
   if (q.out_dtype != VDA_F32 && q.out_dtype != VDA_BF16 && q.out_dtype != VDA_F16)
     return fail(VDA_ERR_DTYPE, "out_dtype = %d (VDA_F32, VDA_BF16 or VDA_F16)", q.out_dtype);
   if (!(q.text_init_scale == q.text_init_scale)) return fail(VDA_ERR_SHAPE, "text_init_scale is NaN");
-  if (q.flags & ~(uint32_t)(VDA_NO_BRIDGE | VDA_PREP | VDA_CHUNK_SCAN))
+  if (q.flags & ~(uint32_t)(VDA_NO_BRIDGE | VDA_PREP | VDA_CHUNK_SCAN | VDA_SANA_WM))
     return fail(VDA_ERR_SHAPE, "unknown flags 0x%x", q.flags);
+  if ((q.flags & VDA_SANA_WM) && (q.flags & VDA_CHUNK_SCAN))
+    return fail(VDA_ERR_SHAPE, "VDA_SANA_WM and VDA_CHUNK_SCAN cannot be combined");
   if ((q.flags & VDA_CHUNK_SCAN) && q.window < 0)
     return fail(VDA_ERR_SHAPE, "VDA_CHUNK_SCAN needs window >= 0 (states at chunk boundaries)");
   s->H = q.heads;
@@ -75,6 +78,7 @@ int check_desc(const vda_desc* desc, Shape* s) {
     return fail(VDA_ERR_SHAPE, "windowed readout needs n %% chunk == 0 (n = %d, chunk = %d)", s->n, s->P);
   s->count = (s->w >= 0 ? s->C : s->n) + 1;
   s->chunked = (q.flags & VDA_CHUNK_SCAN) != 0;
+  s->sana = (q.flags & VDA_SANA_WM) != 0;
   // 64-bit sizes must not overflow and grids must fit
   const double elems = (double)s->H * s->T * (double)s->U * s->d;
   if (elems > 9.0e15) return fail(VDA_ERR_SHAPE, "tensor too large");
@@ -254,7 +258,15 @@ int scan_args(const vda_desc* desc, const void* ws, const float* alpha, const fl
   return VDA_OK;
 }
 
-int scan_mode(const Shape& s) { return s.chunked ? vda::kChunkScan : vda::kFrameScan; }
+int scan_mode(const Shape& s) { return s.sana ? vda::kSanaScan : s.chunked ? vda::kChunkScan : vda::kFrameScan; }
+
+// the factorisation, or the SANA-WM comparator's transition in its place
+void launch_factor(const Shape& s, const vda::PrepArgs& a, hipStream_t st) {
+  if (s.sana)
+    vda::launch_sana(a, s.d, st);
+  else
+    vda::launch_gj(a, s.d, st);
+}
 
 int read_args(const vda_desc* desc, const void* q, const float* alpha, const float* states_fwd,
               const float* states_rev, void* out, Shape& s, vda::ReadArgs& a, bool& any) {
@@ -307,7 +319,7 @@ int vda_prepare_frames(const vda_desc* desc, const void* k, const void* v, const
   hipStream_t st = static_cast<hipStream_t>(stream);
   vda::launch_clear_status(a.status, st);
   vda::launch_stats(a, s.d, desc->in_dtype == VDA_F32, st);
-  vda::launch_gj(a, s.d, st);
+  launch_factor(s, a, st);
   return launch_status();
 }
 
@@ -346,7 +358,7 @@ int vda_factor_frames(const vda_desc* desc, void* ws, size_t ws_size, void* stre
   a.Nt = s.Nt;
   a.s0 = 0;
   a.cnt = s.n_eff;
-  vda::launch_gj(a, s.d, static_cast<hipStream_t>(stream));
+  launch_factor(s, a, static_cast<hipStream_t>(stream));
   return launch_status();
 }
 
@@ -508,7 +520,7 @@ int vda_forward(const vda_desc* desc, const void* q, const void* k, const void* 
   const bool f32 = desc->in_dtype == VDA_F32;
   vda::launch_clear_status(pa.status, st);
   vda::launch_stats(pa, s.d, f32, st);
-  vda::launch_gj(pa, s.d, st);
+  launch_factor(s, pa, st);
   if (s.chunked) {
     vda::ScanPair cp = sp;  // both directions' chunk maps in one launch
     cp.dir[1] = sp.dir[0];

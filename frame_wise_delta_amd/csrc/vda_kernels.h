@@ -42,6 +42,7 @@ enum ScanMode {
   kFrameScan = 0,  // S_t = (S_{t-1} Diag(alpha_t) + B_t) N_t over the frames
   kCompose = 1,    // the chunk maps (M_c, J_c) of every chunk, in parallel
   kChunkScan = 2,  // S_c = S_{c-1} M_c + J_c over the chunks
+  kSanaScan = 3,   // S_t = X + X (-A_t/U) + B'_t, X = S_{t-1} Diag(alpha_t) (the SANA-WM comparator)
 };
 
 // One or two scans in one launch: blocks [0, H RB) run dir[0], the next
@@ -83,6 +84,8 @@ struct AttnArgs {
 
 int launch_stats(const PrepArgs& a, int d, bool in_f32, hipStream_t stream);
 int launch_gj(const PrepArgs& a, int d, hipStream_t stream);
+// SANA-WM comparator: -A/U and B' = B/sqrt(U) in place of N and B.
+int launch_sana(const PrepArgs& a, int d, hipStream_t stream);
 void launch_clear_status(int* status, hipStream_t stream);
 int launch_scan(const ScanPair& p, int d, hipStream_t stream);
 int launch_readout(const ReadArgs& a, int d, int in_dtype, int out_dtype, hipStream_t stream);

@@ -515,6 +515,92 @@ __global__ __launch_bounds__(64, 2) void gj_kernel(PrepArgs args) {
   if (bad) atomicOr(args.status, bad);
 }
 
+// The SANA-WM comparator's transition in place of the factorisation: the
+// batched additive update ("Video DeltaNet: A Video-Native Hybrid Attention
+// for Livestream Video Generation", core-method section, paragraph 2) is
+// S_t = S_bar_t (I - A'_t) + B'_t with the keys scaled by 1/sqrt(U), i.e.
+// A' = A / U and B' = B / sqrt(U) (U = tokens of the slot: the frame's, or
+// the text tokens).  One workgroup per slot: A's upper-triangle tiles are
+// staged into LDS as the full symmetric matrix, -A / U is written over them
+// as f16 in the fragment order of N (the scan adds the identity part
+// itself: f16 holds -A/U to 2^-12 of its own size, while next to 1 its
+// spacing would be a large part of A/U), then B is staged and rewritten in
+// place as B' (f16) in the scan's accumulator order: the f16x4 at index
+// (R * d/16 + ct) * 64 + l holds B'[16R + 4(l/16) + e][16ct + l%16].
+template <int D>
+__global__ __launch_bounds__(kThreads) void sana_kernel(PrepArgs args) {
+  constexpr int RT = D / 16;
+  constexpr int AP = D + 4;  // LDS pitch (floats) of A
+  constexpr int BP = D + 8;  // LDS pitch (halves) of B
+  constexpr int KS = D >= 32 ? D / 32 : 1;
+  constexpr int LG = D >= 32 ? 4 : D / 8;
+  __shared__ __attribute__((aligned(16))) float sA[D * AP];
+
+  const int tid = threadIdx.x;
+  const int h = blockIdx.x / args.cnt;
+  const int f = args.s0 + (blockIdx.x - h * args.cnt);
+  float* slot = args.frames + ((size_t)h * args.n_eff + f) * ws_slot_floats(D);
+  const int U = f < args.n ? args.U : args.Nt;
+  const float inv_u = U > 0 ? 1.f / (float)U : 0.f;
+  const float inv_su = U > 0 ? 1.f / sqrtf((float)U) : 0.f;
+  int bad = 0;
+
+  // ---- A: tile (ri, cj), cj >= ri, lane l holds A[16ri + 4(l/16) + e][16cj + l%16]
+  for (int i = tid; i < RT * RT * 64; i += kThreads) {
+    const int l = i & 63, t = i >> 6;
+    const int ri = t / RT, cj = t - ri * RT;
+    if (cj < ri) continue;
+    const f32x4 v = *reinterpret_cast<const f32x4*>(slot + (size_t)i * 4);
+    const int c = 16 * cj + (l & 15);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = 16 * ri + 4 * (l >> 4) + e;
+      sA[r * AP + c] = v[e];
+      if (cj != ri) sA[c * AP + r] = v[e];
+    }
+  }
+  __syncthreads();
+  // ---- -A / U in fragment order (chunk q holds row j, columns 8c .. 8c+7)
+  f16x8* tf = reinterpret_cast<f16x8*>(slot);
+  for (int q = tid; q < D * D / 8; q += kThreads) {
+    const int t = q / (16 * LG);
+    const int c = 4 * (t % KS) + (q / 16) % LG;
+    const int j = 16 * (t / KS) + (q & 15);
+    f16x8 o;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float x = -inv_u * sA[j * AP + 8 * c + e];
+      if (!__builtin_isfinite(x)) bad |= VDA_DEV_NONFINITE;
+      o[e] = (_Float16)x;
+    }
+    tf[q] = o;
+  }
+  __syncthreads();
+  // ---- B (row-major f16 at byte 4 d^2) -> B' = B / sqrt(U) in accumulator order, in place
+  _Float16* sB = reinterpret_cast<_Float16*>(sA);
+  f16x8* bm = reinterpret_cast<f16x8*>(slot + D * D);
+  for (int i = tid; i < D * D / 8; i += kThreads) {
+    const int r = i / (D / 8), c8 = i - r * (D / 8);
+    *reinterpret_cast<f16x8*>(sB + r * BP + 8 * c8) = bm[i];
+  }
+  __syncthreads();
+  f16x4* bo = reinterpret_cast<f16x4*>(slot + D * D);
+  for (int q = tid; q < D * D / 4; q += kThreads) {
+    const int l = q & 63, t = q >> 6;
+    const int rt = t / RT, ct = t - rt * RT;
+    const int row = 16 * rt + 4 * (l >> 4), col = 16 * ct + (l & 15);
+    f16x4 o;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float x = inv_su * (float)sB[(row + e) * BP + col];
+      if (!__builtin_isfinite(x)) bad |= VDA_DEV_NONFINITE;
+      o[e] = (_Float16)x;
+    }
+    bo[q] = o;
+  }
+  if (bad) atomicOr(args.status, bad);
+}
+
 __global__ void clear_status_kernel(int* status) { *status = 0; }
 
 int launch_stats(const PrepArgs& a, int d, bool in_f32, hipStream_t stream) {
@@ -547,6 +633,19 @@ int launch_gj(const PrepArgs& a, int d, hipStream_t stream) {
   }
   VDA_GJ(16) VDA_GJ(32) VDA_GJ(64) VDA_GJ(128)
 #undef VDA_GJ
+  return -1;
+}
+
+int launch_sana(const PrepArgs& a, int d, hipStream_t stream) {
+  if (a.H == 0 || a.cnt == 0) return 0;
+  dim3 grid((unsigned)(a.H * a.cnt)), block(kThreads);
+#define VDA_SANA(DD)                                                                  \
+  if (d == DD) {                                                                      \
+    hipLaunchKernelGGL((sana_kernel<DD>), grid, block, 0, stream, a);                 \
+    return 0;                                                                         \
+  }
+  VDA_SANA(16) VDA_SANA(32) VDA_SANA(64) VDA_SANA(128)
+#undef VDA_SANA
   return -1;
 }
 

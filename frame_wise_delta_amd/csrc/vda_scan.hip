@@ -72,7 +72,11 @@ struct FrameRegs {
 
 template <int D, int MODE>
 __global__ __launch_bounds__(ScanShape<D>::NT) void scan_kernel(ScanPair p) {
-  static_assert(MODE == kFrameScan || MODE == kChunkScan, "compose runs in compose_kernel");
+  static_assert(MODE == kFrameScan || MODE == kChunkScan || MODE == kSanaScan, "compose runs in compose_kernel");
+  // SANA-WM frame slots hold -A/U as the operand and B' in accumulator order,
+  // added after the product together with X; the chunk maps' J_c is added
+  // after the product in any case
+  constexpr bool POST = MODE == kSanaScan;
   using SS = ScanShape<D>;
   constexpr int ROWS = SS::ROWS, NQ = SS::NQ, PD = SS::PD;
   static_assert(NQ == SS::RTS, "one B / J register per 16-row tile");
@@ -107,6 +111,7 @@ __global__ __launch_bounds__(ScanShape<D>::NT) void scan_kernel(ScanPair p) {
     const float* base = frames + (size_t)slot * slot_floats;
     const _Float16* nf = reinterpret_cast<const _Float16*>(base);
     const _Float16* bm = reinterpret_cast<const _Float16*>(base + D * D);
+    const f16x4* ba = reinterpret_cast<const f16x4*>(base + D * D);  // SANA-WM: B' in accumulator order
     // fragment order: one wavefront reads 64 consecutive 16-byte chunks
 #pragma unroll
     for (int kk = 0; kk < SS::KS; ++kk) {
@@ -119,8 +124,12 @@ __global__ __launch_bounds__(ScanShape<D>::NT) void scan_kernel(ScanPair p) {
       }
     }
 #pragma unroll
-    for (int q = 0; q < NQ; ++q)
-      fr.b[q] = *reinterpret_cast<const f16x4*>(bm + (size_t)(r0 + xrow + 16 * q) * D + xc0);
+    for (int q = 0; q < NQ; ++q) {
+      if constexpr (MODE == kSanaScan)
+        fr.b[q] = ba[((r0 / 16 + q) * SS::NW + ct) * 64 + lane];
+      else
+        fr.b[q] = *reinterpret_cast<const f16x4*>(bm + (size_t)(r0 + xrow + 16 * q) * D + xc0);
+    }
     fr.al = alpha_row ? *reinterpret_cast<const float4*>(alpha_row + xc0) : make_float4(1.f, 1.f, 1.f, 1.f);
   };
 
@@ -147,8 +156,9 @@ __global__ __launch_bounds__(ScanShape<D>::NT) void scan_kernel(ScanPair p) {
 
   // one frame write on the LDS state slice: S <- (S Diag(al) + B) N; a step
   // with live == false leaves S unchanged (padding at the end of the chain);
-  // with logits the decay is sigmoid(al).  With post, one chunk step
-  // S <- S M_c + J_c instead (fr from load_map).
+  // with logits the decay is sigmoid(al).  With post, B is added after the
+  // product, S <- S Diag(al) N + B, B in accumulator order: one chunk step
+  // S M_c + J_c (al = 1, fr from load_map) or one SANA-WM frame write.
   auto step = [&](const FrameRegs<D>& fr, float* rec, bool live, bool logits, bool post) {
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
@@ -157,7 +167,7 @@ __global__ __launch_bounds__(ScanShape<D>::NT) void scan_kernel(ScanPair p) {
       float4 al = fr.al;
       if (logits) al = make_float4(sigmoid_gate(al.x), sigmoid_gate(al.y), sigmoid_gate(al.z), sigmoid_gate(al.w));
       const f16x4 bb = fr.b[q];
-      float x[4] = {s.x, s.y, s.z, s.w};
+      float x[4] = {s.x * al.x, s.y * al.y, s.z * al.z, s.w * al.w};
       if (!post) {
         x[0] = fmaf(s.x, al.x, (float)bb[0]);
         x[1] = fmaf(s.y, al.y, (float)bb[1]);
@@ -177,10 +187,18 @@ __global__ __launch_bounds__(ScanShape<D>::NT) void scan_kernel(ScanPair p) {
     f32x4 acc[SS::RTS];
 #pragma unroll
     for (int rt = 0; rt < SS::RTS; ++rt) {
-      if (post)
+      if (post) {
         acc[rt] = f32x4{(float)fr.b[rt][0], (float)fr.b[rt][1], (float)fr.b[rt][2], (float)fr.b[rt][3]};
-      else
+        if constexpr (MODE == kSanaScan) {  // the identity part: X (I - A') = X + X (-A')
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int at = (16 * rt + 4 * lg + e) * SS::XP + 16 * ct + lr;
+            acc[rt][e] += (float)sXh[at] + (float)sXl[at];
+          }
+        }
+      } else {
         acc[rt] = f32x4{0, 0, 0, 0};
+      }
     }
 #pragma unroll
     for (int kk = 0; kk < SS::KS; ++kk) {
@@ -224,7 +242,7 @@ __global__ __launch_bounds__(ScanShape<D>::NT) void scan_kernel(ScanPair p) {
   if (!a.s_init && a.use_text) {
     FrameRegs<D> fr;
     load(fr, a.n, nullptr);
-    step(fr, nullptr, true, false, false);  // S^T = (0 + B_T) N_T
+    step(fr, nullptr, true, false, POST);  // S^T = (0 + B_T) N_T, SANA-WM: 0 T_T + B'_T
   }
   for (int i = tid; i < ROWS * D; i += SS::NT) {
     const float s0 = a.scale * sS[i];
@@ -277,7 +295,7 @@ __global__ __launch_bounds__(ScanShape<D>::NT) void scan_kernel(ScanPair p) {
     for (int j = 0; j <= PD; ++j) {
       const int i = i0 + j;
       load(fr[(j + PD) % (PD + 1)], slot_of(cl(i + PD)), alpha_of(cl(i + PD)));
-      step(fr[j], rec_of(i), i < n, a.prep != 0, false);
+      step(fr[j], rec_of(i), i < n, a.prep != 0, POST);
     }
   }
 }
@@ -519,7 +537,7 @@ int launch_scan(const ScanPair& p, int d, hipStream_t stream) {
     hipLaunchKernelGGL((scan_kernel<DD, MM>), dim3((unsigned)blocks), dim3(ScanShape<DD>::NT), 0, stream, p); \
     return 0;                                                                                        \
   }
-#define VDA_SCAN_D(DD) VDA_SCAN(DD, kFrameScan) VDA_SCAN(DD, kChunkScan)
+#define VDA_SCAN_D(DD) VDA_SCAN(DD, kFrameScan) VDA_SCAN(DD, kChunkScan) VDA_SCAN(DD, kSanaScan)
   VDA_SCAN_D(16) VDA_SCAN_D(32) VDA_SCAN_D(64) VDA_SCAN_D(128)
 #undef VDA_SCAN_D
 #undef VDA_SCAN

@@ -74,11 +74,19 @@ enum {
                               L2-normalised per token, x / sqrt(||x||^2 + 1e-6), and
                               beta, beta_text and alpha are logits whose gates are
                               sigmoid(logit) */
-  VDA_CHUNK_SCAN = 1u << 2 /* the scans run at chunk level [VDN 方法步骤详情 step (4)]:
+  VDA_CHUNK_SCAN = 1u << 2, /* the scans run at chunk level [VDN 方法步骤详情 step (4)]:
                               vda_compose_chunks turns each chunk's P frame writes
                               into one affine map (M_c, J_c) and the scans apply
                               S <- S M_c + J_c once per chunk; needs window >= 0
                               and a larger workspace (vda_workspace_bytes) */
+  VDA_SANA_WM = 1u << 3    /* comparator: the SANA-WM batched additive update
+                              [VDN 核心方法 para 2] in place of the VDA write,
+                              S_t = S_{t-1} Diag(alpha_t) (I - A_t/U) + B_t/sqrt(U)
+                              (keys scaled by 1/sqrt(U), U the tokens of the frame;
+                              N_text for the text write, so S^T = B_T/sqrt(N_text));
+                              vda_factor_frames then forms -A_t/U and B_t/sqrt(U)
+                              in place of (I + A_t)^{-1} and B_t; not with
+                              VDA_CHUNK_SCAN */
 };
 
 /* bits of the device status word */
@@ -103,7 +111,7 @@ typedef struct vda_desc {
   int32_t out_dtype;   /* out: VDA_F32, VDA_BF16 or VDA_F16 */
   float text_init_scale; /* both scans start from text_init_scale * S^T;
                             1/2 reads the page's "initialised by halves" */
-  uint32_t flags;      /* VDA_NO_BRIDGE | VDA_PREP | VDA_CHUNK_SCAN */
+  uint32_t flags;      /* VDA_NO_BRIDGE | VDA_PREP | VDA_CHUNK_SCAN | VDA_SANA_WM */
 } vda_desc;
 
 /* Bytes of device workspace vda_prepare_frames needs for `desc` (host only,

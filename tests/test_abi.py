@@ -70,7 +70,7 @@ def test_bad_dtypes_and_flags():
         vda.vda_state_count(d)
     assert e.value.code == vda.VDA_ERR_DTYPE
     d = _desc()
-    d.flags = 8
+    d.flags = 16
     with pytest.raises(vda.VdaError) as e:
         vda.vda_state_count(d)
     assert e.value.code == vda.VDA_ERR_SHAPE
@@ -79,6 +79,12 @@ def test_bad_dtypes_and_flags():
     vda.vda_state_count(d)
     with pytest.raises(vda.VdaError) as e:  # chunk-level scans record chunk boundaries only
         vda.vda_state_count(_desc(chunk_scan=True, window=-1))
+    assert e.value.code == vda.VDA_ERR_SHAPE
+    d = _desc(sana_wm=True, prep=True)  # the SANA-WM comparator, also on raw inputs
+    assert d.flags == vda.VDA_SANA_WM | vda.VDA_PREP
+    assert vda.vda_workspace_bytes(d) == vda.vda_workspace_bytes(_desc())
+    with pytest.raises(vda.VdaError) as e:  # its frame map has no chunk composition
+        vda.vda_state_count(_desc(sana_wm=True, chunk_scan=True))
     assert e.value.code == vda.VDA_ERR_SHAPE
 
 
