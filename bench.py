@@ -13,7 +13,7 @@ a roofline entry for the dominant HBM-bound kernel timed with HIP events on
 the stream it runs on, and the float64 oracle timed on this host's cores.
 
     python bench.py [--steps K] [--warmup W] [--config h3] [--no-cpu-baseline] [--epilogue] [--prep]
-                    [--chunk-scan] [--sana-wm]
+                    [--chunk-scan] [--sana-wm] [--newton]
     python bench.py --softmax [--steps K] [--warmup W]
 
 --epilogue replaces the readout by vda_readout_gated (the readout followed by
@@ -25,6 +25,8 @@ gate them.  Both measure next steps of the path; neither is the default line.
 then the scans at chunk level (S <- S M_c + J_c once per chunk).
 --sana-wm sets VDA_SANA_WM: the SANA-WM batched additive update as a
 comparator (the "factor" call then forms -A/U and B/sqrt(U)).
+--newton sets VDA_NEWTON: (I + A)^-1 by Newton iteration in the "factor"
+call instead of Gauss-Jordan.
 --softmax times the softmax window + anchor + text branch (vda_softmax_branch)
 on the same workload instead: an MFMA-bound kernel, reported against the
 bf16 MFMA peak.
@@ -57,7 +59,8 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16/f16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 COPY_BYTES = 512 * 1024 * 1024
-KERNELS = ("stats_kernel", "gj_kernel", "scan_kernel", "compose_kernel", "readout_kernel", "readout_gated")
+KERNELS = ("stats_kernel", "gj_kernel", "ns_kernel", "sana_kernel", "scan_kernel", "compose_kernel",
+           "readout_kernel", "readout_gated")
 EPS = 1e-6  # RMSNorm epsilon of the epilogue
 
 
@@ -96,6 +99,7 @@ def kernel_bytes(cfg):
 
 
 KERNEL_SRC = {"stats_kernel": "vda_prepare.hip", "gj_kernel": "vda_prepare.hip",
+              "ns_kernel": "vda_prepare.hip", "sana_kernel": "vda_prepare.hip",
               "scan_kernel": "vda_scan.hip", "compose_kernel": "vda_scan.hip", "readout_kernel": "vda_readout.hip",
               "readout_gated": "vda_readout.hip"}
 
@@ -331,6 +335,8 @@ def main():
                     help="scans at chunk level from composed chunk maps (VDA_CHUNK_SCAN)")
     ap.add_argument("--sana-wm", action="store_true",
                     help="the SANA-WM batched additive update in place of the VDA write (VDA_SANA_WM)")
+    ap.add_argument("--newton", action="store_true",
+                    help="(I + A)^-1 by Newton iteration instead of Gauss-Jordan (VDA_NEWTON)")
     ap.add_argument("--softmax", action="store_true",
                     help="time the softmax window + anchor + text branch instead of the linear branch")
     ap.add_argument("--copy-calibration", action="store_true")
@@ -359,7 +365,8 @@ def main():
     t0 = time.time()
     heads_in = inp.all_raw_heads(cfg) if args.prep else inp.all_heads(cfg)
     print(f"[bench] inputs for {cfg.name} drawn in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
-    desc = vda.desc_for(cfg, prep=args.prep, chunk_scan=args.chunk_scan, sana_wm=args.sana_wm)
+    desc = vda.desc_for(cfg, prep=args.prep, chunk_scan=args.chunk_scan, sana_wm=args.sana_wm,
+                        newton=args.newton)
     dev = runner.upload(cfg, heads_in, "cuda")
     bufs = runner.allocate(desc, cfg.out_dtype, "cuda")
     epi_in, gate, norm_w = None, None, None
@@ -455,9 +462,10 @@ def main():
                                + (", readout epilogue (RMSNorm + sigmoid gate)" if args.epilogue else "")
                                + (", raw inputs prepared in the kernels" if args.prep else "")
                                + (", chunk-level scans from composed chunk maps" if args.chunk_scan else "")
-                               + (", SANA-WM batched additive update (comparator)" if args.sana_wm else ""),
+                               + (", SANA-WM batched additive update (comparator)" if args.sana_wm else "")
+                               + (", Newton-iteration inverse" if args.newton else ""),
                    "epilogue": bool(args.epilogue), "prep": bool(args.prep), "chunk_scan": bool(args.chunk_scan),
-                   "sana_wm": bool(args.sana_wm),
+                   "sana_wm": bool(args.sana_wm), "newton": bool(args.newton),
                    "heads": cfg.heads, "d": cfg.d, "frames": cfg.frames, "tokens": cfg.tokens,
                    "text_tokens": cfg.text_tokens, "in_dtype": cfg.in_dtype, "out_dtype": cfg.out_dtype,
                    "state_dtype": "f32", "global_batch": 1, "seq_len": cfg.frames * cfg.tokens,

@@ -33,6 +33,7 @@ struct Shape {
   int H, T, U, d, P, a, n, C, w, Nt, n_eff, count;
   bool chunked;  // VDA_CHUNK_SCAN
   bool sana;     // VDA_SANA_WM
+  bool newton;   // VDA_NEWTON
 };
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -57,8 +58,10 @@ int check_desc(const vda_desc* desc, Shape* s) {
   if (q.out_dtype != VDA_F32 && q.out_dtype != VDA_BF16 && q.out_dtype != VDA_F16)
     return fail(VDA_ERR_DTYPE, "out_dtype = %d (VDA_F32, VDA_BF16 or VDA_F16)", q.out_dtype);
   if (!(q.text_init_scale == q.text_init_scale)) return fail(VDA_ERR_SHAPE, "text_init_scale is NaN");
-  if (q.flags & ~(uint32_t)(VDA_NO_BRIDGE | VDA_PREP | VDA_CHUNK_SCAN | VDA_SANA_WM))
+  if (q.flags & ~(uint32_t)(VDA_NO_BRIDGE | VDA_PREP | VDA_CHUNK_SCAN | VDA_SANA_WM | VDA_NEWTON))
     return fail(VDA_ERR_SHAPE, "unknown flags 0x%x", q.flags);
+  if ((q.flags & VDA_SANA_WM) && (q.flags & VDA_NEWTON))
+    return fail(VDA_ERR_SHAPE, "VDA_SANA_WM has no inverse for VDA_NEWTON to form");
   if ((q.flags & VDA_SANA_WM) && (q.flags & VDA_CHUNK_SCAN))
     return fail(VDA_ERR_SHAPE, "VDA_SANA_WM and VDA_CHUNK_SCAN cannot be combined");
   if ((q.flags & VDA_CHUNK_SCAN) && q.window < 0)
@@ -79,6 +82,7 @@ int check_desc(const vda_desc* desc, Shape* s) {
   s->count = (s->w >= 0 ? s->C : s->n) + 1;
   s->chunked = (q.flags & VDA_CHUNK_SCAN) != 0;
   s->sana = (q.flags & VDA_SANA_WM) != 0;
+  s->newton = (q.flags & VDA_NEWTON) != 0;
   // 64-bit sizes must not overflow and grids must fit
   const double elems = (double)s->H * s->T * (double)s->U * s->d;
   if (elems > 9.0e15) return fail(VDA_ERR_SHAPE, "tensor too large");
@@ -260,10 +264,13 @@ int scan_args(const vda_desc* desc, const void* ws, const float* alpha, const fl
 
 int scan_mode(const Shape& s) { return s.sana ? vda::kSanaScan : s.chunked ? vda::kChunkScan : vda::kFrameScan; }
 
-// the factorisation, or the SANA-WM comparator's transition in its place
+// the factorisation (Gauss-Jordan, or Newton iteration), or the SANA-WM
+// comparator's transition in its place
 void launch_factor(const Shape& s, const vda::PrepArgs& a, hipStream_t st) {
   if (s.sana)
     vda::launch_sana(a, s.d, st);
+  else if (s.newton)
+    vda::launch_ns(a, s.d, st);
   else
     vda::launch_gj(a, s.d, st);
 }

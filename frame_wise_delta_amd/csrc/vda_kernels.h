@@ -84,6 +84,8 @@ struct AttnArgs {
 
 int launch_stats(const PrepArgs& a, int d, bool in_f32, hipStream_t stream);
 int launch_gj(const PrepArgs& a, int d, hipStream_t stream);
+// N = (I + A)^{-1} by Newton iteration instead of Gauss-Jordan.
+int launch_ns(const PrepArgs& a, int d, hipStream_t stream);
 // SANA-WM comparator: -A/U and B' = B/sqrt(U) in place of N and B.
 int launch_sana(const PrepArgs& a, int d, hipStream_t stream);
 void launch_clear_status(int* status, hipStream_t stream);

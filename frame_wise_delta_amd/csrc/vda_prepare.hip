@@ -601,6 +601,233 @@ __global__ __launch_bounds__(kThreads) void sana_kernel(PrepArgs args) {
   if (bad) atomicOr(args.status, bad);
 }
 
+// Newton iteration for N = (I + A)^{-1} in place of the Gauss-Jordan
+// inverse ("Video DeltaNet: A Video-Native Hybrid Attention for Livestream
+// Video Generation", experiments section, the weaknesses discussion: Newton
+// iteration instead of the exact inverse).  G = I + A is symmetric with
+// eigenvalues in [1, g], g its largest absolute row sum, so from
+// X_0 = c I, c = 2 / (1 + g), the residual I - G X_k is (I - c G)^(2^k) with
+// norm <= r^(2^k), r = (g - 1) / (g + 1); k is the smallest count with
+// r^(2^k) <= kNsTol.  Each step is X <- X + X R with R = I - G X, i.e.
+// X (2I - G X), whose residual is exactly R^2 whether or not X commutes
+// with G (the left-sided X + R X needs that, and the f16 steps break it at
+// the 1e-3 level, where the iteration then stalls).  X and R are written to
+// LDS transposed, so the columns of X (B operands of G X) and of R (B
+// operands of X R) are rows there.  The A operand of X R takes the rows of
+// X^T, i.e. the columns of X: X is symmetric up to rounding, and that
+// difference enters the residual only multiplied by R.
+// Precision: the steps before the last form G X from f16 G and X (the
+// residual then stalls near 1e-3); the last step forms G X from f16 hi/lo
+// pairs of both (float32 accuracy), which squares that residual away.  X is
+// kept in float32 accumulators throughout; R X uses f16 R and X (R is small).
+// One workgroup per matrix; a wavefront owns D/NWV rows of every product.
+constexpr float kNsTol = 1e-6f;
+
+template <int D>
+struct NsShape {
+  static constexpr int NWV = D / 16;                // wavefronts: one 16-row tile each
+  static constexpr int NTH = 64 * NWV;
+  static constexpr int RT = D / 16;                 // 16-row tiles of the matrix
+  static constexpr int RTW = RT / NWV;              // row tiles per wavefront
+  static constexpr int KS = D >= 32 ? D / 32 : 1;   // MFMA k-steps (D = 16: one, zero padded)
+  static constexpr int AP = D + 4;                  // LDS pitch (floats) of the A staging
+  static constexpr int XP = D + 8;                  // LDS pitch (halves) of X and R
+  static constexpr int LDS = D * AP * 4 > 2 * D * XP * 2 ? D * AP * 4 : 2 * D * XP * 2;
+};
+
+template <int D>
+__global__ __launch_bounds__(NsShape<D>::NTH, 2) void ns_kernel(PrepArgs args) {
+  using NS = NsShape<D>;
+  constexpr int RT = NS::RT, RTW = NS::RTW, KS = NS::KS, AP = NS::AP, XP = NS::XP;
+  __shared__ __attribute__((aligned(16))) float lds[NS::LDS / 4];
+  __shared__ float sMax[NS::NWV];
+  float* sA = lds;
+  _Float16* sXh = reinterpret_cast<_Float16*>(lds);  // X (f16 hi)
+  _Float16* sXl = sXh + D * XP;                      // X (f16 lo), or R
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lr = lane & 15, lg = lane >> 4;
+  const int h = blockIdx.x / args.cnt;
+  const int f = args.s0 + (blockIdx.x - h * args.cnt);
+  float* slot = args.frames + ((size_t)h * args.n_eff + f) * ws_slot_floats(D);
+  int bad = 0;
+
+  // ---- A (upper-triangle tiles, accumulator layout) -> LDS, full symmetric
+  for (int i = tid; i < RT * RT * 64; i += NS::NTH) {
+    const int l = i & 63, t = i >> 6;
+    const int ri = t / RT, cj = t - ri * RT;
+    if (cj < ri) continue;
+    const f32x4 v = *reinterpret_cast<const f32x4*>(slot + (size_t)i * 4);
+    const int c = 16 * cj + (l & 15);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = 16 * ri + 4 * (l >> 4) + e;
+      sA[r * AP + c] = v[e];
+      if (cj != ri) sA[c * AP + r] = v[e];
+    }
+  }
+  __syncthreads();
+  // ---- this wavefront's rows of G = I + A as A operands (hi/lo); row sums of |G|
+  f16x8 gh[RTW][KS], gl[RTW][KS];
+  float rs[RTW];
+#pragma unroll
+  for (int rt = 0; rt < RTW; ++rt) {
+    const int m = 16 * (wave * RTW + rt) + lr;
+    rs[rt] = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+      const int k0 = 32 * kk + 8 * lg;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float gv = k0 < D ? (m == k0 + e ? 1.f : 0.f) + sA[m * AP + k0 + e] : 0.f;
+        const _Float16 hi = (_Float16)gv;
+        gh[rt][kk][e] = hi;
+        gl[rt][kk][e] = (_Float16)(gv - (float)hi);
+        rs[rt] += fabsf(gv);
+      }
+    }
+    rs[rt] += __shfl_xor(rs[rt], 16, 64);
+    rs[rt] += __shfl_xor(rs[rt], 32, 64);
+  }
+  float gmax = 0.f;
+#pragma unroll
+  for (int rt = 0; rt < RTW; ++rt) gmax = fmaxf(gmax, rs[rt]);
+#pragma unroll
+  for (int off = 8; off > 0; off >>= 1) gmax = fmaxf(gmax, __shfl_xor(gmax, off, 64));
+  if (lane == 0) sMax[wave] = gmax;
+  __syncthreads();  // also: every wavefront is done with the A staging
+  gmax = sMax[0];
+#pragma unroll
+  for (int w = 1; w < NS::NWV; ++w) gmax = fmaxf(gmax, sMax[w]);
+  if (!__builtin_isfinite(gmax)) bad |= VDA_DEV_NONFINITE;
+  const float r = (gmax - 1.f) / (gmax + 1.f);
+  int k = 0;
+  for (float pw = r; pw > kNsTol && k < 64; pw *= pw) ++k;
+  const float c0 = 2.f / (1.f + gmax);
+
+  // ---- X in float32 accumulators: x[rt][ct][e] = X[16(wave RTW + rt) + 4lg + e][16ct + lr]
+  f32x4 x[RTW][RT];
+#pragma unroll
+  for (int rt = 0; rt < RTW; ++rt)
+#pragma unroll
+    for (int ct = 0; ct < RT; ++ct)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        x[rt][ct][e] = (16 * (wave * RTW + rt) + 4 * lg + e == 16 * ct + lr) ? c0 : 0.f;
+  // X^T = X to LDS: the 4 rows of a lane land as 4 consecutive halves of row 16ct + lr
+  auto put_x = [&](bool with_lo) {
+#pragma unroll
+    for (int rt = 0; rt < RTW; ++rt)
+#pragma unroll
+      for (int ct = 0; ct < RT; ++ct) {
+        f16x4 hi, lo;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          hi[e] = (_Float16)x[rt][ct][e];
+          lo[e] = (_Float16)(x[rt][ct][e] - (float)hi[e]);
+        }
+        const int at = (16 * ct + lr) * XP + 16 * (wave * RTW + rt) + 4 * lg;
+        *reinterpret_cast<f16x4*>(sXh + at) = hi;
+        if (with_lo) *reinterpret_cast<f16x4*>(sXl + at) = lo;
+      }
+  };
+  // B operand: row n = 16ct + lr (= column n), k = 32kk + 8lg .. +7
+  auto brow = [&](const _Float16* buf, int ct, int kk) {
+    const int k0 = 32 * kk + 8 * lg;
+    f16x8 v;
+    if (k0 < D) {
+      v = *reinterpret_cast<const f16x8*>(buf + (16 * ct + lr) * XP + k0);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = (_Float16)0.f;
+    }
+    return v;
+  };
+  put_x(k == 1);
+  __syncthreads();
+  for (int it = 0; it < k; ++it) {
+    const bool last = it == k - 1;
+    // Y = G X; R = I - Y
+    f32x4 y[RTW][RT];
+#pragma unroll
+    for (int rt = 0; rt < RTW; ++rt)
+#pragma unroll
+      for (int ct = 0; ct < RT; ++ct) y[rt][ct] = f32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int ct = 0; ct < RT; ++ct)
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) {
+        const f16x8 xb = brow(sXh, ct, kk);
+#pragma unroll
+        for (int rt = 0; rt < RTW; ++rt) y[rt][ct] = mfma_f16(gh[rt][kk], xb, y[rt][ct]);
+        if (last) {
+          const f16x8 xl = brow(sXl, ct, kk);
+#pragma unroll
+          for (int rt = 0; rt < RTW; ++rt) {
+            y[rt][ct] = mfma_f16(gh[rt][kk], xl, y[rt][ct]);
+            y[rt][ct] = mfma_f16(gl[rt][kk], xb, y[rt][ct]);
+          }
+        }
+      }
+    __syncthreads();  // X lo is read before R takes its place
+#pragma unroll
+    for (int rt = 0; rt < RTW; ++rt)
+#pragma unroll
+      for (int ct = 0; ct < RT; ++ct) {
+        f16x4 rv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float id = (16 * (wave * RTW + rt) + 4 * lg + e == 16 * ct + lr) ? 1.f : 0.f;
+          rv[e] = (_Float16)(id - y[rt][ct][e]);
+        }
+        *reinterpret_cast<f16x4*>(sXl + (16 * ct + lr) * XP + 16 * (wave * RTW + rt) + 4 * lg) = rv;  // R^T
+      }
+    __syncthreads();
+    // X <- X + X R: A operand = this wavefront's rows of X^T, B operand = rows of R^T
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+      f16x8 xa[RTW];
+#pragma unroll
+      for (int rt = 0; rt < RTW; ++rt) {
+        const int k0 = 32 * kk + 8 * lg;
+        if (k0 < D) {
+          xa[rt] = *reinterpret_cast<const f16x8*>(sXh + (16 * (wave * RTW + rt) + lr) * XP + k0);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) xa[rt][e] = (_Float16)0.f;
+        }
+      }
+#pragma unroll
+      for (int ct = 0; ct < RT; ++ct) {
+        const f16x8 rb = brow(sXl, ct, kk);
+#pragma unroll
+        for (int rt = 0; rt < RTW; ++rt) x[rt][ct] = mfma_f16(xa[rt], rb, x[rt][ct]);
+      }
+    }
+    __syncthreads();
+    if (!last) {
+      put_x(it + 1 == k - 1);
+      __syncthreads();
+    }
+  }
+
+  // ---- N = X -> workspace as f16 in fragment order; a tile covers column
+  //      16ct + lr, rows 16R + 4lg + e: half of chunk (16ct + lr, 2R + lg/2)
+  _Float16* nf = reinterpret_cast<_Float16*>(slot);
+#pragma unroll
+  for (int rt = 0; rt < RTW; ++rt)
+#pragma unroll
+    for (int ct = 0; ct < RT; ++ct) {
+      const int R = wave * RTW + rt;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (!__builtin_isfinite(x[rt][ct][e])) bad |= VDA_DEV_NONFINITE;
+      const size_t off = (size_t)ntile_chunk(D, 16 * ct + lr, 2 * R + (lg >> 1)) * 8 + 4 * (lg & 1);
+      *reinterpret_cast<f16x4*>(nf + off) = __builtin_convertvector(x[rt][ct], f16x4);
+    }
+  if (bad) atomicOr(args.status, bad);
+}
+
 __global__ void clear_status_kernel(int* status) { *status = 0; }
 
 int launch_stats(const PrepArgs& a, int d, bool in_f32, hipStream_t stream) {
@@ -633,6 +860,19 @@ int launch_gj(const PrepArgs& a, int d, hipStream_t stream) {
   }
   VDA_GJ(16) VDA_GJ(32) VDA_GJ(64) VDA_GJ(128)
 #undef VDA_GJ
+  return -1;
+}
+
+int launch_ns(const PrepArgs& a, int d, hipStream_t stream) {
+  if (a.H == 0 || a.cnt == 0) return 0;
+  dim3 grid((unsigned)(a.H * a.cnt));
+#define VDA_NS(DD)                                                                    \
+  if (d == DD) {                                                                      \
+    hipLaunchKernelGGL((ns_kernel<DD>), grid, dim3(NsShape<DD>::NTH), 0, stream, a);  \
+    return 0;                                                                         \
+  }
+  VDA_NS(16) VDA_NS(32) VDA_NS(64) VDA_NS(128)
+#undef VDA_NS
   return -1;
 }
 

@@ -30,6 +30,7 @@ VDA_NO_BRIDGE = 1
 VDA_PREP = 2
 VDA_CHUNK_SCAN = 4
 VDA_SANA_WM = 8
+VDA_NEWTON = 16
 VDA_DEV_NONFINITE, VDA_DEV_PIVOT = 1, 2
 
 DTYPES = {"f32": VDA_F32, "bf16": VDA_BF16, "f16": VDA_F16}
@@ -130,11 +131,12 @@ def _stream(stream):
 
 def make_desc(heads, frames, tokens, d, chunk=5, anchors=1, window=1, text_tokens=0,
               in_dtype="bf16", out_dtype="bf16", text_init_scale=0.5, bridge=True, prep=False,
-              chunk_scan=False, sana_wm=False) -> vda_desc:
+              chunk_scan=False, sana_wm=False, newton=False) -> vda_desc:
     return vda_desc(heads, frames, tokens, d, d, chunk, anchors, window, text_tokens,
                     DTYPES[in_dtype], DTYPES[out_dtype], text_init_scale,
                     (0 if bridge else VDA_NO_BRIDGE) | (VDA_PREP if prep else 0) |
-                    (VDA_CHUNK_SCAN if chunk_scan else 0) | (VDA_SANA_WM if sana_wm else 0))
+                    (VDA_CHUNK_SCAN if chunk_scan else 0) | (VDA_SANA_WM if sana_wm else 0) |
+                    (VDA_NEWTON if newton else 0))
 
 
 def desc_for(cfg, **over) -> vda_desc:

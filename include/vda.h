@@ -86,7 +86,14 @@ enum {
                               N_text for the text write, so S^T = B_T/sqrt(N_text));
                               vda_factor_frames then forms -A_t/U and B_t/sqrt(U)
                               in place of (I + A_t)^{-1} and B_t; not with
-                              VDA_CHUNK_SCAN */
+                              VDA_CHUNK_SCAN */,
+  VDA_NEWTON = 1u << 4     /* (I + A_t)^{-1} by Newton iteration
+                              [VDN 实验结果, weaknesses: Newton iteration in place
+                              of the exact inverse] instead of Gauss-Jordan:
+                              X <- X + (I - G X) X from X_0 = 2/(1+g) I, g the largest
+                              absolute row sum of G = I + A_t, until the residual
+                              bound ((g-1)/(g+1))^(2^k) <= 1e-6; same workspace
+                              contents and layout; not with VDA_SANA_WM */
 };
 
 /* bits of the device status word */
@@ -111,7 +118,7 @@ typedef struct vda_desc {
   int32_t out_dtype;   /* out: VDA_F32, VDA_BF16 or VDA_F16 */
   float text_init_scale; /* both scans start from text_init_scale * S^T;
                             1/2 reads the page's "initialised by halves" */
-  uint32_t flags;      /* VDA_NO_BRIDGE | VDA_PREP | VDA_CHUNK_SCAN | VDA_SANA_WM */
+  uint32_t flags;      /* VDA_NO_BRIDGE | VDA_PREP | VDA_CHUNK_SCAN | VDA_SANA_WM | VDA_NEWTON */
 } vda_desc;
 
 /* Bytes of device workspace vda_prepare_frames needs for `desc` (host only,

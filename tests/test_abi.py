@@ -70,7 +70,7 @@ def test_bad_dtypes_and_flags():
         vda.vda_state_count(d)
     assert e.value.code == vda.VDA_ERR_DTYPE
     d = _desc()
-    d.flags = 16
+    d.flags = 32
     with pytest.raises(vda.VdaError) as e:
         vda.vda_state_count(d)
     assert e.value.code == vda.VDA_ERR_SHAPE
@@ -85,6 +85,11 @@ def test_bad_dtypes_and_flags():
     assert vda.vda_workspace_bytes(d) == vda.vda_workspace_bytes(_desc())
     with pytest.raises(vda.VdaError) as e:  # its frame map has no chunk composition
         vda.vda_state_count(_desc(sana_wm=True, chunk_scan=True))
+    assert e.value.code == vda.VDA_ERR_SHAPE
+    d = _desc(newton=True, chunk_scan=True, prep=True)  # the Newton inverse goes with every other mode
+    assert vda.vda_workspace_bytes(d) == vda.vda_workspace_bytes(_desc(chunk_scan=True))
+    with pytest.raises(vda.VdaError) as e:  # the additive update has no inverse
+        vda.vda_state_count(_desc(sana_wm=True, newton=True))
     assert e.value.code == vda.VDA_ERR_SHAPE
 
 
