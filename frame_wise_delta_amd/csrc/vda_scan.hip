@@ -39,6 +39,8 @@
 //    path as a frame step (S as an f16 hi/lo pair, M_c as the B operand) with
 //    the accumulators starting from J_c; the state is recorded after every
 //    chunk, which is where the windowed readout needs it.
+#include <type_traits>
+
 #include "vda_common.h"
 #include "vda_kernels.h"
 
@@ -305,20 +307,28 @@ namespace {
 template <int D>
 struct ComposeShape {
   static constexpr int NTW = D == 128 ? 2 : 1;         // 16-row tiles of Z per wavefront
-  static constexpr int NWV = D / (16 * NTW);            // wavefronts: one workgroup holds a d x d half of Z
-  static constexpr int NTH = 64 * NWV;                  // threads
+  static constexpr int NWH = D / (16 * NTW);            // wavefronts per d x d half of Z
+  static constexpr int NTH = 2 * 64 * NWH;              // threads: both halves
   static constexpr int MT = D / 16;                     // 16-column tiles of Z
   static constexpr int KS = D >= 32 ? D / 32 : 1;       // MFMA k-steps (D = 16: one, zero padded)
   static constexpr int NCH = 2 * D * D / 16;            // 16-byte chunks of N
   static constexpr int CPT = (NCH + NTH - 1) / NTH;     // chunks staged per thread
-  static constexpr int TP = D + 8;                      // LDS pitch (halves) of the output tile
+  static constexpr int TP = D + 8;                      // LDS pitch (halves) of the output tiles
+  static constexpr int NLDS = 2 * D * TP > 2 * D * D ? 2 * D * TP : 2 * D * D;  // halves
+};
+
+template <int D>
+struct ComposeLds {
+  _Float16 n[ComposeShape<D>::NLDS];  // N of two frames; then both output tiles
+  float al[2][D];                     // alpha of two frames
 };
 
 }  // namespace
 
 // The chunk maps of every (head, chunk, direction).  One workgroup runs one
-// half of the stacked state of one chain: the d rows of Y (part 0, from I)
-// or of X (part 1, from 0, with B).  The product is taken transposed,
+// chain: its first half of wavefronts the d rows of Y (from I, no B), its
+// second half the d rows of X (from 0, with B); N and alpha of each frame
+// are staged once for both.  The product is taken transposed,
 // Z^T <- N X^T (N is symmetric), so that a lane's accumulators hold four
 // consecutive columns of one row of Z: the next step's X = Z Diag(alpha) + B
 // is then formed in registers and is already the B operand of the next
@@ -331,27 +341,28 @@ struct ComposeShape {
 // as f16 on the Y rows (M_c: the product of contractions, whose rounding the
 // f16 store of M_c dominates).
 template <int D>
-struct ComposeLds {
-  _Float16 n[2 * D * D + (D == 16 ? D * 8 : 0)];  // N of two frames; then the output tile
-  float al[2][D];                                  // alpha of two frames
-};
-
-template <int D, bool JPART>
-__device__ __forceinline__ void compose_half(const ScanArgs& a, int h, int cc, ComposeLds<D>& lds) {
+__global__ __launch_bounds__(ComposeShape<D>::NTH, 1) void compose_kernel(ScanPair p) {
   using CS = ComposeShape<D>;
   constexpr int MT = CS::MT, NTW = CS::NTW, KS = CS::KS, TP = CS::TP;
-  static_assert(2 * D * D >= D * TP || D == 16, "output tile fits the two N buffers");
+  __shared__ __attribute__((aligned(16))) ComposeLds<D> lds;
   _Float16* sN = lds.n;
   float (*sA)[D] = lds.al;
-  constexpr bool jpart = JPART;  // rows of J_c (else of M_c)
+
+  int L = xcd_block(blockIdx.x, gridDim.x);
+  const int per_dir = p.dir[0].H * p.dir[0].C;
+  const int dir = L >= per_dir ? 1 : 0;
+  L -= dir * per_dir;
+  const ScanArgs& a = p.dir[dir];
+  const int h = L / a.C, cc = L - h * a.C;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, lg = lane >> 4;
+  const bool jpart = wave >= CS::NWH;                     // rows of J_c (else of M_c); wave-uniform
+  const int n0 = 16 * NTW * (jpart ? wave - CS::NWH : wave);  // first row of Z (within its half)
   const int P = a.P;
   const size_t slot_floats = ws_slot_floats(D);
   const float* frames = a.frames + (size_t)h * a.n_eff * slot_floats;
   const float* alpha_h = a.alpha + (size_t)h * a.T * D;
   auto slot_of = [&](int i) { return P * cc + (a.reverse ? P - 1 - i : i); };
-  const int n0 = 16 * NTW * wave;  // this wavefront's first row of Z (within its half)
 
   f16x8 nreg[CS::CPT];
   float areg = 0.f;
@@ -384,7 +395,7 @@ __device__ __forceinline__ void compose_half(const ScanArgs& a, int h, int cc, C
     if (tid < D) sA[buf][tid] = a.prep ? sigmoid_gate(areg) : areg;
   };
 
-  // Z (this half) in accumulators: acc[mt][nt][e] = Z[n0 + 16nt + lr][16mt + 4lg + e]
+  // this half of Z in accumulators: acc[mt][nt][e] = Z[n0 + 16nt + lr][16mt + 4lg + e]
   f32x4 acc[MT][NTW];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
@@ -393,90 +404,93 @@ __device__ __forceinline__ void compose_half(const ScanArgs& a, int h, int cc, C
 #pragma unroll
       for (int e = 0; e < 4; ++e) acc[mt][nt][e] = (!jpart && n0 + 16 * nt + lr == 16 * mt + 4 * lg + e) ? 1.f : 0.f;
 
-  fetch(0);
-  stage(0);
-  lds_barrier();
-  for (int i = 0; i < P; ++i) {
-    const int buf = i & 1;
-    // X = Z Diag(alpha) (+ B) as the B operands of the k-steps
-    f16x8 xh[NTW][KS], xl[NTW][KS];
-#pragma unroll
-    for (int kk = 0; kk < KS; ++kk)
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const int mt = 2 * kk + half;
-        if (mt < MT) {
-          const float4 al = *reinterpret_cast<const float4*>(&sA[buf][16 * mt + 4 * lg]);
-          const float alv[4] = {al.x, al.y, al.z, al.w};
-#pragma unroll
-          for (int nt = 0; nt < NTW; ++nt)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const float x = jpart ? fmaf(acc[mt][nt][e], alv[e], (float)breg[nt][mt][e]) : acc[mt][nt][e] * alv[e];
-              const _Float16 hi = (_Float16)x;
-              xh[nt][kk][4 * half + e] = hi;
-              xl[nt][kk][4 * half + e] = (_Float16)(x - (float)hi);
-            }
-        } else {
-#pragma unroll
-          for (int nt = 0; nt < NTW; ++nt)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) xh[nt][kk][4 * half + e] = xl[nt][kk][4 * half + e] = (_Float16)0.f;
-        }
-      }
-    if (i + 1 < P) fetch(i + 1);
-    // Z^T <- N X^T
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int nt = 0; nt < NTW; ++nt) acc[mt][nt] = f32x4{0, 0, 0, 0};
-    const _Float16* nb = sN + buf * D * D;
-#pragma unroll
-    for (int kk = 0; kk < KS; ++kk)
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        const int m = 16 * mt + lr;
-        const f16x4 lo4 = *reinterpret_cast<const f16x4*>(nb + ntile_chunk(D, m, 4 * kk + (lg >> 1)) * 8 + 4 * (lg & 1));
-        f16x4 hi4;
-        if (32 * kk + 16 < D) {
-          hi4 = *reinterpret_cast<const f16x4*>(nb + ntile_chunk(D, m, 4 * kk + 2 + (lg >> 1)) * 8 + 4 * (lg & 1));
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) hi4[e] = (_Float16)0.f;
-        }
-        const f16x8 av = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
-#pragma unroll
-        for (int nt = 0; nt < NTW; ++nt) {
-          acc[mt][nt] = mfma_f16(av, xh[nt][kk], acc[mt][nt]);
-          if (jpart) acc[mt][nt] = mfma_f16(av, xl[nt][kk], acc[mt][nt]);
-        }
-      }
-    if (i + 1 < P) stage(buf ^ 1);
+  // the frames of the chunk on this half (JP: the X rows); both halves run
+  // the same sequence of barriers
+  auto run = [&](auto jp) {
+    constexpr bool JP = decltype(jp)::value;
+    fetch(0);
+    stage(0);
     lds_barrier();
-  }
+    for (int i = 0; i < P; ++i) {
+      const int buf = i & 1;
+      // X = Z Diag(alpha) (+ B) as the B operands of the k-steps
+      f16x8 xh[NTW][KS], xl[NTW][KS];
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk)
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          const int mt = 2 * kk + half;
+          if (mt < MT) {
+            const float4 al = *reinterpret_cast<const float4*>(&sA[buf][16 * mt + 4 * lg]);
+            const float alv[4] = {al.x, al.y, al.z, al.w};
+#pragma unroll
+            for (int nt = 0; nt < NTW; ++nt)
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const float x = JP ? fmaf(acc[mt][nt][e], alv[e], (float)breg[nt][mt][e]) : acc[mt][nt][e] * alv[e];
+                const _Float16 hi = (_Float16)x;
+                xh[nt][kk][4 * half + e] = hi;
+                xl[nt][kk][4 * half + e] = JP ? (_Float16)(x - (float)hi) : (_Float16)0.f;
+              }
+          } else {
+#pragma unroll
+            for (int nt = 0; nt < NTW; ++nt)
+#pragma unroll
+              for (int e = 0; e < 4; ++e) xh[nt][kk][4 * half + e] = xl[nt][kk][4 * half + e] = (_Float16)0.f;
+          }
+        }
+      // the next frame's loads are in flight during the MFMAs
+      if (i + 1 < P) fetch(i + 1);
+      // Z^T <- N X^T
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < NTW; ++nt) acc[mt][nt] = f32x4{0, 0, 0, 0};
+      const _Float16* nb = sN + buf * D * D;
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          const int m = 16 * mt + lr;
+          const f16x4 lo4 = *reinterpret_cast<const f16x4*>(nb + ntile_chunk(D, m, 4 * kk + (lg >> 1)) * 8 + 4 * (lg & 1));
+          f16x4 hi4;
+          if (32 * kk + 16 < D) {
+            hi4 = *reinterpret_cast<const f16x4*>(nb + ntile_chunk(D, m, 4 * kk + 2 + (lg >> 1)) * 8 + 4 * (lg & 1));
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) hi4[e] = (_Float16)0.f;
+          }
+          const f16x8 av = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+#pragma unroll
+          for (int nt = 0; nt < NTW; ++nt) {
+            acc[mt][nt] = mfma_f16(av, xh[nt][kk], acc[mt][nt]);
+            if (JP) acc[mt][nt] = mfma_f16(av, xl[nt][kk], acc[mt][nt]);
+          }
+        }
+      if (i + 1 < P) stage(buf ^ 1);
+      lds_barrier();
+    }
+  };
+  if (jpart)
+    run(std::true_type{});
+  else
+    run(std::false_type{});
 
-  // ---- store the half through LDS (the N buffers are free now)
+  // ---- store through LDS (the N buffers are free now): M_c from the first
+  //      half of the tile memory, J_c from the second
   char* out = static_cast<char*>(a.chunks) + ((size_t)(2 * h + a.reverse) * a.C + cc) * (size_t)(4 * D * D);
-  _Float16* T = sN;
+  _Float16* TM = sN;
+  _Float16* TJ = sN + D * TP;
   if (!jpart) {
-    // M_c: T[m][n] = M_c[n][m], read back as column chunks in the fragment order of N
+    // T_M[m][n] = M_c[n][m]
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int nt = 0; nt < NTW; ++nt)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) T[(16 * mt + 4 * lg + e) * TP + n0 + 16 * nt + lr] = (_Float16)acc[mt][nt][e];
-    lds_barrier();
-    constexpr int LG = D >= 32 ? 4 : D / 8;
-    f16x8* mf = reinterpret_cast<f16x8*>(out);
-    for (int q = tid; q < D * D / 8; q += CS::NTH) {
-      const int t = q / (16 * LG);
-      const int c = 4 * (t % KS) + (q / 16) % LG;
-      const int j = 16 * (t / KS) + (q & 15);
-      mf[q] = *reinterpret_cast<const f16x8*>(T + j * TP + 8 * c);
-    }
+        for (int e = 0; e < 4; ++e) TM[(16 * mt + 4 * lg + e) * TP + n0 + 16 * nt + lr] = (_Float16)acc[mt][nt][e];
   } else {
-    // J_c: T[n][m] = J_c[n][m], read back in the chunk scan's accumulator order
+    // T_J[n][m] = J_c[n][m]
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -484,36 +498,30 @@ __device__ __forceinline__ void compose_half(const ScanArgs& a, int h, int cc, C
         f16x4 v;
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] = (_Float16)acc[mt][nt][e];
-        *reinterpret_cast<f16x4*>(T + (n0 + 16 * nt + lr) * TP + 16 * mt + 4 * lg) = v;
+        *reinterpret_cast<f16x4*>(TJ + (n0 + 16 * nt + lr) * TP + 16 * mt + 4 * lg) = v;
       }
-    lds_barrier();
-    f16x4* jf = reinterpret_cast<f16x4*>(out + 2 * D * D);
-    for (int q = tid; q < D * D / 4; q += CS::NTH) {
-      const int l = q & 63, t = q >> 6;
-      const int rt = t / MT, ct = t - rt * MT;
-      const int row = 16 * rt + 4 * (l >> 4), col = 16 * ct + (l & 15);
-      f16x4 v;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] = T[(row + e) * TP + col];
-      jf[q] = v;
-    }
   }
-}
-
-template <int D>
-__global__ __launch_bounds__(ComposeShape<D>::NTH, 2) void compose_kernel(ScanPair p) {
-  __shared__ __attribute__((aligned(16))) ComposeLds<D> lds;
-  int L = xcd_block(blockIdx.x, gridDim.x);
-  const int per_dir = p.dir[0].H * p.dir[0].C * 2;
-  const int dir = L >= per_dir ? 1 : 0;
-  L -= dir * per_dir;
-  const ScanArgs& a = p.dir[dir];
-  const int chain = L >> 1;
-  const int h = chain / a.C, cc = chain - h * a.C;
-  if (L & 1)
-    compose_half<D, true>(a, h, cc, lds);
-  else
-    compose_half<D, false>(a, h, cc, lds);
+  lds_barrier();
+  // M_c as column chunks in the fragment order of N
+  constexpr int LG = D >= 32 ? 4 : D / 8;
+  f16x8* mf = reinterpret_cast<f16x8*>(out);
+  for (int q = tid; q < D * D / 8; q += CS::NTH) {
+    const int t = q / (16 * LG);
+    const int c = 4 * (t % KS) + (q / 16) % LG;
+    const int j = 16 * (t / KS) + (q & 15);
+    mf[q] = *reinterpret_cast<const f16x8*>(TM + j * TP + 8 * c);
+  }
+  // J_c in the chunk scan's accumulator order
+  f16x4* jf = reinterpret_cast<f16x4*>(out + 2 * D * D);
+  for (int q = tid; q < D * D / 4; q += CS::NTH) {
+    const int l = q & 63, t = q >> 6;
+    const int rt = t / MT, ct = t - rt * MT;
+    const int row = 16 * rt + 4 * (l >> 4), col = 16 * ct + (l & 15);
+    f16x4 v;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = TJ[(row + e) * TP + col];
+    jf[q] = v;
+  }
 }
 
 int launch_scan(const ScanPair& p, int d, hipStream_t stream) {
@@ -521,7 +529,7 @@ int launch_scan(const ScanPair& p, int d, hipStream_t stream) {
   if (H == 0) return 0;
   if (p.mode == kCompose) {
     if (p.dir[0].C == 0 || p.dir[0].P == 0) return 0;
-    const long blocks = (long)p.ndir * H * p.dir[0].C * 2;  // two halves of the stacked state per chain
+    const long blocks = (long)p.ndir * H * p.dir[0].C;  // one workgroup per chain
 #define VDA_COMPOSE(DD)                                                                               \
     if (d == DD) {                                                                                    \
       hipLaunchKernelGGL((compose_kernel<DD>), dim3((unsigned)blocks), dim3(ComposeShape<DD>::NTH), 0, stream, p); \
