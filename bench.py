@@ -48,6 +48,7 @@ import csv
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -147,9 +148,12 @@ def copy_calibration():
 
 def _short(name):
     """Short name of a profiled kernel; the gated readout is the
-    readout_kernel instantiation with its last template argument true."""
+    readout_kernel instantiation whose fourth template argument (GATED) is
+    true: readout_kernel<D, TIN, OUT, GATED, PREP>."""
     if "readout_kernel" in name:
-        return "readout_gated" if ("ELb1E" in name or "true>" in name) else "readout_kernel"
+        m = re.search(r"readout_kernel<([^>]*)>", name)
+        args = [x.strip() for x in m.group(1).split(",")] if m else []
+        return "readout_gated" if len(args) >= 4 and args[3] == "true" else "readout_kernel"
     for k in KERNELS:
         if k in name:
             return k
