@@ -350,9 +350,9 @@ def main():
         write_traffic(*args.traffic)
         return
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (--gpus {args.gpus} requested): the VDA path is "
-              "built and measured on a single MI355X; heads would shard across GPUs with no "
-              "communication, which this build does not run.", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (--gpus {args.gpus} requested): libvda runs and is "
+              "measured on a single MI355X; heads would shard across GPUs with no communication, "
+              "but no multi-GPU path exists here.", file=sys.stderr)
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration()
