@@ -8,9 +8,13 @@ tokens per frame, 512 text tokens, bf16 inputs, float32 state, bf16 output):
 
 (the same kernels, in the same order, as one vda_forward call).  Inputs are
 seeded synthetic draws (frame_wise_delta_amd.inputs) resident in HBM before
-timing starts.  Prints one JSON line: latent frames/s, algorithmic TFLOP/s,
-a roofline entry for the dominant HBM-bound kernel timed with HIP events on
-the stream it runs on, and the float64 oracle timed on this host's cores.
+timing starts.  The timed region is K steps back to back (ms_per_step, the
+headline); a second pass of K steps brackets every call with HIP events on
+the stream it runs on, for the per-call times and the roofline of the
+dominant HBM-bound kernel (the events add ~30 us per step, so that pass is
+not the step time).  Prints one JSON line: latent frames/s, algorithmic
+TFLOP/s, the roofline entry, and the float64 oracle timed on this host's
+cores.
 
     python bench.py [--steps K] [--warmup W] [--config h3] [--no-cpu-baseline] [--epilogue] [--prep]
                     [--chunk-scan] [--sana-wm] [--newton]
@@ -325,8 +329,9 @@ def softmax_bench(args):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=20,
+                    help="untimed steps first (the clock settles over the first ~20 steps)")
     ap.add_argument("--config", default="h3")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
@@ -379,17 +384,16 @@ def main():
         gate, norm_w = runner.upload_epilogue(cfg, epi_in)
     main_s = torch.cuda.current_stream()
 
-    # events around each call, on the stream they all run on
+    # the calls of a step, as named in call_ms
     names = ["stats", "factor"] + (["compose"] if args.chunk_scan else []) + ["scans", "readout"]
-    ev = {k: [] for k in names}
 
-    def step(record):
+    def step(pairs=None):
+        """One step; with pairs (event pairs per call) each call is bracketed
+        by HIP events recorded on the stream it runs on."""
         x, b = dev, bufs
-        pairs = {k: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                 for k in names} if record else None
 
         def mark(k, i):
-            if record:
+            if pairs is not None:
                 pairs[k][i].record(main_s)
         mark("stats", 0)
         vda.vda_frame_stats(desc, x.k, x.v, x.beta, x.kt, x.vt, x.bt, b.ws, b.ws_bytes, stream=main_s)
@@ -411,22 +415,28 @@ def main():
         else:
             vda.vda_readout(desc, x.q, x.alpha, b.states_f, b.states_r, b.out, stream=main_s)
         mark("readout", 1)
-        if record:
-            for k in names:
-                ev[k].append(pairs[k])
 
     for _ in range(args.warmup):
-        step(False)
+        step()
     torch.cuda.synchronize()
     print(f"[bench] warmup {args.warmup} steps done", file=sys.stderr, flush=True)
+    # the timed region: K steps back to back, nothing else on the stream
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        step(True)
+        step()
     torch.cuda.synchronize()
     t_total = time.perf_counter() - t0
     status = vda.vda_device_status(desc, bufs.ws)
     ms_step = 1e3 * t_total / args.steps
-    kms = {k: float(np.mean([a.elapsed_time(b) for a, b in ev[k]])) for k in names}
+    # per-call times: K more steps with an event pair (created beforehand)
+    # around every call; the events themselves cost ~30 us per step, so this
+    # pass gives the kernels' durations, not the step time
+    pairs = [{k: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for k in names}
+             for _ in range(args.steps)]
+    for i in range(args.steps):
+        step(pairs[i])
+    torch.cuda.synchronize()
+    kms = {k: float(np.mean([pr[k][0].elapsed_time(pr[k][1]) for pr in pairs])) for k in names}
     print(f"[bench] {args.steps} steps: {ms_step:.3f} ms/step; calls {kms}", file=sys.stderr, flush=True)
 
     flops, nbytes = algorithmic_work(cfg, args.epilogue)
