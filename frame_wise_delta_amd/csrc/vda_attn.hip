@@ -176,18 +176,34 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
   };
 
   uint4 pk[LPT], pv[LPT];
+  // this thread's 16-byte chunks of a key tile: row c / CPR, channels 8 (c % CPR) ..
+  // (the same offsets for every tile; rows are contiguous within a segment)
+  int coff[LPT], crow[LPT], loff[LPT];  // global (elements) and LDS (halves) offsets
+#pragma unroll
+  for (int i = 0; i < LPT; ++i) {
+    const int c = tid + i * kThreads;
+    crow[i] = c / CPR;
+    coff[i] = crow[i] * D + 8 * (c - crow[i] * CPR);
+    loff[i] = crow[i] * KP + 8 * (c - crow[i] * CPR);
+  }
   auto fetch = [&](int j) {
     const u16* kb;
     const u16* vb;
     int n;
     tile_src(j, kb, vb, n);
+    if (n == kKT) {  // a full tile (every tile but a segment's last): no masks
 #pragma unroll
-    for (int i = 0; i < LPT; ++i) {
-      const int c = tid + i * kThreads;
-      const int r = c / CPR, ch = c - r * CPR;
-      const bool ok = r < n;
-      pk[i] = ok ? *reinterpret_cast<const uint4*>(kb + (size_t)r * D + 8 * ch) : make_uint4(0, 0, 0, 0);
-      pv[i] = ok ? *reinterpret_cast<const uint4*>(vb + (size_t)r * D + 8 * ch) : make_uint4(0, 0, 0, 0);
+      for (int i = 0; i < LPT; ++i) {
+        pk[i] = *reinterpret_cast<const uint4*>(kb + coff[i]);
+        pv[i] = *reinterpret_cast<const uint4*>(vb + coff[i]);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < LPT; ++i) {
+        const bool ok = crow[i] < n;
+        pk[i] = ok ? *reinterpret_cast<const uint4*>(kb + coff[i]) : make_uint4(0, 0, 0, 0);
+        pv[i] = ok ? *reinterpret_cast<const uint4*>(vb + coff[i]) : make_uint4(0, 0, 0, 0);
+      }
     }
     return n;
   };
@@ -216,11 +232,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
     // ---- stage tile j: K as loaded, V converted to f16
 #pragma unroll
     for (int i = 0; i < LPT; ++i) {
-      const int c = tid + i * kThreads;
-      const int r = c / CPR, ch = c - r * CPR;
-      *reinterpret_cast<uint4*>(sK + r * KP + 8 * ch) = pk[i];
+      *reinterpret_cast<uint4*>(sK + loff[i]) = pk[i];
       if constexpr (VF16) {
-        *reinterpret_cast<uint4*>(sV + r * KP + 8 * ch) = pv[i];
+        *reinterpret_cast<uint4*>(sV + loff[i]) = pv[i];
       } else {  // bf16 V -> f16
         const uint32_t u[4] = {pv[i].x, pv[i].y, pv[i].z, pv[i].w};
         f16x8 hv;
@@ -229,7 +243,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
           hv[2 * e] = (_Float16)__uint_as_float(u[e] << 16);
           hv[2 * e + 1] = (_Float16)__uint_as_float(u[e] & 0xffff0000u);
         }
-        *reinterpret_cast<f16x8*>(sV + r * KP + 8 * ch) = hv;
+        *reinterpret_cast<f16x8*>(sV + loff[i]) = hv;
       }
     }
     const int n_tile = n_cur;
