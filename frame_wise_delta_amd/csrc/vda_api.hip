@@ -497,7 +497,7 @@ int vda_softmax_branch(const vda_desc* desc, const void* q, const void* k, const
   a.Nt = s.Nt;
   a.scale = scale;
   a.v_f16 = v_dtype == VDA_F16;
-  const int qb = 128;  // queries per workgroup
+  const int qb = 256;  // queries per workgroup (the attention kernel's kQB)
   a.anchor_tiles = s.a ? (s.U + qb - 1) / qb : 0;
   a.chunk_tiles = (s.P * s.U + qb - 1) / qb;
   a.tiles_per_head = 2 * a.anchor_tiles + s.C * a.chunk_tiles;

@@ -9,11 +9,12 @@
 //
 //   o = softmax(q K^T * scale) V  over those keys.
 //
-// Flash-attention style: one 256-thread workgroup per 128 query tokens of
-// one query block (a chunk's frames, or one anchor frame), four wavefronts of
-// 32 queries.  Keys stream through LDS in 64-key tiles, segment by segment
-// (window frames, anchor frames, text), with the next tile's loads in flight
-// during the current tile's work.  The scores are formed transposed,
+// Flash-attention style: one 512-thread workgroup per 256 query tokens of
+// one query block (a chunk's frames, or one anchor frame), eight wavefronts
+// of 32 queries, so that every key tile is fetched and staged once for 256
+// queries.  Keys stream through LDS in 64-key tiles, segment by segment
+// (window frames, anchor frames, text); the next two tiles' loads are in
+// flight, in two register sets, during the current tile's work.  The scores are formed transposed,
 // S^T = K Q^T (16x16x32 bf16 MFMA), so that a wavefront's accumulator lane
 // holds four consecutive keys of one query; two such tiles make the B
 // operand of a 16x16x32 MFMA.  The output is accumulated transposed as well,
@@ -22,6 +23,8 @@
 // transposing load in the same key order; the softmax denominators come out
 // of the same MFMAs (an all-ones row block in place of V^T).  The softmax is online (running max and
 // sum per query, in float32, base 2).
+#include <type_traits>
+
 #include "vda_common.h"
 #include "vda_kernels.h"
 
@@ -29,7 +32,8 @@ namespace vda {
 
 namespace {
 
-constexpr int kQB = 128;  // queries per workgroup
+constexpr int kQB = 256;  // queries per workgroup
+constexpr int kAT = 512;  // threads per workgroup: eight wavefronts of 32 queries
 constexpr int kKT = 64;   // keys per LDS tile
 
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
@@ -66,14 +70,14 @@ __device__ __forceinline__ void store_out4(void* base, size_t idx, f32x4 v) {
 // [anchor frame T-1]; block b has nq(b) query tokens starting at token
 // q0(b) of the head and ceil(nq / kQB) workgroups.
 template <int D, int OUT, bool VF16>
-__global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
+__global__ __launch_bounds__(kAT, 1) void attn_kernel(AttnArgs a) {
   static_assert(D % 32 == 0 && D <= 128, "head size must be 32, 64 or 128");
   constexpr int KS = D / 32;   // k-steps of the score product
   constexpr int DT = D / 16;   // 16-wide output tiles
   constexpr int KP = D + 16;   // LDS row pitch (halves): rows 32 bytes apart modulo 256
   constexpr int CPR = D / 8;   // 16-byte chunks per key row
-  constexpr int LPT = kKT * CPR / kThreads;  // chunks per thread per tile (K and V each)
-  static_assert(LPT >= 1, "tile too small");
+  constexpr int NCH = kKT * CPR;               // 16-byte chunks per tile (K and V each)
+  constexpr int LPT = (NCH + kAT - 1) / kAT;   // chunks per thread per tile
   __shared__ __attribute__((aligned(16))) u16 sK[kKT * KP];
   __shared__ __attribute__((aligned(16))) _Float16 sV[kKT * KP];
 
@@ -175,18 +179,22 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
     n = 0;
   };
 
-  uint4 pk[LPT], pv[LPT];
+  uint4 pk[2][LPT], pv[2][LPT];  // two register sets: tiles j and j + 1 in flight
   // this thread's 16-byte chunks of a key tile: row c / CPR, channels 8 (c % CPR) ..
   // (the same offsets for every tile; rows are contiguous within a segment)
   int coff[LPT], crow[LPT], loff[LPT];  // global (elements) and LDS (halves) offsets
 #pragma unroll
   for (int i = 0; i < LPT; ++i) {
-    const int c = tid + i * kThreads;
+    const int c0 = tid + i * kAT;
+    const int c = c0 < NCH ? c0 : 0;  // threads past the tile's chunks (d = 32) stay idle
     crow[i] = c / CPR;
     coff[i] = crow[i] * D + 8 * (c - crow[i] * CPR);
     loff[i] = crow[i] * KP + 8 * (c - crow[i] * CPR);
   }
-  auto fetch = [&](int j) {
+  // chunk slot i of this thread exists (always for d >= 64)
+  auto chunk_live = [&](int i) { return NCH % kAT == 0 || tid + i * kAT < NCH; };
+  auto fetch = [&](int j, auto set) {
+    constexpr int S = decltype(set)::value;
     const u16* kb;
     const u16* vb;
     int n;
@@ -194,15 +202,17 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
     if (n == kKT) {  // a full tile (every tile but a segment's last): no masks
 #pragma unroll
       for (int i = 0; i < LPT; ++i) {
-        pk[i] = *reinterpret_cast<const uint4*>(kb + coff[i]);
-        pv[i] = *reinterpret_cast<const uint4*>(vb + coff[i]);
+        if (!chunk_live(i)) continue;
+        pk[S][i] = *reinterpret_cast<const uint4*>(kb + coff[i]);
+        pv[S][i] = *reinterpret_cast<const uint4*>(vb + coff[i]);
       }
     } else {
 #pragma unroll
       for (int i = 0; i < LPT; ++i) {
+        if (!chunk_live(i)) continue;
         const bool ok = crow[i] < n;
-        pk[i] = ok ? *reinterpret_cast<const uint4*>(kb + coff[i]) : make_uint4(0, 0, 0, 0);
-        pv[i] = ok ? *reinterpret_cast<const uint4*>(vb + coff[i]) : make_uint4(0, 0, 0, 0);
+        pk[S][i] = ok ? *reinterpret_cast<const uint4*>(kb + coff[i]) : make_uint4(0, 0, 0, 0);
+        pv[S][i] = ok ? *reinterpret_cast<const uint4*>(vb + coff[i]) : make_uint4(0, 0, 0, 0);
       }
     }
     return n;
@@ -227,16 +237,22 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
   // 16 dt + 4 (j & 3) .. +3
   const int vrow = 4 * lg + (ln >> 2), vcol = 4 * (ln & 3);
 
-  int n_cur = all_tiles > 0 ? fetch(0) : 0;
-  for (int j = 0; j < all_tiles; ++j) {
+  // tiles alternate between the two register sets: set j % 2 holds tile j
+  // until it is staged, then receives tile j + 2
+  int n_t[2] = {0, 0};
+  if (all_tiles > 0) n_t[0] = fetch(0, std::integral_constant<int, 0>{});
+  if (all_tiles > 1) n_t[1] = fetch(1, std::integral_constant<int, 1>{});
+  auto tile_step = [&](int j, auto set) {
+    constexpr int S = decltype(set)::value;
     // ---- stage tile j: K as loaded, V converted to f16
 #pragma unroll
     for (int i = 0; i < LPT; ++i) {
-      *reinterpret_cast<uint4*>(sK + loff[i]) = pk[i];
+      if (!chunk_live(i)) continue;
+      *reinterpret_cast<uint4*>(sK + loff[i]) = pk[S][i];
       if constexpr (VF16) {
-        *reinterpret_cast<uint4*>(sV + loff[i]) = pv[i];
+        *reinterpret_cast<uint4*>(sV + loff[i]) = pv[S][i];
       } else {  // bf16 V -> f16
-        const uint32_t u[4] = {pv[i].x, pv[i].y, pv[i].z, pv[i].w};
+        const uint32_t u[4] = {pv[S][i].x, pv[S][i].y, pv[S][i].z, pv[S][i].w};
         f16x8 hv;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -246,9 +262,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
         *reinterpret_cast<f16x8*>(sV + loff[i]) = hv;
       }
     }
-    const int n_tile = n_cur;
+    const int n_tile = n_t[S];
     lds_barrier();
-    if (j + 1 < all_tiles) n_cur = fetch(j + 1);
+    if (j + 2 < all_tiles) n_t[S] = fetch(j + 2, set);
 
     // ---- S^T = K Q^T: 4 key sub-tiles x 2 query tiles
     f32x4 s[4][2];
@@ -319,6 +335,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
       lsum[1] = mfma_f16(ones, p[kp][1], lsum[1]);
     }
     lds_barrier();
+  };
+  for (int j = 0; j < all_tiles; j += 2) {
+    tile_step(j, std::integral_constant<int, 0>{});
+    if (j + 1 < all_tiles) tile_step(j + 1, std::integral_constant<int, 1>{});
   }
 
   // ---- O = O^T / l: lane (n, g) holds channels 16 dt + 4g + e of query n
@@ -335,7 +355,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
 
 template <bool VF16>
 static int launch_attn_v(const AttnArgs& a, int d, int out_dtype, hipStream_t stream) {
-  dim3 grid((unsigned)(a.H * a.tiles_per_head)), block(kThreads);
+  dim3 grid((unsigned)(a.H * a.tiles_per_head)), block(kAT);
 #define VDA_AT(DD)                                                                                         \
   if (d == DD) {                                                                                           \
     if (out_dtype == VDA_F32)                                                                              \

@@ -79,7 +79,7 @@ struct AttnArgs {
   int H, T, U, a, P, C, w, Nt;
   float scale;
   int v_f16;              // v, vt are f16 (else bf16)
-  int tiles_per_head, anchor_tiles, chunk_tiles;  // 128-query workgroups
+  int tiles_per_head, anchor_tiles, chunk_tiles;  // 256-query workgroups
 };
 
 int launch_stats(const PrepArgs& a, int d, bool in_f32, hipStream_t stream);
