@@ -20,8 +20,10 @@
 // frame, and that is what bounds a step, so N and B are kept to 2 bytes per
 // entry (f16).
 // The chain is bound by the latency of these per-frame operand loads, so
-// frames are prefetched three or four steps ahead into registers; the barriers wait
-// for LDS traffic only, so the global loads stay in flight across them.
+// frames are prefetched three or four steps ahead into registers, their
+// loads issued part by part between the k-steps of the current step's
+// MFMAs; the barriers wait for LDS traffic only, so the global loads stay in
+// flight across them.
 //
 // The same kernel also runs the scan at chunk level (method-steps section,
 // step (4): S_out = S_in M_chunk + J_chunk), in two launches:
@@ -109,7 +111,10 @@ __global__ __launch_bounds__(ScanShape<D>::NT) void scan_kernel(ScanPair p) {
   auto chunk_map = [&](int c) {
     return static_cast<char*>(a.chunks) + ((size_t)(2 * h + a.reverse) * a.C + c) * (size_t)(4 * D * D);
   };
-  auto load = [&](FrameRegs<D>& fr, int slot, const float* alpha_row) {
+  // A frame's operands come in four parts, so that a step can issue the
+  // loads of the frame PD steps ahead part by part between its own k-steps:
+  // part 0: N's k-slices 0, 1; part 1: k-slices 2, 3; part 2: B; part 3: alpha.
+  auto load_part = [&](FrameRegs<D>& fr, int slot, const float* alpha_row, int part) {
     const float* base = frames + (size_t)slot * slot_floats;
     const _Float16* nf = reinterpret_cast<const _Float16*>(base);
     const _Float16* bm = reinterpret_cast<const _Float16*>(base + D * D);
@@ -117,6 +122,7 @@ __global__ __launch_bounds__(ScanShape<D>::NT) void scan_kernel(ScanPair p) {
     // fragment order: one wavefront reads 64 consecutive 16-byte chunks
 #pragma unroll
     for (int kk = 0; kk < SS::KS; ++kk) {
+      if (kk / 2 != part) continue;
       if (lg < SS::LG) {
         const int chunk = ((ct * SS::KS + kk) * SS::LG + lg) * 16 + lr;
         fr.nk[kk] = reinterpret_cast<const f16x8*>(nf)[chunk];
@@ -125,24 +131,32 @@ __global__ __launch_bounds__(ScanShape<D>::NT) void scan_kernel(ScanPair p) {
         for (int e = 0; e < 8; ++e) fr.nk[kk][e] = (_Float16)0.f;
       }
     }
+    if (part == 2) {
 #pragma unroll
-    for (int q = 0; q < NQ; ++q) {
-      if constexpr (MODE == kSanaScan)
-        fr.b[q] = ba[((r0 / 16 + q) * SS::NW + ct) * 64 + lane];
-      else
-        fr.b[q] = *reinterpret_cast<const f16x4*>(bm + (size_t)(r0 + xrow + 16 * q) * D + xc0);
+      for (int q = 0; q < NQ; ++q) {
+        if constexpr (MODE == kSanaScan)
+          fr.b[q] = ba[((r0 / 16 + q) * SS::NW + ct) * 64 + lane];
+        else
+          fr.b[q] = *reinterpret_cast<const f16x4*>(bm + (size_t)(r0 + xrow + 16 * q) * D + xc0);
+      }
     }
-    fr.al = alpha_row ? *reinterpret_cast<const float4*>(alpha_row + xc0) : make_float4(1.f, 1.f, 1.f, 1.f);
+    if (part == 3)
+      fr.al = alpha_row ? *reinterpret_cast<const float4*>(alpha_row + xc0) : make_float4(1.f, 1.f, 1.f, 1.f);
+  };
+  auto load = [&](FrameRegs<D>& fr, int slot, const float* alpha_row) {
+#pragma unroll
+    for (int part = 0; part < 4; ++part) load_part(fr, slot, alpha_row, part);
   };
 
   // chunk scan: M_c as the B operand (fragment order, like N) and this
   // lane's accumulator-order J_c entries
-  auto load_map = [&](FrameRegs<D>& fr, int c) {
+  auto load_map_part = [&](FrameRegs<D>& fr, int c, int part) {
     const char* base = chunk_map(c);
     const _Float16* mf = reinterpret_cast<const _Float16*>(base);
     const f16x4* jf = reinterpret_cast<const f16x4*>(base + 2 * D * D);
 #pragma unroll
     for (int kk = 0; kk < SS::KS; ++kk) {
+      if (kk / 2 != part) continue;
       if (lg < SS::LG) {
         const int chunk = ((ct * SS::KS + kk) * SS::LG + lg) * 16 + lr;
         fr.nk[kk] = reinterpret_cast<const f16x8*>(mf)[chunk];
@@ -151,9 +165,15 @@ __global__ __launch_bounds__(ScanShape<D>::NT) void scan_kernel(ScanPair p) {
         for (int e = 0; e < 8; ++e) fr.nk[kk][e] = (_Float16)0.f;
       }
     }
+    if (part == 2) {
 #pragma unroll
-    for (int rt = 0; rt < SS::RTS; ++rt) fr.b[rt] = jf[((r0 / 16 + rt) * SS::NW + ct) * 64 + lane];
-    fr.al = make_float4(1.f, 1.f, 1.f, 1.f);
+      for (int rt = 0; rt < SS::RTS; ++rt) fr.b[rt] = jf[((r0 / 16 + rt) * SS::NW + ct) * 64 + lane];
+    }
+    if (part == 3) fr.al = make_float4(1.f, 1.f, 1.f, 1.f);
+  };
+  auto load_map = [&](FrameRegs<D>& fr, int c) {
+#pragma unroll
+    for (int part = 0; part < 4; ++part) load_map_part(fr, c, part);
   };
 
   // one frame write on the LDS state slice: S <- (S Diag(al) + B) N; a step
@@ -161,7 +181,12 @@ __global__ __launch_bounds__(ScanShape<D>::NT) void scan_kernel(ScanPair p) {
   // with logits the decay is sigmoid(al).  With post, B is added after the
   // product, S <- S Diag(al) N + B, B in accumulator order: one chunk step
   // S M_c + J_c (al = 1, fr from load_map) or one SANA-WM frame write.
-  auto step = [&](const FrameRegs<D>& fr, float* rec, bool live, bool logits, bool post) {
+  // next(part) issues part `part` of a later frame's loads; it is called
+  // after each k-step's MFMAs, so that those loads leave this wavefront
+  // while its MFMAs run instead of in one burst per step (eight wavefronts'
+  // bursts through one CU's vector-memory path otherwise hold up the last
+  // wavefront, and every barrier waits for it).
+  auto step = [&](const FrameRegs<D>& fr, float* rec, bool live, bool logits, bool post, auto&& next) {
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
       const int row = xrow + 16 * q;
@@ -218,7 +243,10 @@ __global__ __launch_bounds__(ScanShape<D>::NT) void scan_kernel(ScanPair p) {
         acc[rt] = mfma_f16(xh, fr.nk[kk], acc[rt]);
         acc[rt] = mfma_f16(xl, fr.nk[kk], acc[rt]);
       }
+      if (kk < 4) next(kk);
     }
+#pragma unroll
+    for (int part = SS::KS; part < 4; ++part) next(part);
 #pragma unroll
     for (int rt = 0; rt < SS::RTS; ++rt) {
       if (live) {
@@ -244,7 +272,7 @@ __global__ __launch_bounds__(ScanShape<D>::NT) void scan_kernel(ScanPair p) {
   if (!a.s_init && a.use_text) {
     FrameRegs<D> fr;
     load(fr, a.n, nullptr);
-    step(fr, nullptr, true, false, POST);  // S^T = (0 + B_T) N_T, SANA-WM: 0 T_T + B'_T
+    step(fr, nullptr, true, false, POST, [](int) {});  // S^T = (0 + B_T) N_T, SANA-WM: 0 T_T + B'_T
   }
   for (int i = tid; i < ROWS * D; i += SS::NT) {
     const float s0 = a.scale * sS[i];
@@ -267,8 +295,10 @@ __global__ __launch_bounds__(ScanShape<D>::NT) void scan_kernel(ScanPair p) {
 #pragma unroll
       for (int j = 0; j <= PD; ++j) {
         const int i = i0 + j;
+        // the maps' loads issued in one piece before the step (spreading them
+        // over the k-steps, as the frame scan does, measured slower here)
         load_map(fr[(j + PD) % (PD + 1)], slot_of(cl(i + PD)));
-        step(fr[j], i < n ? states_h + (size_t)(i + 1) * D * D : nullptr, i < n, false, true);
+        step(fr[j], i < n ? states_h + (size_t)(i + 1) * D * D : nullptr, i < n, false, true, [](int) {});
       }
     }
     return;
@@ -296,8 +326,10 @@ __global__ __launch_bounds__(ScanShape<D>::NT) void scan_kernel(ScanPair p) {
 #pragma unroll
     for (int j = 0; j <= PD; ++j) {
       const int i = i0 + j;
-      load(fr[(j + PD) % (PD + 1)], slot_of(cl(i + PD)), alpha_of(cl(i + PD)));
-      step(fr[j], rec_of(i), i < n, a.prep != 0, POST);
+      const int ns = slot_of(cl(i + PD));
+      const float* na = alpha_of(cl(i + PD));
+      step(fr[j], rec_of(i), i < n, a.prep != 0, POST,
+           [&](int part) { load_part(fr[(j + PD) % (PD + 1)], ns, na, part); });
     }
   }
 }
