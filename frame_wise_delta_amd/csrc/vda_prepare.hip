@@ -189,6 +189,17 @@ __device__ __forceinline__ f32x4 tr_get(const float* buf, int n, int g) {
 
 }  // namespace
 
+// Row tile m of wavefront `wave` in the statistics kernel.  With eight row
+// tiles (d = 128) the wavefronts take the pairs {w, 7 - w}, so each one owns
+// exactly nine of the 36 upper-triangle tiles of the symmetric A (tile (i, j),
+// j >= i, is computed by the wavefront owning row tile i); otherwise row
+// tiles wave, wave + 4, ...
+template <int RT>
+__device__ __forceinline__ int row_tile(int wave, int m) {
+  if constexpr (RT == 8) return m == 0 ? wave : RT - 1 - wave;
+  return wave + 4 * m;
+}
+
 // Row pitch (floats) of the 64-row float32 staging buffers: d + 4 puts the
 // four 16-lane groups of an accumulator tile (rows 4 apart) on disjoint banks.
 template <int D>
@@ -204,12 +215,12 @@ __device__ __forceinline__ void store_rows(const f32x4 (&acc)[NRW][D / 16], floa
   constexpr int SP = kSP<D>;
 #pragma unroll
   for (int m = 0; m < NRW; ++m) {
-    const int ri = wave + 4 * m;
+    const int ri = row_tile<RT>(wave, m);  // within rows 64 m .. 64 m + 63
     if (ri < RT) {
 #pragma unroll
       for (int cj = 0; cj < RT; ++cj)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) stage[(16 * wave + 4 * lg + e) * SP + 16 * cj + lr] = acc[m][cj][e];
+        for (int e = 0; e < 4; ++e) stage[(16 * (ri - 4 * m) + 4 * lg + e) * SP + 16 * cj + lr] = acc[m][cj][e];
     }
     lds_barrier();
     const int rows = (D - 64 * m) < 64 ? (D - 64 * m) : 64;
@@ -233,7 +244,7 @@ __global__ __launch_bounds__(kThreads, 2) void stats_kernel(PrepArgs args) {
   __shared__ __attribute__((aligned(16))) char smem[kBytes];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lr = lane & 15, lg = lane >> 4;
 
   const int h = blockIdx.x / args.cnt;
@@ -335,7 +346,7 @@ __global__ __launch_bounds__(kThreads, 2) void stats_kernel(PrepArgs args) {
       f16x8 aK[NRW], aV[NRW];
 #pragma unroll
       for (int m = 0; m < NRW; ++m) {
-        const int ri = wave + 4 * m;
+        const int ri = row_tile<RT>(wave, m);
         if (ri < RT) {
           aK[m] = *reinterpret_cast<const f16x8*>(sK + tile_off(16 * ri + lr, grp));
           aV[m] = *reinterpret_cast<const f16x8*>(sV + tile_off(16 * ri + lr, grp));
@@ -346,8 +357,9 @@ __global__ __launch_bounds__(kThreads, 2) void stats_kernel(PrepArgs args) {
         const f16x8 b = *reinterpret_cast<const f16x8*>(sBK + tile_off(16 * cj + lr, grp));
 #pragma unroll
         for (int m = 0; m < NRW; ++m) {
-          if (wave + 4 * m < RT) {
-            accA[m][cj] = mfma_f16(aK[m], b, accA[m][cj]);
+          const int ri = row_tile<RT>(wave, m);
+          if (ri < RT) {
+            if (cj >= ri) accA[m][cj] = mfma_f16(aK[m], b, accA[m][cj]);  // upper triangle only
             accB[m][cj] = mfma_f16(aV[m], b, accB[m][cj]);
           }
         }
@@ -368,7 +380,7 @@ __global__ __launch_bounds__(kThreads, 2) void stats_kernel(PrepArgs args) {
   // A where N will go: the upper-triangle tiles, straight from the accumulators
 #pragma unroll
   for (int m = 0; m < NRW; ++m) {
-    const int ri = wave + 4 * m;
+    const int ri = row_tile<RT>(wave, m);
     if (ri < RT) {
 #pragma unroll
       for (int cj = 0; cj < RT; ++cj)
