@@ -247,10 +247,35 @@ __global__ __launch_bounds__(kThreads, GATED ? 3 : 2) void readout_kernel(ReadAr
   };
   fetch(0);
 
-  // ---- states and bridges for this frame
+  // ---- states and bridges for this frame; without the epilogue this lane's
+  // entries of the two states are loaded first, so that their latency
+  // overlaps the bridges' (the bridges' alpha loads and the states' otherwise
+  // make two round trips to memory in a row before the first product; the
+  // gated launch, at three workgroups per CU, has no registers to hold them)
   const int f = t - a.a;
   const float* sf;
   const float* sr = nullptr;
+  float4 rf[NVT][KS][2], rr[NVT][KS][2];
+  auto load_states = [&]() {
+    if constexpr (GATED) return;
+#pragma unroll
+    for (int i = 0; i < NVT; ++i) {
+      const int vt = wave + 4 * i;
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) {
+        const int k0 = 32 * kk + 8 * lg;
+        if (vt < VT && k0 < D) {
+          const size_t idx = (size_t)chan(wave, i, lr) * D + k0;
+          rf[i][kk][0] = *reinterpret_cast<const float4*>(sf + idx);
+          rf[i][kk][1] = *reinterpret_cast<const float4*>(sf + idx + 4);
+          if (sr) {
+            rr[i][kk][0] = *reinterpret_cast<const float4*>(sr + idx);
+            rr[i][kk][1] = *reinterpret_cast<const float4*>(sr + idx + 4);
+          }
+        }
+      }
+    }
+  };
   const float* alpha_h = a.alpha + (size_t)h * a.T * D;
   if (a.w >= 0) {
     const int c = f / a.P;
@@ -260,6 +285,7 @@ __global__ __launch_bounds__(kThreads, GATED ? 3 : 2) void readout_kernel(ReadAr
     const int we = a.a + a.P * (hi + 1) - 1;
     sf = a.sf + ((size_t)h * a.count + lo) * D * D;
     sr = a.sr + ((size_t)h * a.count + (a.C - 1 - hi)) * D * D;
+    load_states();  // in flight while the bridges are formed
     // thread k < D: forward bridge of channel k; D <= k < 2D: reverse bridge
     for (int k2 = tid; k2 < 2 * D; k2 += kThreads) {
       const bool rev = k2 >= D;
@@ -283,6 +309,7 @@ __global__ __launch_bounds__(kThreads, GATED ? 3 : 2) void readout_kernel(ReadAr
     }
   } else {
     sf = a.sf + ((size_t)h * a.count + f + 1) * D * D;
+    load_states();
     for (int k = tid; k < D; k += kThreads) {
       sBf[k] = 1.f;
       sBr[k] = 0.f;
@@ -301,13 +328,13 @@ __global__ __launch_bounds__(kThreads, GATED ? 3 : 2) void readout_kernel(ReadAr
       float x[8];
       if (vt < VT && k0 < D) {
         const size_t idx = (size_t)chan(wave, i, lr) * D + k0;
-        const float4 f0 = *reinterpret_cast<const float4*>(sf + idx);
-        const float4 f1 = *reinterpret_cast<const float4*>(sf + idx + 4);
+        const float4 f0 = GATED ? *reinterpret_cast<const float4*>(sf + idx) : rf[i][kk][0];
+        const float4 f1 = GATED ? *reinterpret_cast<const float4*>(sf + idx + 4) : rf[i][kk][1];
         x[0] = f0.x * sBf[k0]; x[1] = f0.y * sBf[k0 + 1]; x[2] = f0.z * sBf[k0 + 2]; x[3] = f0.w * sBf[k0 + 3];
         x[4] = f1.x * sBf[k0 + 4]; x[5] = f1.y * sBf[k0 + 5]; x[6] = f1.z * sBf[k0 + 6]; x[7] = f1.w * sBf[k0 + 7];
         if (sr) {
-          const float4 r0 = *reinterpret_cast<const float4*>(sr + idx);
-          const float4 r1 = *reinterpret_cast<const float4*>(sr + idx + 4);
+          const float4 r0 = GATED ? *reinterpret_cast<const float4*>(sr + idx) : rr[i][kk][0];
+          const float4 r1 = GATED ? *reinterpret_cast<const float4*>(sr + idx + 4) : rr[i][kk][1];
           x[0] = fmaf(r0.x, sBr[k0], x[0]); x[1] = fmaf(r0.y, sBr[k0 + 1], x[1]);
           x[2] = fmaf(r0.z, sBr[k0 + 2], x[2]); x[3] = fmaf(r0.w, sBr[k0 + 3], x[3]);
           x[4] = fmaf(r1.x, sBr[k0 + 4], x[4]); x[5] = fmaf(r1.y, sBr[k0 + 5], x[5]);
