@@ -84,7 +84,7 @@ __global__ __launch_bounds__(kAT, 1) void attn_kernel(AttnArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int ln = lane & 15, lg = lane >> 4;
 
-  // ---- which head, query block and 128-query tile
+  // ---- which head, query block and 256-query tile
   int L = xcd_block(blockIdx.x, gridDim.x);
   const int h = L / a.tiles_per_head;
   L -= h * a.tiles_per_head;
