@@ -43,9 +43,10 @@ Readings of points the page leaves open:
   read by the linear branch (their output rows are zero).
 * With ``window = -1`` (no exclusion) the readout of frame t is S^f_t q where
   S^f_t includes frame t's own write.
-* Softmax branch: scores are scaled by 1/sqrt(d); the query and key
-  projections arrive after the branch's QK normalisation and rotary
-  position encoding, which need weights and positions and are not part of it.
+* Softmax branch: scores are scaled by 1/sqrt(d) unless a scale is given;
+  the query and key projections arrive after the branch's QK normalisation
+  and rotary position encoding, which need weights and positions and are not
+  part of it.
 * Prep: q and k are normalised as x / sqrt(||x||^2 + eps) per token
   (eps = 1e-6); the write gate is beta = sigmoid(logit) per token and the
   decay gate alpha = sigmoid(logit) per frame and channel.
@@ -315,17 +316,22 @@ def softmax_key_frames(frames: int, chunk: int, window: int, anchors: int):
     return out
 
 
-def softmax_branch(q, k, v, kt, vt, frames, chunk, window, anchors, scale=None):
+def softmax_branch(q, k, v, kt, vt, frames, chunk, window, anchors, scale=None, query_frames=None):
     """Softmax branch of the hybrid attention for one head [VDN 核心方法 ¶1;
     方法步骤详情 step (1)]: every query token of frame t attends with
     softmax(q K^T * scale) to the tokens of its visible key frames
     (``softmax_key_frames``) and to all text tokens, which are always
     visible.  q, k, v [T, U, d]; kt, vt [N_text, d] or None; scale defaults
-    to 1 / sqrt(d).  Row by row, in float64."""
+    to 1 / sqrt(d).  Row by row, in float64.  ``query_frames`` (default: all)
+    lists the query frames to compute; the rows of the other frames are
+    left zero."""
     T, U, d = q.shape
     scale = 1.0 / np.sqrt(d) if scale is None else scale
     O = np.zeros((T, U, v.shape[-1]))
+    wanted = set(range(T)) if query_frames is None else set(query_frames)
     for t, fr in enumerate(softmax_key_frames(frames, chunk, window, anchors)):
+        if t not in wanted:
+            continue
         K = k[fr].reshape(-1, d)
         V = v[fr].reshape(-1, v.shape[-1])
         if kt is not None and len(kt):
@@ -411,7 +417,8 @@ def run_head(frames, chunk, window, anchors, q, k, v, beta, alpha,
 
 
 def rel_l2(x, ref) -> float:
-    """||x - ref||_2 / ||ref||_2 in float64."""
+    """||x - ref||_2 / ||ref||_2 in float64, both norms taken over every
+    element (all axes); a zero reference gives ||x - ref||_2."""
     x = np.asarray(x, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
     den = np.linalg.norm(ref.ravel())

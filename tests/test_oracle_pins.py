@@ -713,3 +713,92 @@ def test_newton_schulz_residual_is_a_power_of_the_start():
         assert np.linalg.norm(np.eye(d) - G @ X, 2) <= r ** (2 ** k) * (1 + 1e-9) + 1e-12
         assert r ** (2 ** k) <= tol < r ** (2 ** (k - 1))
         assert np.abs(X - X.T).max() <= 1e-12
+
+
+# ------------------------------------------------- the comparison and scale --
+
+def test_rel_l2_hand_values():
+    """The measure every parity test uses: ||x - ref|| / ||ref||, with both
+    norms over all elements.  ref = (3, 4), x = (3, 5): |x - ref| = 1 and
+    |ref| = 5, so 0.2; swapping the roles gives 1 / sqrt(34)."""
+    assert orc.rel_l2(np.array([3.0, 5.0]), np.array([3.0, 4.0])) == pytest.approx(0.2, rel=1e-15)
+    assert orc.rel_l2(np.array([3.0, 4.0]), np.array([3.0, 5.0])) == pytest.approx(1 / np.sqrt(34), rel=1e-15)
+    assert orc.rel_l2(np.array([3.0, 4.0]), np.array([3.0, 4.0])) == 0.0
+
+
+def test_rel_l2_runs_over_every_axis():
+    """A 2 x 3 x 4 reference of ones has norm sqrt(24); one element off by
+    0.5 gives 0.5 / sqrt(24) wherever it sits (a norm per row or per slice,
+    or a ravel of one axis only, would give another value), and a uniform
+    relative error e of every element gives e."""
+    ref = np.ones((2, 3, 4))
+    for idx in [(0, 0, 0), (1, 2, 3), (1, 0, 2)]:
+        x = ref.copy()
+        x[idx] += 0.5
+        assert orc.rel_l2(x, ref) == pytest.approx(0.5 / np.sqrt(24), rel=1e-14)
+    g = np.random.default_rng(9)
+    ref = g.standard_normal((3, 5, 7))
+    assert orc.rel_l2(ref * (1 + 3e-4), ref) == pytest.approx(3e-4, rel=1e-9)
+    assert orc.rel_l2(-ref, ref) == pytest.approx(2.0, rel=1e-14)
+
+
+def test_rel_l2_zero_reference_and_dtypes():
+    """A zero reference leaves the absolute norm; 16-bit and integer inputs
+    are compared in float64."""
+    assert orc.rel_l2(np.array([0.0, 3.0, 4.0]), np.zeros(3)) == pytest.approx(5.0, rel=1e-15)
+    assert orc.rel_l2(np.array([3, 5], dtype=np.int32), np.array([3.0, 4.0], dtype=np.float16)) \
+        == pytest.approx(0.2, rel=1e-15)
+
+
+def _two_key_case():
+    """One frame (no anchors, one chunk) of two tokens in d = 2: keys (1, 0)
+    and (0, 0), values (1, 0) and (0, 1); query 0 is (1, 0), query 1 is 0."""
+    q = np.array([[[1.0, 0.0], [0.0, 0.0]]])
+    k = np.array([[[1.0, 0.0], [0.0, 0.0]]])
+    v = np.array([[[1.0, 0.0], [0.0, 1.0]]])
+    return q, k, v
+
+
+@pytest.mark.parametrize("scale", [2.0, 0.5, None])
+def test_softmax_branch_scale_hand_worked(scale):
+    """Query 0 scores s = scale * (1, 0).(1, 0) against key 0 and 0 against
+    key 1, so its weights are e^s / (1 + e^s) and 1 / (1 + e^s) and its
+    output is that pair (the values are the unit vectors); query 1 scores 0
+    against both and averages them.  The default scale is 1 / sqrt(d) =
+    1 / sqrt(2).  Dropping, squaring or inverting the scale changes
+    query 0's output."""
+    q, k, v = _two_key_case()
+    O = orc.softmax_branch(q, k, v, None, None, 1, 1, 0, 0, scale)
+    s = 1 / np.sqrt(2) if scale is None else scale
+    w = np.exp(s) / (1 + np.exp(s))
+    np.testing.assert_allclose(O[0, 0], [w, 1 - w], rtol=1e-14)
+    np.testing.assert_allclose(O[0, 1], [0.5, 0.5], rtol=1e-14)
+    for wrong in (1.0, s * s, 1 / s):
+        wx = np.exp(wrong) / (1 + np.exp(wrong))
+        assert abs(wx - w) > 1e-3
+
+
+def test_softmax_branch_text_tokens_join_the_softmax():
+    """Adding one text token with key (1, 0) and value (0, 0) to the same
+    frame: query 0 now weighs e^s, 1, e^s over keys 0, 1 and the text key,
+    so its output is (e^s, 1) / (2 e^s + 1)."""
+    q, k, v = _two_key_case()
+    s = 0.75
+    O = orc.softmax_branch(q, k, v, np.array([[1.0, 0.0]]), np.array([[0.0, 0.0]]), 1, 1, 0, 0, s)
+    np.testing.assert_allclose(O[0, 0], np.array([np.exp(s), 1.0]) / (2 * np.exp(s) + 1), rtol=1e-14)
+
+
+def test_softmax_branch_query_frame_subset():
+    """Computing only some query frames gives exactly those rows of the full
+    result and zeros elsewhere."""
+    g = np.random.default_rng(12)
+    T, U, d = 12, 3, 8
+    q, k, v = (g.standard_normal((T, U, d)) for _ in range(3))
+    kt, vt = g.standard_normal((2, d)), g.standard_normal((2, d))
+    full = orc.softmax_branch(q, k, v, kt, vt, T, 5, 1, 1)
+    part = orc.softmax_branch(q, k, v, kt, vt, T, 5, 1, 1, query_frames=[0, 4, 11])
+    for t in range(T):
+        if t in (0, 4, 11):
+            assert np.array_equal(part[t], full[t])
+        else:
+            assert not part[t].any()
