@@ -169,27 +169,36 @@ int vda_index_map(const vda_desc* desc, int32_t* chunk_rows, int32_t* frame_chun
   const int w = s.w < 0 ? 0 : s.w;
   if (chunk_rows) {
     for (int c = 0; c < s.C; ++c) {
-      const int lo = c - w > 0 ? c - w : 0;
-      const int hi = c + w < s.C - 1 ? c + w : s.C - 1;
-      int we = s.a + s.P * (hi + 1) - 1;
-      if (we > s.a + s.n - 1) we = s.a + s.n - 1;  // ragged last chunk
+      const vda::ChunkWindow cw = vda::chunk_window(c, s.C, w, s.P, s.a, s.n);
       int32_t* r = chunk_rows + 7 * (size_t)c;
       r[0] = c;
-      r[1] = lo;
-      r[2] = hi;
-      r[3] = s.a + s.P * lo;
-      r[4] = we;
-      r[5] = lo;
-      r[6] = s.C - 1 - hi;
+      r[1] = cw.lo;
+      r[2] = cw.hi;
+      r[3] = cw.ws;
+      r[4] = cw.we;
+      r[5] = cw.F;
+      r[6] = cw.R;
     }
   }
   if (frame_chunk) {
-    for (int t = 0; t < s.T; ++t) {
-      const int f = t - s.a;
-      frame_chunk[t] = (f >= 0 && f < s.n) ? f / s.P : -1;
-    }
+    for (int t = 0; t < s.T; ++t) frame_chunk[t] = vda::frame_chunk_of(t, s.a, s.n, s.P);
   }
   return ok();
+}
+
+int vda_index_map_device(const vda_desc* desc, int32_t* chunk_rows, int32_t* frame_chunk, void* stream) {
+  Shape s;
+  int rc = check_desc(desc, &s);
+  if (rc) return rc;
+  if ((!chunk_rows && s.C > 0) || (!frame_chunk && s.T > 0))
+    return fail(VDA_ERR_NULL, "chunk_rows or frame_chunk is NULL");
+  if (!aligned16(chunk_rows) || !aligned16(frame_chunk))
+    return fail(VDA_ERR_ALIGN, "chunk_rows and frame_chunk need 16-byte alignment");
+  rc = check_device();
+  if (rc) return rc;
+  vda::launch_index_map(s.C, s.T, s.w < 0 ? 0 : s.w, s.P, s.a, s.n, chunk_rows, frame_chunk,
+                        static_cast<hipStream_t>(stream));
+  return launch_status();
 }
 
 }  // extern "C"
@@ -506,9 +515,14 @@ int vda_softmax_branch(const vda_desc* desc, const void* q, const void* k, const
   return launch_status();
 }
 
-int vda_forward(const vda_desc* desc, const void* q, const void* k, const void* v, const float* beta,
-                const float* alpha, const void* k_text, const void* v_text, const float* beta_text, void* ws,
-                size_t ws_size, float* states_fwd, float* states_rev, void* out, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The whole path on one stream.
+int forward_impl(const vda_desc* desc, const void* q, const void* k, const void* v, const float* beta,
+                 const float* alpha, const void* k_text, const void* v_text, const float* beta_text, void* ws,
+                 size_t ws_size, float* states_fwd, float* states_rev, void* out, void* stream) {
   Shape s;
   vda::PrepArgs pa;
   vda::ScanPair sp;
@@ -540,6 +554,17 @@ int vda_forward(const vda_desc* desc, const void* q, const void* k, const void* 
   vda::launch_scan(sp, s.d, st);  // both directions in one launch
   if (any) vda::launch_readout(qa, s.d, desc->in_dtype, desc->out_dtype, st);
   return launch_status();
+}
+
+}  // namespace
+
+extern "C" {
+
+int vda_forward(const vda_desc* desc, const void* q, const void* k, const void* v, const float* beta,
+                const float* alpha, const void* k_text, const void* v_text, const float* beta_text, void* ws,
+                size_t ws_size, float* states_fwd, float* states_rev, void* out, void* stream) {
+  return forward_impl(desc, q, k, v, beta, alpha, k_text, v_text, beta_text, ws, ws_size, states_fwd, states_rev,
+                      out, stream);
 }
 
 int vda_device_status(const vda_desc* desc, const void* ws, void* stream, int32_t* flags) {

@@ -114,10 +114,9 @@ __global__ __launch_bounds__(kAT, 1) void attn_kernel(AttnArgs a) {
     seg_e[0] = a.T * a.U;
     nseg = 1;
   } else {
-    const int lo = qb - a.w > 0 ? qb - a.w : 0;
-    const int hi = qb + a.w < a.C - 1 ? qb + a.w : a.C - 1;
-    seg_s[0] = (a.a + a.P * lo) * a.U;
-    seg_e[0] = (a.a + a.P * (hi + 1)) * a.U;
+    const ChunkWindow cw = chunk_window(qb, a.C, a.w, a.P, a.a, a.T - 2 * a.a);
+    seg_s[0] = cw.ws * a.U;
+    seg_e[0] = (cw.we + 1) * a.U;
     nseg = 1;
     if (a.a) {
       seg_s[1] = 0;

@@ -99,6 +99,37 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
+// ------------------------------------------------------------ index maps --
+// Window of query chunk c ("Video DeltaNet: A Video-Native Hybrid Attention
+// for Livestream Video Generation", core-method section, paragraph 1: a
+// bidirectional window aligned to the 5-frame chunks; the forward scan reads
+// the history before it, the reverse scan the history after it): window
+// chunks lo..hi = c-w..c+w clipped to [0, C-1]; first and last window frame
+// ws, we (we clipped to the last scanned frame); the forward state index
+// F = lo (chunks wholly before ws) and the reverse state index R = C-1-hi
+// (chunks wholly after we).  a = 1 with anchor frames, n scanned frames,
+// P frames per chunk.  The host's index map, the readout and the softmax
+// branch all take their windows from this one function.
+struct ChunkWindow {
+  int lo, hi, ws, we, F, R;
+};
+__host__ __device__ inline ChunkWindow chunk_window(int c, int C, int w, int P, int a, int n) {
+  ChunkWindow r;
+  r.lo = c - w > 0 ? c - w : 0;
+  r.hi = c + w < C - 1 ? c + w : C - 1;
+  r.ws = a + P * r.lo;
+  r.we = a + P * (r.hi + 1) - 1;
+  if (r.we > a + n - 1) r.we = a + n - 1;
+  r.F = r.lo;
+  r.R = C - 1 - r.hi;
+  return r;
+}
+// Chunk of frame t (-1 for the anchor frames).
+__host__ __device__ inline int frame_chunk_of(int t, int a, int n, int P) {
+  const int f = t - a;
+  return (f >= 0 && f < n) ? f / P : -1;
+}
+
 // Element type tags for the input / output tensors.
 struct InF32 { typedef float T; static constexpr int bytes = 4; };
 struct InBF16 { typedef u16 T; static constexpr int bytes = 2; };

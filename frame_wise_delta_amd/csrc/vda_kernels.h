@@ -94,5 +94,9 @@ int launch_readout(const ReadArgs& a, int d, int in_dtype, int out_dtype, hipStr
 // The readout with the RMSNorm + sigmoid-gate epilogue (a.gate, a.normw, a.eps).
 int launch_readout_gated(const ReadArgs& a, int d, int in_dtype, int out_dtype, hipStream_t stream);
 int launch_attn(const AttnArgs& a, int d, int out_dtype, hipStream_t stream);
+// The index maps computed on the device by chunk_window / frame_chunk_of,
+// the functions the readout and attention kernels use.
+void launch_index_map(int C, int T, int w, int P, int a, int n, int32_t* rows, int32_t* frame_chunk,
+                      hipStream_t stream);
 
 }  // namespace vda

@@ -278,13 +278,10 @@ __global__ __launch_bounds__(kThreads, GATED ? 3 : 2) void readout_kernel(ReadAr
   };
   const float* alpha_h = a.alpha + (size_t)h * a.T * D;
   if (a.w >= 0) {
-    const int c = f / a.P;
-    const int lo = c - a.w > 0 ? c - a.w : 0;
-    const int hi = c + a.w < a.C - 1 ? c + a.w : a.C - 1;
-    const int ws = a.a + a.P * lo;
-    const int we = a.a + a.P * (hi + 1) - 1;
-    sf = a.sf + ((size_t)h * a.count + lo) * D * D;
-    sr = a.sr + ((size_t)h * a.count + (a.C - 1 - hi)) * D * D;
+    const ChunkWindow cw = chunk_window(frame_chunk_of(t, a.a, a.n, a.P), a.C, a.w, a.P, a.a, a.n);
+    const int ws = cw.ws, we = cw.we;
+    sf = a.sf + ((size_t)h * a.count + cw.F) * D * D;
+    sr = a.sr + ((size_t)h * a.count + cw.R) * D * D;
     load_states();  // in flight while the bridges are formed
     // thread k < D: forward bridge of channel k; D <= k < 2D: reverse bridge
     for (int k2 = tid; k2 < 2 * D; k2 += kThreads) {
@@ -524,6 +521,33 @@ __global__ __launch_bounds__(kThreads, GATED ? 3 : 2) void readout_kernel(ReadAr
     }
     lds_barrier();
   }
+}
+
+// Index maps on the device: thread c < C writes row c, thread C + t < C + T
+// the chunk of frame t.
+__global__ void index_map_kernel(int C, int T, int w, int P, int a, int n, int32_t* rows, int32_t* fc) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < C) {
+    const ChunkWindow cw = chunk_window(i, C, w, P, a, n);
+    int32_t* r = rows + 7 * (size_t)i;
+    r[0] = i;
+    r[1] = cw.lo;
+    r[2] = cw.hi;
+    r[3] = cw.ws;
+    r[4] = cw.we;
+    r[5] = cw.F;
+    r[6] = cw.R;
+  } else if (i < C + T) {
+    fc[i - C] = frame_chunk_of(i - C, a, n, P);
+  }
+}
+
+void launch_index_map(int C, int T, int w, int P, int a, int n, int32_t* rows, int32_t* frame_chunk,
+                      hipStream_t stream) {
+  const int total = C + T;
+  if (total <= 0) return;
+  hipLaunchKernelGGL(index_map_kernel, dim3((total + 255) / 256), dim3(256), 0, stream, C, T, w, P, a, n, rows,
+                     frame_chunk);
 }
 
 template <bool GATED>

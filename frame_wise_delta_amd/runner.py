@@ -72,7 +72,7 @@ def allocate(desc: vda.vda_desc, out_dtype: str, device="cuda") -> Buffers:
 
 class Forward:
     """Enqueues the whole hot path with one vda_forward call (the library
-    pipelines it over its own side stream)."""
+    enqueues every kernel on the caller's stream, in order)."""
 
     def __init__(self, desc: vda.vda_desc, dev: DeviceInputs, bufs: Buffers):
         import torch
@@ -86,8 +86,9 @@ class Forward:
 
 
 class Path:
-    """Enqueues the whole hot path step by step; the two scans run on two
-    streams."""
+    """Enqueues the whole hot path step by step, one entry point per step;
+    the reverse scan runs on a second stream, concurrently with the forward
+    scan."""
 
     def __init__(self, desc: vda.vda_desc, dev: DeviceInputs, bufs: Buffers, s_init=None):
         import torch

@@ -13,7 +13,9 @@ import os
 from ctypes import POINTER, c_char_p, c_float, c_int, c_int32, c_size_t, c_uint32, c_void_p
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libvda.so")
+# VDA_LIBRARY names another build of the same library (the CPU tests load the
+# host-sanitizer build that way); the default is the in-tree libvda.so
+LIB_PATH = os.environ.get("VDA_LIBRARY") or os.path.join(_PKG, "libvda.so")
 
 VDA_OK = 0
 VDA_ERR_NULL = -1
@@ -35,7 +37,7 @@ VDA_DEV_NONFINITE, VDA_DEV_PIVOT = 1, 2
 
 DTYPES = {"f32": VDA_F32, "bf16": VDA_BF16, "f16": VDA_F16}
 
-EXPORTS = ("vda_workspace_bytes", "vda_state_count", "vda_index_map", "vda_prepare_frames",
+EXPORTS = ("vda_workspace_bytes", "vda_state_count", "vda_index_map", "vda_index_map_device", "vda_prepare_frames",
            "vda_frame_stats", "vda_factor_frames", "vda_compose_chunks", "vda_scan_fwd", "vda_scan_rev", "vda_scan_bidir",
            "vda_readout", "vda_readout_gated", "vda_softmax_branch", "vda_forward", "vda_device_status",
            "vda_status_string", "vda_last_error")
@@ -74,6 +76,7 @@ def load(path: str | None = None):
         "vda_workspace_bytes": [D, POINTER(c_size_t)],
         "vda_state_count": [D, POINTER(c_int32)],
         "vda_index_map": [D, c_void_p, c_void_p],
+        "vda_index_map_device": [D, c_void_p, c_void_p, c_void_p],
         "vda_prepare_frames": [D, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                c_void_p, c_size_t, c_void_p],
         "vda_frame_stats": [D, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
@@ -172,6 +175,13 @@ def vda_index_map(desc: vda_desc):
     _check(load().vda_index_map(ctypes.byref(desc), rows.ctypes.data if rows.size else None,
                                 fc.ctypes.data if fc.size else None))
     return rows, fc
+
+
+def vda_index_map_device(desc: vda_desc, chunk_rows, frame_chunk, stream=None):
+    """The maps computed on the device into int32 device tensors
+    chunk_rows [C, 7] and frame_chunk [T]."""
+    _check(load().vda_index_map_device(ctypes.byref(desc), _ptr(chunk_rows) if chunk_rows.numel() else None,
+                                       _ptr(frame_chunk) if frame_chunk.numel() else None, _stream(stream)))
 
 
 def vda_prepare_frames(desc, k, v, beta, k_text, v_text, beta_text, ws, ws_bytes=None, stream=None):

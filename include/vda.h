@@ -143,6 +143,13 @@ int vda_state_count(const vda_desc* desc, int32_t* count);
  * Either pointer may be NULL to skip that output. */
 int vda_index_map(const vda_desc* desc, int32_t* chunk_rows, int32_t* frame_chunk);
 
+/* The same maps computed on the device, by the device code the readout and
+ * the softmax branch take their windows from (a check that the two copies
+ * of the map arithmetic agree).  chunk_rows [C][7] and frame_chunk [T] are
+ * 16-byte aligned device pointers (each may be NULL only when its size is
+ * 0); enqueues one small kernel on `stream`. */
+int vda_index_map_device(const vda_desc* desc, int32_t* chunk_rows, int32_t* frame_chunk, void* stream);
+
 /* Frame statistics and factorisation [VDN 方法步骤详情 step (3)]: for every
  * head and every scanned frame t (and the text tokens when text_tokens > 0)
  * computes A_t and B_t over the frame's U tokens, factorises I + A_t and

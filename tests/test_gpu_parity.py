@@ -109,7 +109,7 @@ def test_fused_entry_point_equals_step_by_step():
 
 
 @pytest.mark.parametrize("frames,d,window,text,anchors", [
-    (32, 64, 1, 16, 1),    # C = 6: three prepare groups from each end
+    (32, 64, 1, 16, 1),    # C = 6
     (27, 32, 1, 16, 1),    # C = 5: odd, the reverse half is one chunk shorter
     (7, 32, 1, 16, 1),     # C = 1
     (42, 128, 2, 0, 1),    # C = 8, wide window, no text
@@ -117,9 +117,9 @@ def test_fused_entry_point_equals_step_by_step():
     (23, 64, -1, 16, 0),   # per-frame readout, ragged group sizes
 ])
 def test_fused_schedule_equals_step_by_step(frames, d, window, text, anchors):
-    """vda_forward (the reverse scan on its own stream) gives the same bits
-    as the four calls in order, over chunk counts, windows, text and anchor
-    settings."""
+    """vda_forward (every kernel on the caller's stream) gives the same bits
+    as the step calls (the reverse scan on a second stream), over chunk
+    counts, windows, text and anchor settings."""
     import torch
     cfg = inp.scaled(inp.CONFIG_BY_NAME["h3"], heads=3, d=d, frames=frames, tokens=64, window=window,
                      text_tokens=text, anchors=anchors)
