@@ -519,7 +519,8 @@ int vda_softmax_branch(const vda_desc* desc, const void* q, const void* k, const
 
 namespace {
 
-// The whole path on one stream.
+// The whole path on one stream (vda_forward, and vda_forward_noalloc with
+// its own workspace).
 int forward_impl(const vda_desc* desc, const void* q, const void* k, const void* v, const float* beta,
                  const float* alpha, const void* k_text, const void* v_text, const float* beta_text, void* ws,
                  size_t ws_size, float* states_fwd, float* states_rev, void* out, void* stream) {
@@ -556,6 +557,33 @@ int forward_impl(const vda_desc* desc, const void* q, const void* k, const void*
   return launch_status();
 }
 
+// Workspace of vda_forward_noalloc: a file-scope device array, one copy per
+// device, held from the library's load until the process ends.  In host
+// code `scratch` names a host-side stand-in, so its device address is taken
+// once per device with hipGetSymbolAddress (with that device current) and
+// only that address is handed to kernels.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_addr[64];  // device address of `scratch`, per device index
+
+int scratch_address(void** addr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+    return fail(VDA_ERR_DEVICE, "no usable HIP device for the no-alloc workspace");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_addr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(VDA_ERR_HIP, "hipGetSymbolAddress of the no-alloc workspace failed: %s", hipGetErrorString(e));
+    g_scratch_addr[dev] = p;
+  }
+  *addr = g_scratch_addr[dev];
+  return VDA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -565,6 +593,26 @@ int vda_forward(const vda_desc* desc, const void* q, const void* k, const void* 
                 size_t ws_size, float* states_fwd, float* states_rev, void* out, void* stream) {
   return forward_impl(desc, q, k, v, beta, alpha, k_text, v_text, beta_text, ws, ws_size, states_fwd, states_rev,
                       out, stream);
+}
+
+int vda_forward_noalloc(const vda_desc* desc, const void* q, const void* k, const void* v, const float* beta,
+                        const float* alpha, const void* k_text, const void* v_text, const float* beta_text,
+                        float* states_fwd, float* states_rev, void* out, int32_t* status, void* stream) {
+  Shape s;
+  int rc = check_desc(desc, &s);
+  if (rc) return rc;
+  if (ws_bytes(s) > kScratchBytes)
+    return fail(VDA_ERR_WORKSPACE, "the path needs %zu bytes of workspace; vda_forward_noalloc holds at most %zu",
+                ws_bytes(s), kScratchBytes);
+  if (!aligned16(status)) return fail(VDA_ERR_ALIGN, "status needs 16-byte alignment");
+  if ((rc = check_device())) return rc;
+  void* ws = nullptr;
+  if ((rc = scratch_address(&ws))) return rc;
+  rc = forward_impl(desc, q, k, v, beta, alpha, k_text, v_text, beta_text, ws, kScratchBytes, states_fwd, states_rev,
+                    out, stream);
+  if (rc) return rc;
+  if (status) vda::launch_copy_status(static_cast<const int*>(ws), status, static_cast<hipStream_t>(stream));
+  return launch_status();
 }
 
 int vda_device_status(const vda_desc* desc, const void* ws, void* stream, int32_t* flags) {

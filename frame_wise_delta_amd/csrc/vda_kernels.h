@@ -89,6 +89,8 @@ int launch_ns(const PrepArgs& a, int d, hipStream_t stream);
 // SANA-WM comparator: -A/U and B' = B/sqrt(U) in place of N and B.
 int launch_sana(const PrepArgs& a, int d, hipStream_t stream);
 void launch_clear_status(int* status, hipStream_t stream);
+// *dst = *src on the device (the status word of a workspace to a caller's int).
+void launch_copy_status(const int* src, int32_t* dst, hipStream_t stream);
 int launch_scan(const ScanPair& p, int d, hipStream_t stream);
 int launch_readout(const ReadArgs& a, int d, int in_dtype, int out_dtype, hipStream_t stream);
 // The readout with the RMSNorm + sigmoid-gate epilogue (a.gate, a.normw, a.eps).

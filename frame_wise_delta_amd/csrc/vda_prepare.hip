@@ -841,6 +841,11 @@ __global__ __launch_bounds__(NsShape<D>::NTH, 2) void ns_kernel(PrepArgs args) {
 }
 
 __global__ void clear_status_kernel(int* status) { *status = 0; }
+__global__ void copy_status_kernel(const int* src, int32_t* dst) { *dst = *src; }
+
+void launch_copy_status(const int* src, int32_t* dst, hipStream_t stream) {
+  hipLaunchKernelGGL(copy_status_kernel, dim3(1), dim3(1), 0, stream, src, dst);
+}
 
 int launch_stats(const PrepArgs& a, int d, bool in_f32, hipStream_t stream) {
   if (a.H == 0 || a.cnt == 0) return 0;

@@ -39,7 +39,8 @@ DTYPES = {"f32": VDA_F32, "bf16": VDA_BF16, "f16": VDA_F16}
 
 EXPORTS = ("vda_workspace_bytes", "vda_state_count", "vda_index_map", "vda_index_map_device", "vda_prepare_frames",
            "vda_frame_stats", "vda_factor_frames", "vda_compose_chunks", "vda_scan_fwd", "vda_scan_rev", "vda_scan_bidir",
-           "vda_readout", "vda_readout_gated", "vda_softmax_branch", "vda_forward", "vda_device_status",
+           "vda_readout", "vda_readout_gated", "vda_softmax_branch", "vda_forward", "vda_forward_noalloc",
+           "vda_device_status",
            "vda_status_string", "vda_last_error")
 
 
@@ -93,6 +94,8 @@ def load(path: str | None = None):
                                c_void_p],
         "vda_forward": [D, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                         c_void_p, c_void_p, c_size_t, c_void_p, c_void_p, c_void_p, c_void_p],
+        "vda_forward_noalloc": [D, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p],
         "vda_device_status": [D, c_void_p, c_void_p, POINTER(c_int32)],
     }
     for name, argt in sig.items():
@@ -248,6 +251,15 @@ def vda_forward(desc, q, k, v, beta, alpha, k_text, v_text, beta_text, ws, state
     _check(load().vda_forward(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(alpha),
                               _ptr(k_text), _ptr(v_text), _ptr(beta_text), _ptr(ws), ws_bytes,
                               _ptr(states_fwd), _ptr(states_rev), _ptr(out), _stream(stream)))
+
+
+def vda_forward_noalloc(desc, q, k, v, beta, alpha, k_text, v_text, beta_text, states_fwd, states_rev, out,
+                        status=None, stream=None):
+    """vda_forward with the library's own device workspace (no allocation);
+    status: None or a device int32 tensor receiving the device status word."""
+    _check(load().vda_forward_noalloc(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(alpha),
+                                      _ptr(k_text), _ptr(v_text), _ptr(beta_text), _ptr(states_fwd),
+                                      _ptr(states_rev), _ptr(out), _ptr(status), _stream(stream)))
 
 
 def vda_device_status(desc, ws, stream=None) -> int:

@@ -273,6 +273,24 @@ int vda_forward(const vda_desc* desc, const void* q, const void* k, const void* 
                 void* ws, size_t ws_bytes, float* states_fwd, float* states_rev, void* out,
                 void* stream);
 
+/* vda_forward for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same path, kernels and results as vda_forward, with the workspace taken
+ * from a device array the library holds, 64 MiB per device, from the first
+ * use on a device until the process ends.  The call itself allocates
+ * nothing.  Paths needing a larger workspace (vda_workspace_bytes(desc) >
+ * 64 MiB, e.g. more than five heads of the H3-shaped layer) return
+ * VDA_ERR_WORKSPACE before anything is enqueued.  status: NULL, or a device
+ * int32 that receives the device status word (VDA_DEV_* bits) at the end of
+ * the enqueued work.  Every call on one device shares that array, and it
+ * keeps the last call's contents: calls that overlap on one device (on
+ * different streams, or from different threads without ordering) race and
+ * give undefined results.  The other arguments, layouts and errors are those
+ * of vda_forward. */
+int vda_forward_noalloc(const vda_desc* desc, const void* q, const void* k, const void* v, const float* beta,
+                        const float* alpha, const void* k_text, const void* v_text, const float* beta_text,
+                        float* states_fwd, float* states_rev, void* out, int32_t* status, void* stream);
+
 /* Synchronises `stream`, then copies the device status word of `ws` into
  * *flags (VDA_DEV_* bits; 0 = no fault).  For tests and diagnostics. */
 int vda_device_status(const vda_desc* desc, const void* ws, void* stream, int32_t* flags);

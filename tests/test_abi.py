@@ -239,3 +239,15 @@ def test_host_maps_random_shapes():
         rows, fc = vda.vda_index_map(d)
         rr, ff = orc.index_maps(T, P, w, anchors)
         assert np.array_equal(rows, rr) and np.array_equal(fc, ff), (T, P, w, anchors)
+
+
+def test_noalloc_rejects_a_workspace_beyond_its_array():
+    """vda_forward_noalloc holds a 64 MiB workspace per device: the full
+    H3-shaped layer (24 heads, about 303 MiB) is refused on the host before
+    any device call; one head of it (about 13 MiB) fits."""
+    big = vda.desc_for(inp.CONFIG_BY_NAME["h3"])
+    assert vda.vda_workspace_bytes(big) > 64 << 20
+    with pytest.raises(vda.VdaError) as e:
+        vda.vda_forward_noalloc(big, 16, 16, 16, 16, 16, 16, 16, 16, 16, 16, 16, stream=0)
+    assert e.value.code == vda.VDA_ERR_WORKSPACE and "holds at most" in vda.vda_last_error()
+    assert vda.vda_workspace_bytes(vda.desc_for(inp.CONFIG_BY_NAME["h3"], heads=1)) <= 64 << 20
