@@ -4,7 +4,7 @@ One step = the whole path for one attention layer of the H3-shaped workload
 (24 heads, d = 128, 102 latent frames of which 2 are anchors, U = 1008
 tokens per frame, 512 text tokens, bf16 inputs, float32 state, bf16 output):
 
-    vda_frame_stats -> vda_factor_frames -> vda_scan_bidir -> vda_readout
+    vda_prepare_frames -> vda_scan_bidir -> vda_readout
 
 (the same kernels, in the same order, as one vda_forward call).  Inputs are
 seeded synthetic draws (frame_wise_delta_amd.inputs) resident in HBM before
@@ -12,11 +12,14 @@ timing starts.  The timed region is K steps back to back (ms_per_step, the
 headline); a second pass of K steps brackets every call with HIP events on
 the stream it runs on, for the per-call times and the roofline of the
 dominant HBM-bound kernel (the events add ~30 us per step, so that pass is
-not the step time).  Prints one JSON line: latent frames/s, algorithmic
-TFLOP/s, the roofline entry, and the float64 oracle timed on this host's
-cores.
+not the step time); a third pass times each step with the caches flushed
+first (a 512 MiB buffer written between steps, outside the events); and a
+plain streaming read of a 2 GiB buffer gives the read bandwidth the device
+reaches without any arithmetic.  Prints one JSON line: latent frames/s,
+algorithmic TFLOP/s, the roofline entry, and the float64 oracle timed on
+this host's cores.
 
-    python bench.py [--steps K] [--warmup W] [--config h3] [--no-cpu-baseline] [--epilogue] [--prep]
+    python bench.py [--steps K] [--warmup W] [--config h3|long|hires] [--no-cpu-baseline] [--epilogue] [--prep]
                     [--chunk-scan] [--sana-wm] [--newton]
     python bench.py --softmax [--steps K] [--warmup W]
 
@@ -28,9 +31,12 @@ gate them.  Both measure next steps of the path; neither is the default line.
 --chunk-scan sets VDA_CHUNK_SCAN: vda_compose_chunks after the factorisation,
 then the scans at chunk level (S <- S M_c + J_c once per chunk).
 --sana-wm sets VDA_SANA_WM: the SANA-WM batched additive update as a
-comparator (the "factor" call then forms -A/U and B/sqrt(U)).
---newton sets VDA_NEWTON: (I + A)^-1 by Newton iteration in the "factor"
+comparator (the prepare call then forms -A/U and B/sqrt(U)).
+--newton sets VDA_NEWTON: (I + A)^-1 by Newton iteration in the prepare
 call instead of Gauss-Jordan.
+--config long / hires time the long-video (202 frames) and high-resolution
+(402 frames, U = 2016) workloads; the oracle baseline then covers the
+heads it finishes in its time budget.
 --softmax times the softmax window + anchor + text branch (vda_softmax_branch)
 on the same workload instead: an MFMA-bound kernel, reported against the
 bf16 MFMA peak.
@@ -64,7 +70,7 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16/f16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 COPY_BYTES = 512 * 1024 * 1024
-KERNELS = ("stats_kernel", "gj_kernel", "ns_kernel", "sana_kernel", "scan_kernel", "compose_kernel",
+KERNELS = ("frame_kernel", "stats_kernel", "ns_kernel", "sana_kernel", "scan_kernel", "compose_kernel",
            "readout_kernel", "readout_gated")
 EPS = 1e-6  # RMSNorm epsilon of the epilogue
 
@@ -72,38 +78,42 @@ EPS = 1e-6  # RMSNorm epsilon of the epilogue
 def algorithmic_work(cfg, epilogue=False):
     """Algorithmic FLOPs and HBM bytes of one step.  Per scanned frame-head:
     2Ud^2 (A) + 2Ud^2 (B) + d^3 (solve) + 2 * 2d^3 (two scan directions)
-    + 2 * 2Ud^2 (forward and reverse reads; one read without window
-    exclusion); bytes: Q, K, V (16-bit), beta, alpha, O (16-bit), plus the
-    gate logits with the epilogue (its few elementwise FLOPs are not
-    counted).  Text state once per head: 4 N_text d^2 + d^3 + 2d^3 FLOPs,
-    k_T, v_T, beta_T."""
+    + 2Ud^2 (the readout: the forward and reverse reads are one product with
+    the merged operand W_t = S^f Diag(b_f) + S^r Diag(b_r), formed in 2d^2);
+    bytes: Q, K, V (16-bit), beta, alpha, O (16-bit), plus the gate logits
+    with the epilogue (its few elementwise FLOPs are not counted).  Text
+    state once per head: 4 N_text d^2 + d^3 + 2d^3 FLOPs, k_T, v_T, beta_T.
+    Returns (flops, bytes, flops counting the two reads as two products)."""
     U, d, n, H, Nt = cfg.tokens, cfg.d, cfg.scanned, cfg.heads, cfg.text_tokens
     ib = 4 if cfg.in_dtype == "f32" else 2
     ob = {"f32": 4, "bf16": 2, "f16": 2}[cfg.out_dtype]
     reads = 2 if cfg.window >= 0 else 1
-    fl_fh = 4 * U * d * d + d ** 3 + 4 * d ** 3 + reads * 2 * U * d * d
+    base = 4 * U * d * d + d ** 3 + 4 * d ** 3
+    fl_fh = base + 2 * U * d * d + (2 * d * d if reads == 2 else 0)
+    fl_fh_two = base + reads * 2 * U * d * d
     by_fh = 3 * U * d * ib + 4 * U + 4 * d + U * d * ob + (U * d * ib if epilogue else 0)
     fl_text = (4 * Nt * d * d + 3 * d ** 3) if Nt else 0
     by_text = (2 * Nt * d * ib + 4 * Nt) if Nt else 0
-    return H * (n * fl_fh + fl_text), H * (n * by_fh + by_text)
+    return H * (n * fl_fh + fl_text), H * (n * by_fh + by_text), H * (n * fl_fh_two + fl_text)
 
 
 def kernel_bytes(cfg):
-    """Algorithmic HBM bytes of one launch of the HBM-bound kernels:
-    statistics read K, V (16-bit) and beta of every scanned frame and the
-    text tokens; the readout reads Q and alpha of every scanned frame and
-    writes every output row (anchor rows are zeros); the gated readout also
-    reads the gate logits of every scanned frame."""
+    """Algorithmic HBM bytes of one launch of the HBM-bound kernels: the
+    statistics (with the factorisation in frame_kernel) read K, V (16-bit)
+    and beta of every scanned frame and the text tokens; the readout reads
+    Q and alpha of every scanned frame and writes every output row (anchor
+    rows are zeros); the gated readout also reads the gate logits of every
+    scanned frame."""
     U, d, n, H, Nt, T = cfg.tokens, cfg.d, cfg.scanned, cfg.heads, cfg.text_tokens, cfg.frames
     ib = 4 if cfg.in_dtype == "f32" else 2
     ob = {"f32": 4, "bf16": 2, "f16": 2}[cfg.out_dtype]
     stats = H * (n * (2 * U * d * ib + 4 * U) + (2 * Nt * d * ib + 4 * Nt))
     read = H * (n * (U * d * ib + 4 * d) + T * U * d * ob)
     gated = read + H * n * U * d * ib + H * d * 4
-    return {"stats_kernel": stats, "readout_kernel": read, "readout_gated": gated}
+    return {"frame_kernel": stats, "stats_kernel": stats, "readout_kernel": read, "readout_gated": gated}
 
 
-KERNEL_SRC = {"stats_kernel": "vda_prepare.hip", "gj_kernel": "vda_prepare.hip",
+KERNEL_SRC = {"frame_kernel": "vda_prepare.hip", "stats_kernel": "vda_prepare.hip",
               "ns_kernel": "vda_prepare.hip", "sana_kernel": "vda_prepare.hip",
               "scan_kernel": "vda_scan.hip", "compose_kernel": "vda_scan.hip", "readout_kernel": "vda_readout.hip",
               "readout_gated": "vda_readout.hip"}
@@ -385,7 +395,7 @@ def main():
     main_s = torch.cuda.current_stream()
 
     # the calls of a step, as named in call_ms
-    names = ["stats", "factor"] + (["compose"] if args.chunk_scan else []) + ["scans", "readout"]
+    names = ["prepare"] + (["compose"] if args.chunk_scan else []) + ["scans", "readout"]
 
     def step(pairs=None):
         """One step; with pairs (event pairs per call) each call is bracketed
@@ -395,12 +405,9 @@ def main():
         def mark(k, i):
             if pairs is not None:
                 pairs[k][i].record(main_s)
-        mark("stats", 0)
-        vda.vda_frame_stats(desc, x.k, x.v, x.beta, x.kt, x.vt, x.bt, b.ws, b.ws_bytes, stream=main_s)
-        mark("stats", 1)
-        mark("factor", 0)
-        vda.vda_factor_frames(desc, b.ws, b.ws_bytes, stream=main_s)
-        mark("factor", 1)
+        mark("prepare", 0)
+        vda.vda_prepare_frames(desc, x.k, x.v, x.beta, x.kt, x.vt, x.bt, b.ws, b.ws_bytes, stream=main_s)
+        mark("prepare", 1)
         if args.chunk_scan:
             mark("compose", 0)
             vda.vda_compose_chunks(desc, b.ws, x.alpha, ws_bytes=b.ws_bytes, stream=main_s)
@@ -439,12 +446,43 @@ def main():
     kms = {k: float(np.mean([pr[k][0].elapsed_time(pr[k][1]) for pr in pairs])) for k in names}
     print(f"[bench] {args.steps} steps: {ms_step:.3f} ms/step; calls {kms}", file=sys.stderr, flush=True)
 
-    flops, nbytes = algorithmic_work(cfg, args.epilogue)
+    # cold steps: a 512 MiB buffer is written before each step (outside the
+    # events), so the L2s and the 256 MB MALL hold none of the step's data
+    flush = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device="cuda")
+    cold = []
+    for i in range(min(args.steps, 20)):
+        flush.fill_(float(i))
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(main_s)
+        step()
+        e1.record(main_s)
+        torch.cuda.synchronize()
+        cold.append(e0.elapsed_time(e1))
+    del flush
+    # the read bandwidth of a plain streaming kernel on this device (2 GiB, 2048 workgroups)
+    src = torch.ones(2 * 1024 * 1024 * 1024 // 4, dtype=torch.float32, device="cuda")
+    sink = torch.empty(2048, dtype=torch.int32, device="cuda")
+    vda.vda_stream_read(src, sink, 2048)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(main_s)
+    for _ in range(5):
+        vda.vda_stream_read(src, sink, 2048)
+    e1.record(main_s)
+    torch.cuda.synchronize()
+    stream_gbs = 5 * src.numel() * 4 / (e0.elapsed_time(e1) / 1e3) / 1e9
+    del src, sink
+    print(f"[bench] cold steps median {np.median(cold):.3f} ms; stream read {stream_gbs:.0f} GB/s", file=sys.stderr,
+          flush=True)
+
+    flops, nbytes, flops_two = algorithmic_work(cfg, args.epilogue)
     t_s = ms_step / 1e3
     kb = kernel_bytes(cfg)
     rk = "readout_gated" if args.epilogue else "readout_kernel"
-    kb = {k: kb[k] for k in ("stats_kernel", rk)}
-    call_of = {"stats_kernel": "stats", rk: "readout"}
+    # the prepare call is one kernel (frame_kernel) on the path; for the
+    # comparators it is the statistics kernel followed by their own kernel
+    pk = "stats_kernel" if (args.sana_wm or args.newton) else "frame_kernel"
+    kb = {k: kb[k] for k in (pk, rk)}
+    call_of = {pk: "prepare", rk: "readout"}
     dom = max(kb, key=lambda k: kms[call_of[k]])
     ach = kb[dom] / (kms[call_of[dom]] / 1e3) / 1e9
     roofline = {"kernel": dom, "bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
@@ -486,8 +524,16 @@ def main():
                    "parallelism": "single GPU"},
         "tflops_algorithmic": round(flops / t_s / 1e12, 2),
         "mfma_peak_frac": round(flops / t_s / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "flop_count": "readout as one product with the merged operand (2Ud^2 per frame-head)",
+        "tflops_algorithmic_two_reads": round(flops_two / t_s / 1e12, 2),
+        "mfma_peak_frac_two_reads": round(flops_two / t_s / 1e12 / PEAK_BF16_TFLOPS, 4),
         "hbm_frac_path": round(nbytes / t_s / 1e9 / PEAK_HBM_GBS, 4),
         "call_ms": {k: round(v, 4) for k, v in kms.items()},
+        "cold": {"ms_per_step_median": round(float(np.median(cold)), 4),
+                 "ms_per_step_min": round(float(np.min(cold)), 4), "steps": len(cold),
+                 "frames_per_s": round(cfg.frames / (float(np.median(cold)) / 1e3), 2),
+                 "flush": "512 MiB written before each step, outside the timed events"},
+        "stream_read_gbs": round(stream_gbs, 1),
         "roofline": roofline,
         "cpu_baseline": cpu,
         "rel_l2_head0": rel,

@@ -251,6 +251,7 @@ int scan_args(const vda_desc* desc, const void* ws, const float* alpha, const fl
   if (!aligned16(alpha) || !aligned16(s_init) || !aligned16(states) || ((uintptr_t)ws & 255u))
     return fail(VDA_ERR_ALIGN, "alpha, s_init, states need 16-byte and ws 256-byte alignment");
   a.frames = reinterpret_cast<const float*>(static_cast<const char*>(ws) + vda::kWsHeader);
+  a.status = static_cast<int*>(const_cast<void*>(ws));
   a.alpha = alpha;
   a.s_init = s_init;
   a.states = states;
@@ -271,17 +272,27 @@ int scan_args(const vda_desc* desc, const void* ws, const float* alpha, const fl
   return VDA_OK;
 }
 
-int scan_mode(const Shape& s) { return s.sana ? vda::kSanaScan : s.chunked ? vda::kChunkScan : vda::kFrameScan; }
+int scan_mode(const Shape& s) {
+  if (s.sana) return vda::kSanaScan;
+  if (s.chunked) return vda::kChunkScan;
+  return s.newton ? vda::kFrameScanB : vda::kFrameScan;
+}
 
-// the factorisation (Gauss-Jordan, or Newton iteration), or the SANA-WM
-// comparator's transition in its place
-void launch_factor(const Shape& s, const vda::PrepArgs& a, hipStream_t st) {
-  if (s.sana)
+// Everything the scans read from the workspace: N_t and J_t from the fused
+// statistics + factorisation kernel; for the comparators, the statistics and
+// then the Newton-iteration inverse (N_t, with B_t) or the SANA-WM transition
+// and injection.  The device status word is cleared first.
+void launch_prepare(const Shape& s, const vda::PrepArgs& a, bool in_f32, hipStream_t st) {
+  vda::launch_clear_status(a.status, st);
+  if (s.sana) {
+    vda::launch_stats(a, s.d, in_f32, st);
     vda::launch_sana(a, s.d, st);
-  else if (s.newton)
+  } else if (s.newton) {
+    vda::launch_stats(a, s.d, in_f32, st);
     vda::launch_ns(a, s.d, st);
-  else
-    vda::launch_gj(a, s.d, st);
+  } else {
+    vda::launch_frame(a, s.d, in_f32, st);
+  }
 }
 
 int read_args(const vda_desc* desc, const void* q, const float* alpha, const float* states_fwd,
@@ -332,49 +343,7 @@ int vda_prepare_frames(const vda_desc* desc, const void* k, const void* v, const
   if (rc) return rc;
   rc = check_device();
   if (rc) return rc;
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  vda::launch_clear_status(a.status, st);
-  vda::launch_stats(a, s.d, desc->in_dtype == VDA_F32, st);
-  launch_factor(s, a, st);
-  return launch_status();
-}
-
-int vda_frame_stats(const vda_desc* desc, const void* k, const void* v, const float* beta, const void* k_text,
-                    const void* v_text, const float* beta_text, void* ws, size_t ws_size, void* stream) {
-  Shape s;
-  vda::PrepArgs a;
-  int rc = prep_args(desc, k, v, beta, k_text, v_text, beta_text, ws, ws_size, s, a);
-  if (rc) return rc;
-  rc = check_device();
-  if (rc) return rc;
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  vda::launch_clear_status(a.status, st);
-  vda::launch_stats(a, s.d, desc->in_dtype == VDA_F32, st);
-  return launch_status();
-}
-
-int vda_factor_frames(const vda_desc* desc, void* ws, size_t ws_size, void* stream) {
-  Shape s;
-  int rc = check_desc(desc, &s);
-  if (rc) return rc;
-  if (!ws) return fail(VDA_ERR_NULL, "ws is NULL");
-  if (ws_size < ws_bytes(s)) return fail(VDA_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_size, ws_bytes(s));
-  if ((uintptr_t)ws & 255u) return fail(VDA_ERR_ALIGN, "ws needs 256-byte alignment");
-  rc = check_device();
-  if (rc) return rc;
-  vda::PrepArgs a = {};
-  a.status = static_cast<int*>(ws);
-  a.frames = reinterpret_cast<float*>(static_cast<char*>(ws) + vda::kWsHeader);
-  a.H = s.H;
-  a.T = s.T;
-  a.U = s.U;
-  a.a = s.a;
-  a.n = s.n;
-  a.n_eff = s.n_eff;
-  a.Nt = s.Nt;
-  a.s0 = 0;
-  a.cnt = s.n_eff;
-  launch_factor(s, a, static_cast<hipStream_t>(stream));
+  launch_prepare(s, a, desc->in_dtype == VDA_F32, static_cast<hipStream_t>(stream));
   return launch_status();
 }
 
@@ -386,7 +355,7 @@ int vda_scan_fwd(const vda_desc* desc, const void* ws, const float* alpha, const
   if (rc) return rc;
   rc = check_device();
   if (rc) return rc;
-  vda::ScanPair p = {{a, a}, 1, scan_mode(s)};
+  vda::ScanPair p = {{a, a}, 1, scan_mode(s), s.newton};
   vda::launch_scan(p, s.d, static_cast<hipStream_t>(stream));
   return launch_status();
 }
@@ -399,7 +368,7 @@ int vda_scan_rev(const vda_desc* desc, const void* ws, const float* alpha, const
   if (rc) return rc;
   rc = check_device();
   if (rc) return rc;
-  vda::ScanPair p = {{a, a}, 1, scan_mode(s)};
+  vda::ScanPair p = {{a, a}, 1, scan_mode(s), s.newton};
   vda::launch_scan(p, s.d, static_cast<hipStream_t>(stream));
   return launch_status();
 }
@@ -416,6 +385,7 @@ int vda_compose_chunks(const vda_desc* desc, void* ws, size_t ws_size, const flo
   if (rc) return rc;
   p.ndir = 2;
   p.mode = vda::kCompose;
+  p.bform = s.newton;
   vda::launch_scan(p, s.d, static_cast<hipStream_t>(stream));
   return launch_status();
 }
@@ -431,6 +401,7 @@ int vda_scan_bidir(const vda_desc* desc, const void* ws, const float* alpha, con
   if (rc) return rc;
   p.ndir = 2;
   p.mode = scan_mode(s);
+  p.bform = s.newton;
   vda::launch_scan(p, s.d, static_cast<hipStream_t>(stream));
   return launch_status();
 }
@@ -539,10 +510,8 @@ int forward_impl(const vda_desc* desc, const void* q, const void* k, const void*
   if ((rc = read_args(desc, q, alpha, states_fwd, states_rev, out, s, qa, any))) return rc;
   if ((rc = check_device())) return rc;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const bool f32 = desc->in_dtype == VDA_F32;
-  vda::launch_clear_status(pa.status, st);
-  vda::launch_stats(pa, s.d, f32, st);
-  launch_factor(s, pa, st);
+  sp.bform = s.newton;
+  launch_prepare(s, pa, desc->in_dtype == VDA_F32, st);
   if (s.chunked) {
     vda::ScanPair cp = sp;  // both directions' chunk maps in one launch
     cp.dir[1] = sp.dir[0];
@@ -584,9 +553,48 @@ int scratch_address(void** addr) {
   return VDA_OK;
 }
 
+// Streams n16 16-byte words of src through the vector memory path (eight
+// independent loads in flight per thread) and writes one word per workgroup
+// to sink, so that the loads cannot be dropped.
+__global__ __launch_bounds__(256) void stream_read_kernel(const uint4* __restrict__ src, size_t n16, uint32_t* sink) {
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  uint32_t x = 0;
+  size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  for (; i + 7 * stride < n16; i += 8 * stride) {
+    uint4 v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = src[i + j * stride];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x ^= v[j].x ^ v[j].y ^ v[j].z ^ v[j].w;
+  }
+  for (; i < n16; i += stride) {
+    const uint4 v = src[i];
+    x ^= v.x ^ v.y ^ v.z ^ v.w;
+  }
+  __shared__ uint32_t red[256];
+  red[threadIdx.x] = x;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t r = 0;
+    for (int t = 0; t < 256; ++t) r ^= red[t];
+    sink[blockIdx.x] = r;
+  }
+}
+
 }  // namespace
 
 extern "C" {
+
+int vda_stream_read(const void* src, size_t bytes, uint32_t* sink, int32_t blocks, void* stream) {
+  if (!src || !sink) return fail(VDA_ERR_NULL, "src or sink is NULL");
+  if (!aligned16(src) || (bytes & 15u)) return fail(VDA_ERR_ALIGN, "src and bytes need 16-byte alignment");
+  if (blocks < 1) return fail(VDA_ERR_VALUE, "blocks = %d < 1", blocks);
+  int rc = check_device();
+  if (rc) return rc;
+  hipLaunchKernelGGL(stream_read_kernel, dim3((unsigned)blocks), dim3(256), 0, static_cast<hipStream_t>(stream),
+                     static_cast<const uint4*>(src), bytes / 16, sink);
+  return launch_status();
+}
 
 int vda_forward(const vda_desc* desc, const void* q, const void* k, const void* v, const float* beta,
                 const float* alpha, const void* k_text, const void* v_text, const float* beta_text, void* ws,

@@ -30,6 +30,7 @@ struct ScanArgs {
   int use_text;         // S_init = S^T from the text slot (slot n) when s_init == nullptr
   float scale;
   int prep;             // alpha holds logits (the gate is sigmoid(logit))
+  int* status;          // device status word (a non-finite recorded state sets VDA_DEV_NONFINITE)
   // chunk maps (compose and chunk-scan launches): per head, direction and
   // chunk, 4 d^2 bytes: M_c (f16, the fragment order of N) then J_c (f16,
   // accumulator order, see vda_scan.hip)
@@ -39,10 +40,11 @@ struct ScanArgs {
 
 // What a scan launch runs.
 enum ScanMode {
-  kFrameScan = 0,  // S_t = (S_{t-1} Diag(alpha_t) + B_t) N_t over the frames
-  kCompose = 1,    // the chunk maps (M_c, J_c) of every chunk, in parallel
-  kChunkScan = 2,  // S_c = S_{c-1} M_c + J_c over the chunks
-  kSanaScan = 3,   // S_t = X + X (-A_t/U) + B'_t, X = S_{t-1} Diag(alpha_t) (the SANA-WM comparator)
+  kFrameScan = 0,   // S_t = (S_{t-1} Diag(alpha_t)) N_t + J_t over the frames (slots from frame_kernel)
+  kCompose = 1,     // the chunk maps (M_c, J_c) of every chunk, in parallel
+  kChunkScan = 2,   // S_c = S_{c-1} M_c + J_c over the chunks
+  kSanaScan = 3,    // S_t = X + X (-A_t/U) + B'_t, X = S_{t-1} Diag(alpha_t) (the SANA-WM comparator)
+  kFrameScanB = 4,  // S_t = (S_{t-1} Diag(alpha_t) + B_t) N_t (slots holding N_t and B_t: the Newton comparator)
 };
 
 // One or two scans in one launch: blocks [0, H RB) run dir[0], the next
@@ -51,7 +53,8 @@ enum ScanMode {
 struct ScanPair {
   ScanArgs dir[2];
   int ndir;
-  int mode;  // ScanMode
+  int mode;    // ScanMode
+  int bform;   // compose: the slots hold N_t and B_t (else N_t and J_t)
 };
 
 struct ReadArgs {
@@ -82,8 +85,10 @@ struct AttnArgs {
   int tiles_per_head, anchor_tiles, chunk_tiles;  // 256-query workgroups
 };
 
+// Statistics, factorisation and injection in one kernel: N_t and J_t = B_t N_t.
+int launch_frame(const PrepArgs& a, int d, bool in_f32, hipStream_t stream);
+// Statistics alone (the comparators): the upper tiles of A_t (float32) and B_t (f16).
 int launch_stats(const PrepArgs& a, int d, bool in_f32, hipStream_t stream);
-int launch_gj(const PrepArgs& a, int d, hipStream_t stream);
 // N = (I + A)^{-1} by Newton iteration instead of Gauss-Jordan.
 int launch_ns(const PrepArgs& a, int d, hipStream_t stream);
 // SANA-WM comparator: -A/U and B' = B/sqrt(U) in place of N and B.

@@ -1,27 +1,23 @@
-// Frame statistics and factorisation of the VDA frame write, as two kernels.
+// Frame statistics and factorisation of the VDA frame write.
 //
-// stats_kernel: for every (head, frame) one workgroup computes, over the
-// frame's U tokens,
-//   A = K^T Diag(beta) K  and  B = V^T Diag(beta) K
-// ("Video DeltaNet: A Video-Native Hybrid Attention for Livestream Video
-// Generation", method-steps section, step (3)) on MFMA with float32
-// accumulation, and stores B (row-major) and the upper-triangle tiles of A
-// (accumulator layout, in the place N will take) in the frame's workspace
-// slot.  K, V rows are streamed from HBM in 64-token rounds, converted
-// to f16 (beta*K is rounded once to f16) and written channel-major into LDS
-// so that an MFMA operand lane reads eight consecutive tokens of one channel
-// with a single 16-byte LDS load.  The 16-byte token groups of each LDS row
-// are XOR-swizzled so that both the transposing writes and the operand reads
-// are free of bank conflicts.  The next round's global loads are issued
-// before the current round's MFMAs.
+// frame_kernel (the path): for every (head, frame slot) one workgroup
+// computes A = K^T Diag(beta) K and B = V^T Diag(beta) K over the frame's U
+// tokens ("Video DeltaNet: A Video-Native Hybrid Attention for Livestream
+// Video Generation", method-steps section, step (3)), factorises I + A by a
+// blocked Gauss-Jordan sweep with B^T as right-hand side, and stores
+// N = (I + A)^{-1} and J = B N in the frame's workspace slot; A and B never
+// leave the workgroup.  K and V rows are streamed from HBM in 64-token
+// rounds, converted to f16 and written channel-major into LDS so that an
+// MFMA operand lane reads eight consecutive tokens of one channel with a
+// single 16-byte LDS load.  The 16-byte token groups of each LDS row are
+// XOR-swizzled so that both the transposing writes and the operand reads are
+// free of bank conflicts.  The next round's global loads are issued before
+// the current round's MFMAs.
 //
-// gj_kernel: one wavefront per frame inverts G = I + A in registers with a
-// blocked Gauss-Jordan sweep (16x16 blocks on MFMA, scalar 16x16 pivot-block
-// inverses) and overwrites A with N = G^{-1}, rounded to f16, in the MFMA
-// fragment order the scan consumes.  G is symmetric positive definite
-// (eigenvalues >= 1), so no pivoting is needed.  Running the latency-bound
-// sweep as single-wavefront workgroups, apart from the bandwidth-bound
-// statistics, lets every SIMD work on its own matrices without barriers.
+// stats_kernel (the comparators): the same statistics, stored as the
+// upper-triangle tiles of A (float32) and B (f16, row-major) for the
+// SANA-WM transition (sana_kernel) and the Newton-iteration inverse
+// (ns_kernel), which read them back.
 #include <utility>
 
 #include "vda_common.h"
@@ -138,53 +134,6 @@ __device__ __forceinline__ void invert16_impl(f32x4& y, int n, int g, int& bad, 
 // In-place inverse of the 16x16 matrix W held four columns per lane (above).
 __device__ __forceinline__ void invert16(f32x4& y, int n, int g, int& bad) {
   invert16_impl(y, n, g, bad, std::make_integer_sequence<int, 16>{});
-}
-
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-
-// bf16 pair with v ~ hi + lo: hi is v truncated to bf16 (exact upper half
-// of the float32 word), lo = v - hi (exact) rounded to bf16, so hi + lo
-// holds v to about 2^-16 relative.
-__device__ __forceinline__ void split4(f32x4 v, bf16x4& hi, bf16x4& lo) {
-  uint32_t w[4];
-  f32x4 r;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    w[e] = __float_as_uint(v[e]);
-    r[e] = v[e] - __uint_as_float(w[e] & 0xffff0000u);
-  }
-  uint2 h;
-  h.x = __builtin_amdgcn_perm(w[1], w[0], 0x07060302u);  // upper halves of w0 (low) and w1 (high)
-  h.y = __builtin_amdgcn_perm(w[3], w[2], 0x07060302u);
-  hi = __builtin_bit_cast(bf16x4, h);
-  lo = __builtin_convertvector(r, bf16x4);
-}
-
-__device__ __forceinline__ bf16x8 cat8(bf16x4 a, bf16x4 b) {
-  return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
-}
-
-__device__ __forceinline__ bf16x8 neg8(bf16x8 a) {
-  uint4 u = __builtin_bit_cast(uint4, a);
-  u.x ^= 0x80008000u; u.y ^= 0x80008000u; u.z ^= 0x80008000u; u.w ^= 0x80008000u;
-  return __builtin_bit_cast(bf16x8, u);
-}
-
-// Index of the upper-triangle tile pair {i, j}, i <= j, of a RT x RT grid.
-__host__ __device__ constexpr int upair(int RT, int i, int j) { return i * RT - i * (i - 1) / 2 + (j - i); }
-
-// 16x16 float32 transposes through LDS, for accumulator-layout tiles (lane
-// (n, g) holds Z[4g + e][n]).  put stores Z^T row-major; get returns the
-// accumulator layout of Z^T.  The 20-float pitch keeps both conflict-free.
-constexpr int kXP = 20;
-__device__ __forceinline__ void tr_put(float* buf, f32x4 v, int n, int g) {
-  *reinterpret_cast<f32x4*>(buf + n * kXP + 4 * g) = v;
-}
-__device__ __forceinline__ f32x4 tr_get(const float* buf, int n, int g) {
-  f32x4 r;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) r[e] = buf[(4 * g + e) * kXP + n];
-  return r;
 }
 
 }  // namespace
@@ -392,136 +341,402 @@ __global__ __launch_bounds__(kThreads, 2) void stats_kernel(PrepArgs args) {
   if (bad) atomicOr(args.status, bad);
 }
 
-// One wavefront inverts one G = I + A.  G is symmetric, so only the pairs
-// {i, j}, i <= j, of 16x16 tiles are kept, each once, in MFMA accumulators
-// (lane (n, g) holds rows 4g .. 4g+3 of column n of the tile).  In-place
-// Gauss-Jordan over the blocks P processed so far keeps the working matrix M
-// symmetric within P and within the rest Q, and antisymmetric between them
-// (M[i][j] = -M[j][i]^T for i in P, j in Q), so either tile of a pair gives
-// the other.  A pair {i, j}, i < j, is held as M[i][j] until step j and as
-// M[j][i] from then on: at step p every pair {j, p} is held as M[p][j], the
-// row strip R_j of the pivot (the pairs {j, p}, j < p, are transposed through
-// LDS at the start of step p).  Step p:
-//   E = M[p][p] -> E^{-1}, scalar Gauss-Jordan, four columns per lane;
-//   r'_j = E^{-1} R_j on MFMA, the new M[p][j] (the new column strip follows
-//          by the symmetry above and is never formed);
-//   every other pair, held as M[x][y]: M[x][y] -= M[x][p] r'_y, where the
-//          operand M[x][p] comes from R_x (= +R_x^T for x > p and -R_x^T
-//          for x < p).
-// An accumulator tile Z used as the MFMA A operand is Z^T and as the B operand
-// Z itself, so every product above reads the tiles in place.  Products use
-// bf16 hi/lo splits of both factors; the K = 32 MFMA forms (a_hi + a_lo) b in
-// one instruction by pairing the hi and lo halves of one factor with two
-// copies of one half of the other, so a four-term product takes two MFMAs.
-// The pivot block is read as E^T (equal to E) and E^{-1} is used as its own
-// transpose.  A pivot <= 0 or a non-finite value sets a bit of the device
-// status word.
-template <int D>
-__global__ __launch_bounds__(64, 2) void gj_kernel(PrepArgs args) {
-  constexpr int RT = D / 16;
-  constexpr int NPR = RT * (RT + 1) / 2;
-  constexpr int NB = RT > 1 ? RT - 1 : 1;  // transpose buffers
-  __shared__ __attribute__((aligned(16))) float sT[NB][16 * kXP];
+// Own column tiles of wavefront w in the frame kernel: w and w + 4 (those
+// below RT).  Column p of every step of the sweep belongs to wavefront p % 4.
+template <int RT>
+constexpr int kOwnCols = (RT + 3) / 4;
 
-  const int lane = threadIdx.x;
-  const int n = lane & 15, g = lane >> 4;
+// f16 hi/lo pair of four floats: hi = v rounded to f16, lo = v - hi (exact)
+// rounded to f16, so hi + lo holds v to about 2^-22 relative (down to the
+// f16 subnormal spacing 2^-24 in absolute terms).
+__device__ __forceinline__ void split_f16(f32x4 v, f16x4& hi, f16x4& lo) {
+  hi = __builtin_convertvector(v, f16x4);
+  lo = __builtin_convertvector(v - __builtin_convertvector(hi, f32x4), f16x4);
+}
+__device__ __forceinline__ f16x8 cat_f16(f16x4 a, f16x4 b) {
+  return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+__device__ __forceinline__ f16x8 neg_f16(f16x8 a) {
+  uint4 u = __builtin_bit_cast(uint4, a);
+  u.x ^= 0x80008000u;
+  u.y ^= 0x80008000u;
+  u.z ^= 0x80008000u;
+  u.w ^= 0x80008000u;
+  return __builtin_bit_cast(f16x8, u);
+}
+
+// Products of 16 x 16 float32 tiles on the K = 32 f16 MFMA, accurate to
+// about 2^-22: a left factor L enters as the A operand [L_hi | L_lo] (lane
+// (m, g) holds L[m][4g .. 4g+3] in both halves), a right factor R as the two
+// B operands [R_hi | R_hi] and [R_lo | R_lo] (lane (n, g) holds
+// R[4g .. 4g+3][n]), so the two MFMAs sum (L_hi + L_lo)(R_hi + R_lo) over the
+// 16-deep k.  An accumulator tile Z (lane (n, g) holds Z[4g + e][n]) is its
+// own right operand; a tile read from LDS can be laid out as either.
+struct RightF16 {
+  f16x8 hh, ll;
+};
+__device__ __forceinline__ f16x8 left_f16(f32x4 v) {
+  f16x4 h, l;
+  split_f16(v, h, l);
+  return cat_f16(h, l);
+}
+__device__ __forceinline__ RightF16 right_f16(f32x4 v) {
+  f16x4 h, l;
+  split_f16(v, h, l);
+  return RightF16{cat_f16(h, h), cat_f16(l, l)};
+}
+__device__ __forceinline__ f32x4 mul_f16(f16x8 left, const RightF16& r, f32x4 acc) {
+  acc = mfma_f16(left, r.hh, acc);
+  return mfma_f16(left, r.ll, acc);
+}
+// Right operands [I | 0], [0 | I] and [-I | -I] in lane (n, g): k = 4g + e.
+__device__ __forceinline__ f16x8 eye_f16(int n, int g, int half, float val) {
+  f16x8 r;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) r[e] = (_Float16)(((e >> 2) == half || half < 0) && 4 * g + (e & 3) == n ? val : 0.f);
+  return r;
+}
+// The left operand [Z_hi | Z_lo] of a tile Z held in accumulator layout:
+// the accumulator registers, read as an A operand, are Z^T, so a product
+// with the identity returns Z^T in accumulator layout, i.e. Z in A-operand
+// layout; the hi and lo halves are moved separately, exactly.
+__device__ __forceinline__ f16x8 to_left_f16(f32x4 z, f16x8 eye_hi, f16x8 eye_lo) {
+  f16x4 h, l;
+  split_f16(z, h, l);
+  const f16x8 a = cat_f16(h, l);
+  const f32x4 th = mfma_f16(a, eye_hi, f32x4{0, 0, 0, 0});
+  const f32x4 tl = mfma_f16(a, eye_lo, f32x4{0, 0, 0, 0});
+  return cat_f16(__builtin_convertvector(th, f16x4), __builtin_convertvector(tl, f16x4));
+}
+
+// The frame write's statistics and factorisation in one workgroup per (head,
+// frame slot) ("Video DeltaNet: A Video-Native Hybrid Attention for
+// Livestream Video Generation", method-steps section, step (3): A_t and B_t
+// from the frame's tokens, the factorisation of I + A_t, the transition and
+// the injection; core-method section, paragraph 2: the frame write
+// S_t = (S_{t-1} Diag(alpha_t) + B_t)(I + A_t)^{-1}).  It stores
+//   N = (I + A)^{-1}      (f16, the fragment order of the scan's B operand)
+//   J = B N               (f16, the scan's accumulator order, at byte 2 d^2)
+// so that the scan computes S_t = (S_{t-1} Diag(alpha_t)) N_t + J_t.  J
+// rather than B is stored because every quantity the scan then reads is of
+// the size of the state: B itself grows with the conditioning of I + A
+// (about by its condition number), and so would the relative effect of any
+// rounding of B or of the N that multiplies it.
+//
+// Statistics.  K and V stream through LDS in 64-token rounds as f16 tiles
+// K, beta*K and beta*V (each rounded once to f16; rounding beta*V instead of
+// using beta*K for B puts the rounding of B in the span of the keys, where
+// N damps it).  Wavefront w owns the column tiles i in {w, w + 4} of
+//   T = I + A    (tile (c, i) = sum_u K[u][c] (beta K)[u][i], plus I)
+//   X = B        (tile (c, i) = sum_u (beta V)[u][c] K[u][i])
+// for every row tile c, in float32 accumulators.
+//
+// Inverse.  Blocked Gauss-Jordan on G = I + A (symmetric positive definite,
+// no pivoting), written for the transpose T = M^T of the working matrix M
+// that the wavefronts hold by columns.  Step p, with E^T the tile T[p][p]:
+//   Ei^T = (E^T)^{-1}, then for every column i != p
+//     T[j][i] -= (T[j][p] Ei^T) T[p][i]   (j != p),
+//     T[p][i]  = -Ei^T T[p][i],
+//   and column p becomes T[j][p] Ei^T, T[p][p] = Ei^T.
+// After the last step T = N^T = N.  The owner of column p inverts the pivot
+// tile (scalar Gauss-Jordan, four columns per lane) and stages column p
+// through LDS (double-buffered, one barrier per step); every wavefront then
+// forms the left factors T[j][p] Ei^T as the transposed products
+// Ei (T[j][p])^T, whose accumulator registers are exactly the A operands of
+// the left factors, and updates its own columns, the next pivot's column
+// first.
+//
+// Injection.  J = B N as a product: the B tiles of four row tiles at a time
+// are staged through LDS by the owners of their columns, and each wavefront
+// forms its columns of J from them and its own columns of N.
+//
+// All products of the inverse and of J use f16 hi/lo pairs (2^-22).  A pivot
+// <= 0 or a non-finite value sets a bit of the device status word.
+template <int D, class TIN, bool PREP>
+__global__ __launch_bounds__(kThreads, 2) void frame_kernel(PrepArgs args) {
+  using T_ = typename TIN::T;
+  constexpr int RT = D / 16;              // 16 x 16 tiles per row / column
+  constexpr int NC = kOwnCols<RT>;        // own column tiles per wavefront
+  constexpr int kTile = D * kRound;       // halves per LDS token tile
+  constexpr int kTP = 20;                 // LDS pitch (floats) of a staged 16 x 16 tile
+  constexpr int kStageT = RT * 16 * kTP;  // floats per sweep buffer (column p of T)
+  constexpr int kSweepB = 2 * kStageT * 4 + RT * 64 * 16;  // two column buffers, RT operand tiles
+  constexpr int kJB = (RT < 4 ? RT : 4) * RT * 64 * 16;     // B operand tiles of four row tiles
+  constexpr int kStageB = kSweepB > kJB ? kSweepB : kJB;
+  constexpr int kBytes = 3 * kTile * 2 > kStageB ? 3 * kTile * 2 : kStageB;
+  __shared__ __attribute__((aligned(16))) char smem[kBytes];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lr = lane & 15, lg = lane >> 4;
+
   const int h = blockIdx.x / args.cnt;
   const int f = args.s0 + (blockIdx.x - h * args.cnt);
-  float* slot = args.frames + ((size_t)h * args.n_eff + f) * ws_slot_floats(D);
-  int bad = 0;
-
-  // ---- G = I + A from the upper-triangle tiles of A (accumulator layout)
-  f32x4 G[NPR];
-#pragma unroll
-  for (int i = 0; i < RT; ++i)
-#pragma unroll
-    for (int j = i; j < RT; ++j)
-      G[upair(RT, i, j)] = *reinterpret_cast<const f32x4*>(slot + ((size_t)(i * RT + j) * 64 + lane) * 4);
-#pragma unroll
-  for (int i = 0; i < RT; ++i)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) G[upair(RT, i, i)][e] += (4 * g + e == n) ? 1.0f : 0.0f;
-
-  // ---- blocked Gauss-Jordan, fully unrolled (every tile index is constant)
-#pragma unroll
-  for (int p = 0; p < RT; ++p) {
-    if (p > 0) {  // pairs {j, p}, j < p: M[j][p] -> M[p][j] = -M[j][p]^T
-#pragma unroll
-      for (int j = 0; j < p; ++j) tr_put(sT[j], G[upair(RT, j, p)], n, g);
-      lds_barrier();
-#pragma unroll
-      for (int j = 0; j < p; ++j) G[upair(RT, j, p)] = -tr_get(sT[j], n, g);
-      lds_barrier();
-    }
-    f32x4 y = G[upair(RT, p, p)];
-    invert16(y, n, g, bad);
-    G[upair(RT, p, p)] = y;
-    bf16x8 e_hh, e_ll;  // A operands [Einv_hi | Einv_hi], [Einv_lo | Einv_lo]
-    {
-      bf16x4 hi, lo;
-      split4(y, hi, lo);
-      e_hh = cat8(hi, hi);
-      e_ll = cat8(lo, lo);
-    }
-    bf16x8 xr[RT];  // [R_hi | R_lo] of the row strip
-#pragma unroll
-    for (int j = 0; j < RT; ++j)
-      if (j != p) {
-        bf16x4 hi, lo;
-        split4(G[upair(RT, j < p ? j : p, j < p ? p : j)], hi, lo);
-        xr[j] = cat8(hi, lo);
-      }
-    // r'_j, then every pair held as M[x][j]: for j > p the pairs {a, j}
-    // (held as M[a][j]), for j < p the pairs {j, b}, b < p (held as M[b][j])
-#pragma unroll
-    for (int j = 0; j < RT; ++j)
-      if (j != p) {
-        f32x4 r = mfma_bf16(e_hh, xr[j], f32x4{0, 0, 0, 0});
-        r = mfma_bf16(e_ll, xr[j], r);
-        G[upair(RT, j < p ? j : p, j < p ? p : j)] = r;
-        bf16x4 hi, lo;
-        split4(r, hi, lo);
-        const bf16x8 b_hh = cat8(hi, hi), b_ll = cat8(lo, lo);  // B operands of r'_j
-        const bf16x8 n_hh = neg8(b_hh), n_ll = neg8(b_ll);
-#pragma unroll
-        for (int x = 0; x < RT; ++x) {
-          const bool held = j > p ? (x <= j && x != p) : (x >= j && x < p);
-          if (!held) continue;
-          const int t = upair(RT, x < j ? x : j, x < j ? j : x);
-          // M[x][j] -= M[x][p] r'_j with M[x][p] = -R_x^T (x < p), +R_x^T (x > p)
-          f32x4 acc = G[t];
-          acc = mfma_bf16(xr[x], x > p ? n_hh : b_hh, acc);
-          acc = mfma_bf16(xr[x], x > p ? n_ll : b_ll, acc);
-          G[t] = acc;
-        }
-      }
+  const bool text = f >= args.n;
+  const int U = text ? args.Nt : args.U;
+  const T_* kp;
+  const T_* vp;
+  const float* bp;
+  if (text) {
+    kp = static_cast<const T_*>(args.kt) + (size_t)h * args.Nt * D;
+    vp = static_cast<const T_*>(args.vt) + (size_t)h * args.Nt * D;
+    bp = args.bt + (size_t)h * args.Nt;
+  } else {
+    const size_t fr = (size_t)h * args.T + (args.a + f);
+    kp = static_cast<const T_*>(args.k) + fr * args.U * D;
+    vp = static_cast<const T_*>(args.v) + fr * args.U * D;
+    bp = args.beta + fr * args.U;
   }
 
-  // ---- N = G^{-1} -> workspace as f16 in fragment order.  Pair
-  //      {i, j}, i < j, is held as N[j][i]; N[i][j] is its transpose.  An
-  //      accumulator tile N[x][y] covers column 16y + n, rows 16x + 4g + e,
-  //      i.e. half of the 16-byte chunk (16y + n, 2x + g/2).
-  _Float16* nf = reinterpret_cast<_Float16*>(slot);
-  auto put = [&](f32x4 v, int x, int yy) {
+  _Float16* sK = reinterpret_cast<_Float16*>(smem);
+  _Float16* sBK = sK + kTile;
+  _Float16* sBV = sBK + kTile;
+
+  // T[m][c] = tile (c, i) of I + A, X[m][c] = tile (c, i) of B, i = wave + 4m
+  f32x4 Tt[NC][RT], Xt[NC][RT];
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      if (!__builtin_isfinite(v[e])) bad |= VDA_DEV_NONFINITE;
-    const size_t off = (size_t)ntile_chunk(D, 16 * yy + n, 2 * x + (g >> 1)) * 8 + 4 * (g & 1);
-    *reinterpret_cast<f16x4*>(nf + off) = __builtin_convertvector(v, f16x4);
-  };
+  for (int m = 0; m < NC; ++m)
 #pragma unroll
-  for (int j = 0; j < RT; ++j) {
-    put(G[upair(RT, j, j)], j, j);
-#pragma unroll
-    for (int i = 0; i < j; ++i) {
-      put(G[upair(RT, i, j)], j, i);
-      tr_put(sT[i], G[upair(RT, i, j)], n, g);
+    for (int c = 0; c < RT; ++c) {
+      Tt[m][c] = f32x4{0, 0, 0, 0};
+      Xt[m][c] = f32x4{0, 0, 0, 0};
     }
-    if (j > 0) {
-      lds_barrier();
+
+  // ---- statistics: one load task per thread and round, 8 tokens x 8
+  //      channels of K (tensor 0) or V (tensor 1), with the tokens' beta
+  constexpr int CG = D / 8;
+  constexpr int TASKS = 2 * (kRound / 8) * CG;  // <= 256
+  const bool has_task = tid < TASKS;
+  const int tensor = tid / ((kRound / 8) * CG);
+  const int trem = tid - tensor * ((kRound / 8) * CG);
+  const int tg = trem / CG, cg = trem - (trem / CG) * CG;
+  const T_* src = tensor == 0 ? kp : vp;
+  Stage8<TIN> pre;
+  float pbt[8];
+  auto fetch = [&](int u0) {
 #pragma unroll
-      for (int i = 0; i < j; ++i) put(tr_get(sT[i], n, g), i, j);
-      lds_barrier();
+    for (int s = 0; s < 8; ++s) {
+      const int u = u0 + tg * 8 + s;
+      const bool ok = has_task && u < U;
+      pre.load(s, src + (size_t)u * D + cg * 8, ok);
+      pbt[s] = ok ? bp[u] : 0.f;
+    }
+  };
+  if (U > 0) fetch(0);
+  for (int u0 = 0; u0 < U; u0 += kRound) {
+    if (has_task) {
+      float sc[8];  // per-token factor of the operand: beta, with raw keys also 1 / ||k||
+      float rn[8];
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        rn[s] = 1.f;
+        sc[s] = PREP ? sigmoid_gate(pbt[s]) : pbt[s];
+      }
+      if (PREP && tensor == 0) {
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+          rn[s] = __builtin_amdgcn_rsqf(group_sum<CG>(pre.sumsq(s)) + kPrepEps);
+          sc[s] *= rn[s];
+        }
+      }
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        f16x8 pb;
+#pragma unroll
+        for (int s = 0; s < 8; ++s) pb[s] = (_Float16)(sc[s] * pre.get(s, c));
+        *reinterpret_cast<f16x8*>((tensor == 0 ? sBK : sBV) + tile_off(cg * 8 + c, tg)) = pb;
+        if (tensor == 0) {
+          f16x8 pk;
+#pragma unroll
+          for (int s = 0; s < 8; ++s) pk[s] = (_Float16)(PREP ? pre.get(s, c) * rn[s] : pre.get(s, c));
+          *reinterpret_cast<f16x8*>(sK + tile_off(cg * 8 + c, tg)) = pk;
+        }
+      }
+    }
+    lds_barrier();
+    if (u0 + kRound < U) fetch(u0 + kRound);  // in flight during the MFMAs
+#pragma unroll
+    for (int kk = 0; kk < kRound / 32; ++kk) {
+      const int grp = kk * 4 + lg;
+      f16x8 bK[NC], bBK[NC];
+#pragma unroll
+      for (int m = 0; m < NC; ++m) {
+        const int i = wave + 4 * m;
+        if (i < RT) {
+          bK[m] = *reinterpret_cast<const f16x8*>(sK + tile_off(16 * i + lr, grp));
+          bBK[m] = *reinterpret_cast<const f16x8*>(sBK + tile_off(16 * i + lr, grp));
+        }
+      }
+#pragma unroll
+      for (int c = 0; c < RT; ++c) {
+        const f16x8 aK = *reinterpret_cast<const f16x8*>(sK + tile_off(16 * c + lr, grp));
+        const f16x8 aV = *reinterpret_cast<const f16x8*>(sBV + tile_off(16 * c + lr, grp));
+#pragma unroll
+        for (int m = 0; m < NC; ++m) {
+          if (wave + 4 * m < RT) {
+            Tt[m][c] = mfma_f16(aK, bBK[m], Tt[m][c]);
+            Xt[m][c] = mfma_f16(aV, bK[m], Xt[m][c]);
+          }
+        }
+      }
+    }
+    lds_barrier();
+  }
+
+  int bad = 0;
+#pragma unroll
+  for (int m = 0; m < NC; ++m)
+#pragma unroll
+    for (int c = 0; c < RT; ++c) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (!__builtin_isfinite(Tt[m][c][e]) || !__builtin_isfinite(Xt[m][c][e])) bad |= VDA_DEV_NONFINITE;
+        if (c == wave + 4 * m && 4 * lg + e == lr) Tt[m][c][e] += 1.f;  // G = I + A
+      }
+    }
+
+  // ---- blocked Gauss-Jordan inverse of G, fully unrolled (tile indices
+  //      constant).  Column p is staged (float32) by its owner once its pivot
+  //      tile is inverted.  The step's left factors -T[j][p] Ei^T (j != p) are
+  //      formed once per workgroup, spread over the wavefronts, and staged as
+  //      ready f16 hi/lo A operands; after a second barrier every wavefront
+  //      updates its columns from them, the owner of column p + 1 that
+  //      column first, after which it inverts the next pivot and stages the
+  //      next column, so that the inversion overlaps the other updates.
+  float* raw = reinterpret_cast<float*>(smem);                // 2 x RT float32 tiles
+  f16x8* packs = reinterpret_cast<f16x8*>(raw + 2 * kStageT);  // RT operand tiles, 64 lanes each
+  const f16x8 eye_hi = eye_f16(lr, lg, 0, 1.f), eye_lo = eye_f16(lr, lg, 1, 1.f);
+  const f16x8 neye = eye_f16(lr, lg, -1, -1.f);  // [-I | -I]
+  auto put_tile = [&](float* buf, int slot, f32x4 v) {  // tile -> row-major 16 x 16 at pitch kTP
+#pragma unroll
+    for (int e = 0; e < 4; ++e) buf[slot * 16 * kTP + (4 * lg + e) * kTP + lr] = v[e];
+  };
+  auto row_of = [&](const float* buf, int slot) {  // lane (m, g): row m, columns 4g .. 4g+3
+    return *reinterpret_cast<const f32x4*>(buf + slot * 16 * kTP + lr * kTP + 4 * lg);
+  };
+  auto pivot_and_stage = [&](int q, int mq) {  // the owner of column q
+    f32x4 y = Tt[mq][q];
+    invert16(y, lr, lg, bad);  // the inverse in the same (accumulator) layout
+    Tt[mq][q] = y;
+    float* buf = raw + (q & 1) * kStageT;
+#pragma unroll
+    for (int j = 0; j < RT; ++j) put_tile(buf, j, Tt[mq][j]);  // slot q holds Ei^T
+  };
+  if (wave == 0) pivot_and_stage(0, 0);
+#pragma unroll
+  for (int p = 0; p < RT; ++p) {
+    const int owner = p % 4, mo = p / 4;
+    const int q = p + 1, owner1 = q % 4, mq = q / 4;
+    lds_barrier();
+    const float* buf = raw + (p & 1) * kStageT;
+    // left factors: -T[j][p] Ei^T = -(Ei (T[j][p])^T)^T for j = wave (mod 4);
+    // the accumulator registers of Ei (T[j][p])^T are the A operand
+    {
+      f32x4 ei_rows;  // Ei in A-operand layout: lane (m, g) needs Ei^T[4g + e][m]
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ei_rows[e] = buf[p * 16 * kTP + (4 * lg + e) * kTP + lr];
+      const f16x8 ei_l = left_f16(ei_rows);
+#pragma unroll
+      for (int j = 0; j < RT; ++j)
+        if (j != p && j % 4 == wave)
+          packs[j * 64 + lane] = neg_f16(left_f16(mul_f16(ei_l, right_f16(row_of(buf, j)), f32x4{0, 0, 0, 0})));
+    }
+    const f16x8 neit_l = neg_f16(left_f16(row_of(buf, p)));  // -Ei^T
+    lds_barrier();
+    if (wave == owner) {  // the new column p: T[j][p] Ei^T = (-L)(-I)
+#pragma unroll
+      for (int j = 0; j < RT; ++j)
+        if (j != p) Tt[mo][j] = mfma_f16(packs[j * 64 + lane], neye, f32x4{0, 0, 0, 0});
+    }
+    auto update = [&](int cols) {  // own columns i = wave + 4m != p, set bit m
+      RightF16 tpi[NC];
+#pragma unroll
+      for (int m = 0; m < NC; ++m)
+        if ((cols >> m) & 1) tpi[m] = right_f16(Tt[m][p]);
+#pragma unroll
+      for (int j = 0; j < RT; ++j) {
+        if (j == p) continue;
+        const f16x8 l = packs[j * 64 + lane];
+#pragma unroll
+        for (int m = 0; m < NC; ++m)
+          if ((cols >> m) & 1) Tt[m][j] = mul_f16(l, tpi[m], Tt[m][j]);
+      }
+#pragma unroll
+      for (int m = 0; m < NC; ++m)
+        if ((cols >> m) & 1) Tt[m][p] = mul_f16(neit_l, tpi[m], f32x4{0, 0, 0, 0});  // -Ei^T T[p][i]
+    };
+    int mine = 0;  // own columns other than p
+#pragma unroll
+    for (int m = 0; m < NC; ++m)
+      if (wave + 4 * m < RT && wave + 4 * m != p) mine |= 1 << m;
+    if (q < RT && wave == owner1) {  // the next pivot's column first
+      update(1 << mq);
+      pivot_and_stage(q, mq);
+      update(mine & ~(1 << mq));
+    } else {
+      update(mine);
+    }
+  }
+
+  // ---- N (f16, fragment order) to the slot.  T = N^T and N is symmetric,
+  //      so tile (c, i) of T is N[16c + 4g + e][16i + n] = N[16i + n][16c + 4g + e]
+  //      in lane (n, g): half of the 16-byte chunk (16i + n, 2c + g/2).
+  float* slot = args.frames + ((size_t)h * args.n_eff + f) * ws_slot_floats(D);
+  _Float16* nf = reinterpret_cast<_Float16*>(slot);
+  f16x4* jf = reinterpret_cast<f16x4*>(reinterpret_cast<char*>(slot) + 2 * D * D);
+#pragma unroll
+  for (int m = 0; m < NC; ++m) {
+    const int i = wave + 4 * m;
+    if (i >= RT) continue;
+#pragma unroll
+    for (int c = 0; c < RT; ++c) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (!__builtin_isfinite(Tt[m][c][e])) bad |= VDA_DEV_NONFINITE;
+      const size_t off = (size_t)ntile_chunk(D, 16 * i + lr, 2 * c + (lg >> 1)) * 8 + 4 * (lg & 1);
+      *reinterpret_cast<f16x4*>(nf + off) = __builtin_convertvector(Tt[m][c], f16x4);
+    }
+  }
+
+  // ---- J = B N (f16, the scan's accumulator order: the f16x4 at
+  //      (r RT + i) 64 + lane holds tile (r, i)), four row tiles at a time:
+  //      the owners of the columns k stage the tiles B[r][k] of those rows as
+  //      ready A operands, then every wavefront forms
+  //      J[r][i] = sum_k B[r][k] N[k][i] for its columns i (N[k][i] is its own
+  //      tile T[k][i]).
+  f16x8* bpk = reinterpret_cast<f16x8*>(smem);
+#pragma unroll
+  for (int r0 = 0; r0 < RT; r0 += 4) {
+    constexpr int kRows = RT < 4 ? RT : 4;
+    lds_barrier();  // the previous readers of this memory are done
+#pragma unroll
+    for (int m = 0; m < NC; ++m)
+      if (wave + 4 * m < RT) {
+#pragma unroll
+        for (int rr = 0; rr < kRows; ++rr)
+          bpk[(rr * RT + wave + 4 * m) * 64 + lane] = to_left_f16(Xt[m][r0 + rr], eye_hi, eye_lo);
+      }
+    lds_barrier();
+#pragma unroll
+    for (int m = 0; m < NC; ++m) {
+      const int i = wave + 4 * m;
+      if (i >= RT) continue;
+      f32x4 acc[kRows];
+#pragma unroll
+      for (int rr = 0; rr < kRows; ++rr) acc[rr] = f32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int k = 0; k < RT; ++k) {
+        const RightF16 nki = right_f16(Tt[m][k]);
+#pragma unroll
+        for (int rr = 0; rr < kRows; ++rr) acc[rr] = mul_f16(bpk[(rr * RT + k) * 64 + lane], nki, acc[rr]);
+      }
+#pragma unroll
+      for (int rr = 0; rr < kRows; ++rr) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (!__builtin_isfinite(acc[rr][e])) bad |= VDA_DEV_NONFINITE;
+        jf[((r0 + rr) * RT + i) * 64 + lane] = __builtin_convertvector(acc[rr], f16x4);
+      }
     }
   }
   if (bad) atomicOr(args.status, bad);
@@ -867,16 +1082,23 @@ int launch_stats(const PrepArgs& a, int d, bool in_f32, hipStream_t stream) {
   return -1;
 }
 
-int launch_gj(const PrepArgs& a, int d, hipStream_t stream) {
+int launch_frame(const PrepArgs& a, int d, bool in_f32, hipStream_t stream) {
   if (a.H == 0 || a.cnt == 0) return 0;
-  dim3 grid((unsigned)(a.H * a.cnt)), block(64);
-#define VDA_GJ(DD)                                                                    \
+  dim3 grid((unsigned)(a.H * a.cnt)), block(kThreads);
+#define VDA_FRAME(DD)                                                                 \
   if (d == DD) {                                                                      \
-    hipLaunchKernelGGL((gj_kernel<DD>), grid, block, 0, stream, a);                   \
+    if (in_f32 && a.prep)                                                             \
+      hipLaunchKernelGGL((frame_kernel<DD, InF32, true>), grid, block, 0, stream, a); \
+    else if (in_f32)                                                                  \
+      hipLaunchKernelGGL((frame_kernel<DD, InF32, false>), grid, block, 0, stream, a); \
+    else if (a.prep)                                                                  \
+      hipLaunchKernelGGL((frame_kernel<DD, InBF16, true>), grid, block, 0, stream, a); \
+    else                                                                              \
+      hipLaunchKernelGGL((frame_kernel<DD, InBF16, false>), grid, block, 0, stream, a); \
     return 0;                                                                         \
   }
-  VDA_GJ(16) VDA_GJ(32) VDA_GJ(64) VDA_GJ(128)
-#undef VDA_GJ
+  VDA_FRAME(16) VDA_FRAME(32) VDA_FRAME(64) VDA_FRAME(128)
+#undef VDA_FRAME
   return -1;
 }
 

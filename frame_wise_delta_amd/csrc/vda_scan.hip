@@ -76,11 +76,14 @@ struct FrameRegs {
 
 template <int D, int MODE>
 __global__ __launch_bounds__(ScanShape<D>::NT) void scan_kernel(ScanPair p) {
-  static_assert(MODE == kFrameScan || MODE == kChunkScan || MODE == kSanaScan, "compose runs in compose_kernel");
-  // SANA-WM frame slots hold -A/U as the operand and B' in accumulator order,
-  // added after the product together with X; the chunk maps' J_c is added
-  // after the product in any case
-  constexpr bool POST = MODE == kSanaScan;
+  static_assert(MODE == kFrameScan || MODE == kFrameScanB || MODE == kChunkScan || MODE == kSanaScan,
+                "compose runs in compose_kernel");
+  // frame slots of frame_kernel hold J_t in accumulator order, added after
+  // the product; SANA-WM frame slots hold -A/U as the operand and B' in
+  // accumulator order, added after the product together with X; the chunk
+  // maps' J_c is added after the product in any case; only the Newton
+  // comparator's slots hold B_t, added before the product
+  constexpr bool POST = MODE != kFrameScanB;
   using SS = ScanShape<D>;
   constexpr int ROWS = SS::ROWS, NQ = SS::NQ, PD = SS::PD;
   static_assert(NQ == SS::RTS, "one B / J register per 16-row tile");
@@ -114,11 +117,16 @@ __global__ __launch_bounds__(ScanShape<D>::NT) void scan_kernel(ScanPair p) {
   // A frame's operands come in four parts, so that a step can issue the
   // loads of the frame PD steps ahead part by part between its own k-steps:
   // part 0: N's k-slices 0, 1; part 1: k-slices 2, 3; part 2: B; part 3: alpha.
+  // What a frame slot holds after N (or the SANA-WM transition): J_t in
+  // accumulator order at byte 2 d^2 (frame_kernel), B_t row-major at byte
+  // 4 d^2 (the Newton comparator), or B' in accumulator order at byte 4 d^2
+  // (SANA-WM).  The chunk scan reads frame slots only for the text step.
+  const int form = MODE == kSanaScan ? 2 : (MODE == kFrameScanB || (MODE == kChunkScan && p.bform)) ? 1 : 0;
   auto load_part = [&](FrameRegs<D>& fr, int slot, const float* alpha_row, int part) {
     const float* base = frames + (size_t)slot * slot_floats;
     const _Float16* nf = reinterpret_cast<const _Float16*>(base);
-    const _Float16* bm = reinterpret_cast<const _Float16*>(base + D * D);
-    const f16x4* ba = reinterpret_cast<const f16x4*>(base + D * D);  // SANA-WM: B' in accumulator order
+    const _Float16* bm = reinterpret_cast<const _Float16*>(base + D * D);  // B_t, row-major
+    const f16x4* ba = reinterpret_cast<const f16x4*>(form == 0 ? base + D * D / 2 : base + D * D);
     // fragment order: one wavefront reads 64 consecutive 16-byte chunks
 #pragma unroll
     for (int kk = 0; kk < SS::KS; ++kk) {
@@ -134,10 +142,10 @@ __global__ __launch_bounds__(ScanShape<D>::NT) void scan_kernel(ScanPair p) {
     if (part == 2) {
 #pragma unroll
       for (int q = 0; q < NQ; ++q) {
-        if constexpr (MODE == kSanaScan)
-          fr.b[q] = ba[((r0 / 16 + q) * SS::NW + ct) * 64 + lane];
-        else
+        if (form == 1)
           fr.b[q] = *reinterpret_cast<const f16x4*>(bm + (size_t)(r0 + xrow + 16 * q) * D + xc0);
+        else
+          fr.b[q] = ba[((r0 / 16 + q) * SS::NW + ct) * 64 + lane];
       }
     }
     if (part == 3)
@@ -254,8 +262,13 @@ __global__ __launch_bounds__(ScanShape<D>::NT) void scan_kernel(ScanPair p) {
         for (int e = 0; e < 4; ++e) sS[(16 * rt + 4 * lg + e) * D + 16 * ct + lr] = acc[rt][e];
       }
       if (rec) {
+        bool fin = true;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) rec[(size_t)(r0 + 16 * rt + 4 * lg + e) * D + 16 * ct + lr] = acc[rt][e];
+        for (int e = 0; e < 4; ++e) {
+          rec[(size_t)(r0 + 16 * rt + 4 * lg + e) * D + 16 * ct + lr] = acc[rt][e];
+          fin = fin && __builtin_isfinite(acc[rt][e]);
+        }
+        if (!fin) atomicOr(a.status, VDA_DEV_NONFINITE);
       }
     }
     lds_barrier();
@@ -272,7 +285,7 @@ __global__ __launch_bounds__(ScanShape<D>::NT) void scan_kernel(ScanPair p) {
   if (!a.s_init && a.use_text) {
     FrameRegs<D> fr;
     load(fr, a.n, nullptr);
-    step(fr, nullptr, true, false, POST, [](int) {});  // S^T = (0 + B_T) N_T, SANA-WM: 0 T_T + B'_T
+    step(fr, nullptr, true, false, form != 1, [](int) {});  // S^T = 0 N_T + J_T (or (0 + B_T) N_T, or 0 T_T + B'_T)
   }
   for (int i = tid; i < ROWS * D; i += SS::NT) {
     const float s0 = a.scale * sS[i];
@@ -358,21 +371,23 @@ struct ComposeLds {
 }  // namespace
 
 // The chunk maps of every (head, chunk, direction).  One workgroup runs one
-// chain: its first half of wavefronts the d rows of Y (from I, no B), its
-// second half the d rows of X (from 0, with B); N and alpha of each frame
-// are staged once for both.  The product is taken transposed,
-// Z^T <- N X^T (N is symmetric), so that a lane's accumulators hold four
-// consecutive columns of one row of Z: the next step's X = Z Diag(alpha) + B
-// is then formed in registers and is already the B operand of the next
-// MFMAs, with the k order permuted so that k-slot group g covers columns
-// 32kk + 4g .. +3 and 32kk + 16 + 4g .. +3 (both operands agree on it).  N's
-// fragment order serves that order as two 8-byte LDS reads per operand.  N
-// and alpha of the next frame are fetched during the current frame's MFMAs
-// and staged into the other LDS buffer; one barrier per frame.  X enters the
-// MFMA as an f16 hi/lo pair on the X rows (J_c keeps float32 accuracy) and
-// as f16 on the Y rows (M_c: the product of contractions, whose rounding the
-// f16 store of M_c dominates).
-template <int D>
+// chain: its first half of wavefronts the d rows of Y (from I, no
+// injection), its second half the d rows of X (from 0, with the injection);
+// N and alpha of each frame are staged once for both.  A frame step is
+// Z <- (Z Diag(alpha)) N + J_t on slots holding N_t and J_t, or
+// Z <- (Z Diag(alpha) + B_t) N on slots holding N_t and B_t (BFORM, the
+// Newton comparator).  The product is taken transposed, Z^T <- N X^T (N is
+// symmetric), so that a lane's accumulators hold four consecutive columns of
+// one row of Z: the next step's X is then formed in registers and is already
+// the B operand of the next MFMAs, with the k order permuted so that k-slot
+// group g covers columns 32kk + 4g .. +3 and 32kk + 16 + 4g .. +3 (both
+// operands agree on it).  N's fragment order serves that order as two 8-byte
+// LDS reads per operand.  N and alpha of the next frame are fetched during
+// the current frame's MFMAs and staged into the other LDS buffer; one barrier
+// per frame.  X enters the MFMA as an f16 hi/lo pair on the X rows (J_c keeps
+// float32 accuracy) and as f16 on the Y rows (M_c: the product of
+// contractions, whose rounding the f16 store of M_c dominates).
+template <int D, bool BFORM>
 __global__ __launch_bounds__(ComposeShape<D>::NTH, 1) void compose_kernel(ScanPair p) {
   using CS = ComposeShape<D>;
   constexpr int MT = CS::MT, NTW = CS::NTW, KS = CS::KS, TP = CS::TP;
@@ -408,13 +423,27 @@ __global__ __launch_bounds__(ComposeShape<D>::NTH, 1) void compose_kernel(ScanPa
       if (c < CS::NCH) nreg[j] = src[c];
     }
     if (tid < D) areg = alpha_h[(size_t)(a.a + slot_of(i)) * D + tid];
-    if (jpart) {
+    if (jpart && BFORM) {  // B_t[row][4 consecutive columns], row-major at byte 4 d^2
       const _Float16* bm = reinterpret_cast<const _Float16*>(base + D * D);
 #pragma unroll
       for (int nt = 0; nt < NTW; ++nt)
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
           breg[nt][mt] = *reinterpret_cast<const f16x4*>(bm + (size_t)(n0 + 16 * nt + lr) * D + 16 * mt + 4 * lg);
+    } else if (jpart) {
+      // J_t[r][c .. c+3] from the accumulator order at byte 2 d^2 (four
+      // consecutive rows of one column per 8 bytes): element (r, c) sits in
+      // tile (r / 16, c / 16), lane 16 (r % 16 / 4) + c % 16, component r % 4
+      const _Float16* jm = reinterpret_cast<const _Float16*>(base + D * D / 2);
+#pragma unroll
+      for (int nt = 0; nt < NTW; ++nt)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          const int R = (n0 + 16 * nt) / 16;
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            breg[nt][mt][e] = jm[((size_t)(R * MT + mt) * 64 + 16 * (lr >> 2) + 4 * lg + e) * 4 + (lr & 3)];
+        }
     }
   };
   auto stage = [&](int buf) {
@@ -459,7 +488,8 @@ __global__ __launch_bounds__(ComposeShape<D>::NTH, 1) void compose_kernel(ScanPa
             for (int nt = 0; nt < NTW; ++nt)
 #pragma unroll
               for (int e = 0; e < 4; ++e) {
-                const float x = JP ? fmaf(acc[mt][nt][e], alv[e], (float)breg[nt][mt][e]) : acc[mt][nt][e] * alv[e];
+                const float x = (JP && BFORM) ? fmaf(acc[mt][nt][e], alv[e], (float)breg[nt][mt][e])
+                                              : acc[mt][nt][e] * alv[e];
                 const _Float16 hi = (_Float16)x;
                 xh[nt][kk][4 * half + e] = hi;
                 xl[nt][kk][4 * half + e] = JP ? (_Float16)(x - (float)hi) : (_Float16)0.f;
@@ -471,13 +501,15 @@ __global__ __launch_bounds__(ComposeShape<D>::NTH, 1) void compose_kernel(ScanPa
               for (int e = 0; e < 4; ++e) xh[nt][kk][4 * half + e] = xl[nt][kk][4 * half + e] = (_Float16)0.f;
           }
         }
-      // the next frame's loads are in flight during the MFMAs
-      if (i + 1 < P) fetch(i + 1);
-      // Z^T <- N X^T
+      // Z^T <- N X^T (+ J_t^T, the accumulators' start)
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int nt = 0; nt < NTW; ++nt) acc[mt][nt] = f32x4{0, 0, 0, 0};
+        for (int nt = 0; nt < NTW; ++nt)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[mt][nt][e] = (JP && !BFORM) ? (float)breg[nt][mt][e] : 0.f;
+      // the next frame's loads are in flight during the MFMAs
+      if (i + 1 < P) fetch(i + 1);
       const _Float16* nb = sN + buf * D * D;
 #pragma unroll
       for (int kk = 0; kk < KS; ++kk)
@@ -564,7 +596,10 @@ int launch_scan(const ScanPair& p, int d, hipStream_t stream) {
     const long blocks = (long)p.ndir * H * p.dir[0].C;  // one workgroup per chain
 #define VDA_COMPOSE(DD)                                                                               \
     if (d == DD) {                                                                                    \
-      hipLaunchKernelGGL((compose_kernel<DD>), dim3((unsigned)blocks), dim3(ComposeShape<DD>::NTH), 0, stream, p); \
+      if (p.bform)                                                                                    \
+        hipLaunchKernelGGL((compose_kernel<DD, true>), dim3((unsigned)blocks), dim3(ComposeShape<DD>::NTH), 0, stream, p); \
+      else                                                                                            \
+        hipLaunchKernelGGL((compose_kernel<DD, false>), dim3((unsigned)blocks), dim3(ComposeShape<DD>::NTH), 0, stream, p); \
       return 0;                                                                                       \
     }
     VDA_COMPOSE(16) VDA_COMPOSE(32) VDA_COMPOSE(64) VDA_COMPOSE(128)
@@ -577,7 +612,8 @@ int launch_scan(const ScanPair& p, int d, hipStream_t stream) {
     hipLaunchKernelGGL((scan_kernel<DD, MM>), dim3((unsigned)blocks), dim3(ScanShape<DD>::NT), 0, stream, p); \
     return 0;                                                                                        \
   }
-#define VDA_SCAN_D(DD) VDA_SCAN(DD, kFrameScan) VDA_SCAN(DD, kChunkScan) VDA_SCAN(DD, kSanaScan)
+#define VDA_SCAN_D(DD) \
+  VDA_SCAN(DD, kFrameScan) VDA_SCAN(DD, kFrameScanB) VDA_SCAN(DD, kChunkScan) VDA_SCAN(DD, kSanaScan)
   VDA_SCAN_D(16) VDA_SCAN_D(32) VDA_SCAN_D(64) VDA_SCAN_D(128)
 #undef VDA_SCAN_D
 #undef VDA_SCAN

@@ -38,10 +38,9 @@ VDA_DEV_NONFINITE, VDA_DEV_PIVOT = 1, 2
 DTYPES = {"f32": VDA_F32, "bf16": VDA_BF16, "f16": VDA_F16}
 
 EXPORTS = ("vda_workspace_bytes", "vda_state_count", "vda_index_map", "vda_index_map_device", "vda_prepare_frames",
-           "vda_frame_stats", "vda_factor_frames", "vda_compose_chunks", "vda_scan_fwd", "vda_scan_rev", "vda_scan_bidir",
+           "vda_compose_chunks", "vda_scan_fwd", "vda_scan_rev", "vda_scan_bidir",
            "vda_readout", "vda_readout_gated", "vda_softmax_branch", "vda_forward", "vda_forward_noalloc",
-           "vda_device_status",
-           "vda_status_string", "vda_last_error")
+           "vda_stream_read", "vda_device_status", "vda_status_string", "vda_last_error")
 
 
 class vda_desc(ctypes.Structure):
@@ -80,9 +79,6 @@ def load(path: str | None = None):
         "vda_index_map_device": [D, c_void_p, c_void_p, c_void_p],
         "vda_prepare_frames": [D, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                c_void_p, c_size_t, c_void_p],
-        "vda_frame_stats": [D, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
-                            c_void_p, c_size_t, c_void_p],
-        "vda_factor_frames": [D, c_void_p, c_size_t, c_void_p],
         "vda_compose_chunks": [D, c_void_p, c_size_t, c_void_p, c_void_p],
         "vda_scan_fwd": [D, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p],
         "vda_scan_rev": [D, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p],
@@ -96,6 +92,7 @@ def load(path: str | None = None):
                         c_void_p, c_void_p, c_size_t, c_void_p, c_void_p, c_void_p, c_void_p],
         "vda_forward_noalloc": [D, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                 c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p],
+        "vda_stream_read": [c_void_p, c_size_t, c_void_p, c_int32, c_void_p],
         "vda_device_status": [D, c_void_p, c_void_p, POINTER(c_int32)],
     }
     for name, argt in sig.items():
@@ -194,19 +191,6 @@ def vda_prepare_frames(desc, k, v, beta, k_text, v_text, beta_text, ws, ws_bytes
                                      _ptr(v_text), _ptr(beta_text), _ptr(ws), ws_bytes, _stream(stream)))
 
 
-def vda_frame_stats(desc, k, v, beta, k_text, v_text, beta_text, ws, ws_bytes=None, stream=None):
-    if ws_bytes is None:
-        ws_bytes = ws.numel() * ws.element_size()
-    _check(load().vda_frame_stats(ctypes.byref(desc), _ptr(k), _ptr(v), _ptr(beta), _ptr(k_text),
-                                  _ptr(v_text), _ptr(beta_text), _ptr(ws), ws_bytes, _stream(stream)))
-
-
-def vda_factor_frames(desc, ws, ws_bytes=None, stream=None):
-    if ws_bytes is None:
-        ws_bytes = ws.numel() * ws.element_size()
-    _check(load().vda_factor_frames(ctypes.byref(desc), _ptr(ws), ws_bytes, _stream(stream)))
-
-
 def vda_compose_chunks(desc, ws, alpha, ws_bytes=None, stream=None):
     if ws_bytes is None:
         ws_bytes = ws.numel() * ws.element_size()
@@ -260,6 +244,11 @@ def vda_forward_noalloc(desc, q, k, v, beta, alpha, k_text, v_text, beta_text, s
     _check(load().vda_forward_noalloc(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(alpha),
                                       _ptr(k_text), _ptr(v_text), _ptr(beta_text), _ptr(states_fwd),
                                       _ptr(states_rev), _ptr(out), _ptr(status), _stream(stream)))
+
+
+def vda_stream_read(src, sink, blocks, stream=None):
+    """Read every byte of the device tensor src (measurement aid)."""
+    _check(load().vda_stream_read(_ptr(src), src.numel() * src.element_size(), _ptr(sink), blocks, _stream(stream)))
 
 
 def vda_device_status(desc, ws, stream=None) -> int:

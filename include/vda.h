@@ -84,8 +84,8 @@ enum {
                               S_t = S_{t-1} Diag(alpha_t) (I - A_t/U) + B_t/sqrt(U)
                               (keys scaled by 1/sqrt(U), U the tokens of the frame;
                               N_text for the text write, so S^T = B_T/sqrt(N_text));
-                              vda_factor_frames then forms -A_t/U and B_t/sqrt(U)
-                              in place of (I + A_t)^{-1} and B_t; not with
+                              vda_prepare_frames then stores -A_t/U and
+                              B_t/sqrt(U) in place of N_t and J_t; not with
                               VDA_CHUNK_SCAN */,
   VDA_NEWTON = 1u << 4     /* (I + A_t)^{-1} by Newton iteration
                               [VDN 实验结果, weaknesses: Newton iteration in place
@@ -98,7 +98,7 @@ enum {
 
 /* bits of the device status word */
 enum {
-  VDA_DEV_NONFINITE = 1, /* a frame statistic or factor was NaN/Inf */
+  VDA_DEV_NONFINITE = 1, /* a frame statistic, factor or recorded state was NaN/Inf */
   VDA_DEV_PIVOT = 2      /* I + A_t had a pivot <= 0 (not positive definite) */
 };
 
@@ -122,9 +122,10 @@ typedef struct vda_desc {
 } vda_desc;
 
 /* Bytes of device workspace vda_prepare_frames needs for `desc` (host only,
- * enqueues nothing).  The workspace carries, per head, the factor
- * (I + A_t)^{-1} and B_t of every scanned frame and of the text "frame", plus
- * the device status word, from vda_prepare_frames to the scans.  With
+ * enqueues nothing).  The workspace carries, per head, N_t = (I + A_t)^{-1}
+ * and J_t = B_t N_t of every scanned frame and of the text "frame" (8 d^2
+ * bytes per slot), plus the device status word, from vda_prepare_frames to
+ * the scans.  With
  * VDA_CHUNK_SCAN it also holds the chunk maps of both directions
  * (4 d^2 bytes per head, direction and chunk). */
 int vda_workspace_bytes(const vda_desc* desc, size_t* bytes);
@@ -152,32 +153,30 @@ int vda_index_map_device(const vda_desc* desc, int32_t* chunk_rows, int32_t* fra
 
 /* Frame statistics and factorisation [VDN 方法步骤详情 step (3)]: for every
  * head and every scanned frame t (and the text tokens when text_tokens > 0)
- * computes A_t and B_t over the frame's U tokens, factorises I + A_t and
- * stores N_t = (I + A_t)^{-1} and B_t in `ws`.  Also clears the device status
- * word.
+ * computes A_t = K_t^T Diag(beta_t) K_t and B_t = V_t^T Diag(beta_t) K_t
+ * over the frame's U tokens, factorises I + A_t and stores, per slot,
+ *   N_t = (I + A_t)^{-1}  and  J_t = B_t N_t
+ * in `ws` (f16 each), so that the frame write is
+ * S_t = (S_{t-1} Diag(alpha_t)) N_t + J_t [VDN 核心方法 para 2].  Also
+ * clears the device status word.  With VDA_NEWTON the slots hold N_t (by
+ * Newton iteration) and B_t instead, and the scans form
+ * (S_{t-1} Diag(alpha_t) + B_t) N_t; with VDA_SANA_WM they hold the
+ * comparator's -A_t/U and B_t/sqrt(U).
  *  k, v        [H][T][U][d] in_dtype (anchor frames are not read)
  *  beta        [H][T][U] float32
  *  k_text, v_text [H][N_text][d] in_dtype; beta_text [H][N_text] float32
  *              (all three may be NULL when text_tokens == 0)
- *  ws          device workspace of ws_bytes >= vda_workspace_bytes(desc). */
+ *  ws          device workspace of ws_bytes >= vda_workspace_bytes(desc),
+ *              256-byte aligned.
+ * Value range: the kernels take K, beta*K and beta*V as f16 operands and
+ * keep N_t, J_t (and B_t) as f16, so every |beta_u v_u|, every entry of
+ * B_t (a sum over the frame's tokens of beta_u v_u k_u^T) and of J_t, and
+ * every state entry must stay below 65504 in magnitude; a value that does
+ * not becomes non-finite and sets VDA_DEV_NONFINITE.  L2-normalised keys and
+ * values of unit scale are far inside this range. */
 int vda_prepare_frames(const vda_desc* desc, const void* k, const void* v, const float* beta,
                        const void* k_text, const void* v_text, const float* beta_text,
                        void* ws, size_t ws_bytes, void* stream);
-
-/* The two halves of vda_prepare_frames, for callers (and profilers) that
- * enqueue them separately; together, in this order on one stream, they do
- * exactly what vda_prepare_frames does.
- * vda_frame_stats [VDN 方法步骤详情 step (3)]: clears the device status word,
- * computes A_t and B_t of every scanned frame and of the text tokens, and
- * stores B_t and the upper triangle of A_t in `ws` (arguments as for
- * vda_prepare_frames).
- * vda_factor_frames [VDN 核心方法 para 2]: replaces every A_t in `ws` by
- * N_t = (I + A_t)^{-1}; `ws` must hold the output of vda_frame_stats for the
- * same desc. */
-int vda_frame_stats(const vda_desc* desc, const void* k, const void* v, const float* beta,
-                    const void* k_text, const void* v_text, const float* beta_text, void* ws,
-                    size_t ws_bytes, void* stream);
-int vda_factor_frames(const vda_desc* desc, void* ws, size_t ws_bytes, void* stream);
 
 /* Chunk composition [VDN 方法步骤详情 step (4): chunk-level scan
  * S_out = S_in M_chunk + J_chunk], for descriptors with VDA_CHUNK_SCAN: with
@@ -193,7 +192,8 @@ int vda_factor_frames(const vda_desc* desc, void* ws, size_t ws_bytes, void* str
 int vda_compose_chunks(const vda_desc* desc, void* ws, size_t ws_bytes, const float* alpha, void* stream);
 
 /* Forward scan [VDN 核心方法 para 1; 方法步骤详情 step (4)]: starting from
- * S_0 = text_init_scale * S_init, applies S_t = (S_{t-1} Diag(alpha_t) + B_t) N_t
+ * S_0 = text_init_scale * S_init, applies the frame write
+ * S_t = (S_{t-1} Diag(alpha_t) + B_t)(I + A_t)^{-1}, as (S_{t-1} Diag(alpha_t)) N_t + J_t
  * over the scanned frames in increasing order and records vda_state_count()
  * states per head into `states` [H][count][d][d] float32 (states[h][0] = S_0).
  *  S_init = s_init [H][d][d] float32 when s_init != NULL, else S^T built from
@@ -290,6 +290,14 @@ int vda_forward(const vda_desc* desc, const void* q, const void* k, const void* 
 int vda_forward_noalloc(const vda_desc* desc, const void* q, const void* k, const void* v, const float* beta,
                         const float* alpha, const void* k_text, const void* v_text, const float* beta_text,
                         float* states_fwd, float* states_rev, void* out, int32_t* status, void* stream);
+
+/* Measurement aid (not part of the path): reads `bytes` (a multiple of 16)
+ * of device memory at `src` with 16-byte loads in `blocks` workgroups of 256
+ * threads and writes one word per workgroup to sink [blocks] (device
+ * uint32).  Timed around a large buffer it gives the read bandwidth a plain
+ * streaming kernel reaches on the device, the practical ceiling of the
+ * bandwidth-bound kernels of the path. */
+int vda_stream_read(const void* src, size_t bytes, uint32_t* sink, int32_t blocks, void* stream);
 
 /* Synchronises `stream`, then copies the device status word of `ws` into
  * *flags (VDA_DEV_* bits; 0 = no fault).  For tests and diagnostics. */

@@ -49,27 +49,33 @@ def test_softmax_work_counts_the_oracles_key_sets(name, over):
 
 
 def test_h3_work_figures():
-    """The H3-shaped workload's figures quoted with the measurements: 343.2
-    GFLOP per step (the scans, readouts, statistics, solves and the text
-    state); the statistics kernel's 1,254,647,808 algorithmic bytes
-    (K, V bf16 and beta of 24 x 100 frames of 1008 tokens plus 512 text
-    tokens per head) and the readout's 1.252 GB (Q bf16, alpha, and every
-    output row in bf16, anchors included)."""
+    """The H3-shaped workload's figures quoted with the measurements.  FLOPs
+    per step: the statistics, solves, both scan directions and the text
+    state, with the readout counted as one product per frame with the merged
+    operand W_t (264.0 GFLOP), and with the forward and reverse reads
+    counted as two products (343.2 GFLOP, the count the measurement plan
+    states).  The prepare kernel's 1,254,647,808 algorithmic bytes (K, V
+    bf16 and beta of 24 x 100 frames of 1008 tokens plus 512 text tokens per
+    head) and the readout's 1.252 GB (Q bf16, alpha, and every output row in
+    bf16, anchors included)."""
     bm = _bench()
     cfg = inp.CONFIG_BY_NAME["h3"]
-    flops, _ = bm.algorithmic_work(cfg)
+    flops, _, flops_two = bm.algorithmic_work(cfg)
     U, d, Nt = 1008, 128, 512
-    per_frame = (2 * U * d * d      # A = K^T Diag(beta) K
-                 + 2 * U * d * d    # B = V^T Diag(beta) K
-                 + d ** 3           # N = (I + A)^-1
-                 + 2 * 2 * d ** 3   # the frame write in the forward and the reverse scan
-                 + 2 * 2 * U * d * d)  # the readout's forward and reverse state products
+    common = (2 * U * d * d      # A = K^T Diag(beta) K
+              + 2 * U * d * d    # B = V^T Diag(beta) K
+              + d ** 3           # N = (I + A)^-1
+              + 2 * 2 * d ** 3)  # the frame write in the forward and the reverse scan
+    merged = common + 2 * d * d + 2 * U * d * d      # W_t formed, then one product with Q
+    two = common + 2 * 2 * U * d * d                 # the forward and reverse state products
     per_text = 4 * Nt * d * d + d ** 3 + 2 * d ** 3  # A_T, B_T, their solve, S^T = B_T N_T
-    assert flops == 24 * (100 * per_frame + per_text)
-    assert round(flops / 1e9, 1) == 343.2
+    assert flops == 24 * (100 * merged + per_text)
+    assert flops_two == 24 * (100 * two + per_text)
+    assert round(flops_two / 1e9, 1) == 343.2
+    assert round(flops / 1e9, 1) == 264.0
     kb = bm.kernel_bytes(cfg)
     frame_bytes = 1008 * 128 * 2 * 2 + 1008 * 4
     text_bytes = 512 * 128 * 2 * 2 + 512 * 4
-    assert kb["stats_kernel"] == 24 * (100 * frame_bytes + text_bytes) == 1_254_647_808
+    assert kb["frame_kernel"] == kb["stats_kernel"] == 24 * (100 * frame_bytes + text_bytes) == 1_254_647_808
     assert kb["readout_kernel"] == 24 * (100 * (1008 * 128 * 2 + 128 * 4) + 102 * 1008 * 128 * 2)
     assert round(kb["readout_kernel"] / 1e9, 3) == 1.252

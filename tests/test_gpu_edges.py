@@ -24,8 +24,6 @@ def test_zero_heads_every_entry_point_is_a_no_op():
         assert wsb == 256
         ws = torch.full((64,), 7.0, device="cuda")
         vda.vda_prepare_frames(d, k, v, beta, kt, vt, bt, ws, wsb)
-        vda.vda_frame_stats(d, k, v, beta, kt, vt, bt, ws, wsb)
-        vda.vda_factor_frames(d, ws, wsb)
         if flags.get("chunk_scan"):
             vda.vda_compose_chunks(d, ws, alpha, ws_bytes=wsb)
         vda.vda_scan_bidir(d, ws, alpha, None, sf, sr)
