@@ -204,9 +204,11 @@ def write_traffic(fetch_csv, write_csv, cal_fetch_csv, cal_write_csv):
             kept = json.load(fh).get("kernels", {})
     except (OSError, ValueError):
         kept = {}
+    # (entries whose sources have changed since are dropped)
     out = {"calibration": {"copy_bytes": COPY_BYTES, "fetch_kib": cf, "write_kib": cw,
                            "fetch_factor": round(ff, 4), "write_factor": round(wf, 4)},
-           "kernels": {k: v for k, v in kept.items() if k in KERNELS and not (k in f and k in w)}}
+           "kernels": {k: v for k, v in kept.items()
+                       if k in KERNELS and not (k in f and k in w) and v.get("src_hash") == _src_hash(k)}}
     for k in KERNELS:
         if k in f and k in w:
             fb, wb = f[k] * 1024.0 * ff, w[k] * 1024.0 * wf

@@ -414,6 +414,9 @@ __global__ __launch_bounds__(ComposeShape<D>::NTH, 1) void compose_kernel(ScanPa
   f16x8 nreg[CS::CPT];
   float areg = 0.f;
   f16x4 breg[NTW][MT];
+  f16x4 eye4;  // the 16 x 16 identity as a B operand: lane (n, g) holds rows 4g .. 4g+3 of column n
+#pragma unroll
+  for (int e = 0; e < 4; ++e) eye4[e] = (_Float16)(4 * lg + e == lr ? 1.f : 0.f);
   auto fetch = [&](int i) {
     const float* base = frames + (size_t)slot_of(i) * slot_floats;
     const f16x8* src = reinterpret_cast<const f16x8*>(base);
@@ -431,19 +434,15 @@ __global__ __launch_bounds__(ComposeShape<D>::NTH, 1) void compose_kernel(ScanPa
         for (int mt = 0; mt < MT; ++mt)
           breg[nt][mt] = *reinterpret_cast<const f16x4*>(bm + (size_t)(n0 + 16 * nt + lr) * D + 16 * mt + 4 * lg);
     } else if (jpart) {
-      // J_t[r][c .. c+3] from the accumulator order at byte 2 d^2 (four
-      // consecutive rows of one column per 8 bytes): element (r, c) sits in
-      // tile (r / 16, c / 16), lane 16 (r % 16 / 4) + c % 16, component r % 4
-      const _Float16* jm = reinterpret_cast<const _Float16*>(base + D * D / 2);
+      // J_t in the accumulator order at byte 2 d^2: this lane's f16x4 of
+      // tile (R, mt), i.e. J[16R + 4 lg + e][16 mt + lr], loaded whole; it is
+      // the transpose of what the accumulators need, which the product with
+      // the identity at the start of each step provides (exactly)
+      const f16x4* jm = reinterpret_cast<const f16x4*>(base + D * D / 2);
 #pragma unroll
       for (int nt = 0; nt < NTW; ++nt)
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          const int R = (n0 + 16 * nt) / 16;
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            breg[nt][mt][e] = jm[((size_t)(R * MT + mt) * 64 + 16 * (lr >> 2) + 4 * lg + e) * 4 + (lr & 3)];
-        }
+        for (int mt = 0; mt < MT; ++mt) breg[nt][mt] = jm[(size_t)(((n0 + 16 * nt) / 16) * MT + mt) * 64 + lane];
     }
   };
   auto stage = [&](int buf) {
@@ -501,13 +500,18 @@ __global__ __launch_bounds__(ComposeShape<D>::NTH, 1) void compose_kernel(ScanPa
               for (int e = 0; e < 4; ++e) xh[nt][kk][4 * half + e] = xl[nt][kk][4 * half + e] = (_Float16)0.f;
           }
         }
-      // Z^T <- N X^T (+ J_t^T, the accumulators' start)
+      // Z^T <- N X^T (+ J_t^T, the accumulators' start: the loaded tile read
+      // as an A operand is J_t^T's tile, and its product with the identity
+      // lays it out as an accumulator)
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int nt = 0; nt < NTW; ++nt)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) acc[mt][nt][e] = (JP && !BFORM) ? (float)breg[nt][mt][e] : 0.f;
+        for (int nt = 0; nt < NTW; ++nt) {
+          if constexpr (JP && !BFORM)
+            acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x16f16(breg[nt][mt], eye4, f32x4{0, 0, 0, 0}, 0, 0, 0);
+          else
+            acc[mt][nt] = f32x4{0, 0, 0, 0};
+        }
       // the next frame's loads are in flight during the MFMAs
       if (i + 1 < P) fetch(i + 1);
       const _Float16* nb = sN + buf * D * D;
