@@ -138,11 +138,15 @@ struct InBF16 { typedef u16 T; static constexpr int bytes = 2; };
 // [0, 256): device status word (int32) + padding.
 // then, per head h and frame slot f (f < n: scanned frame f; f == n: text),
 // 8 d^2 bytes: N = (I + A)^{-1} as a d x d f16 array in MFMA fragment order
-// (below) in the first 2 d^2 bytes, then (at byte 4 d^2) B as a d x d f16
-// array, row-major.  Between the two prepare kernels the first half holds the
-// upper-triangle 16x16 tiles of A (float32) in accumulator order: tile
-// (ri, cj), cj >= ri, lane l holds A[16ri + 4(l/16) + e][16cj + l % 16],
-// e = 0..3, as 16 bytes at float offset ((ri * d/16 + cj) * 64 + l) * 4.
+// (below) in the first 2 d^2 bytes, then (at byte 2 d^2) J = B N as a d x d
+// f16 array in the scan's accumulator order (the f16x4 at (R * d/16 + c) *
+// 64 + l holds J[16R + 4(l/16) + e][16c + l % 16]).  The comparators use the
+// upper half: the Newton path keeps B (f16, row-major) at byte 4 d^2, the
+// SANA-WM path B' = B / sqrt(U) there; between their two prepare kernels the
+// first half holds the upper-triangle 16x16 tiles of A (float32) in
+// accumulator order: tile (ri, cj), cj >= ri, lane l holds
+// A[16ri + 4(l/16) + e][16cj + l % 16], e = 0..3, as 16 bytes at float offset
+// ((ri * d/16 + cj) * 64 + l) * 4.
 constexpr size_t kWsHeader = 256;
 
 __host__ __device__ inline size_t ws_slot_floats(int d) { return (size_t)2 * d * d; }
