@@ -469,6 +469,8 @@ __global__ __launch_bounds__(kThreads, 2) void frame_kernel(PrepArgs args) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lr = lane & 15, lg = lane >> 4;
+  // wavefront `wave` owns column tile wave + 4 m (always, when 4 divides RT)
+  auto owns = [&](int m) { return RT % 4 == 0 || wave + 4 * m < RT; };
 
   const int h = blockIdx.x / args.cnt;
   const int f = args.s0 + (blockIdx.x - h * args.cnt);
@@ -562,7 +564,7 @@ __global__ __launch_bounds__(kThreads, 2) void frame_kernel(PrepArgs args) {
 #pragma unroll
       for (int m = 0; m < NC; ++m) {
         const int i = wave + 4 * m;
-        if (i < RT) {
+        if (owns(m)) {
           bK[m] = *reinterpret_cast<const f16x8*>(sK + tile_off(16 * i + lr, grp));
           bBK[m] = *reinterpret_cast<const f16x8*>(sBK + tile_off(16 * i + lr, grp));
         }
@@ -573,7 +575,7 @@ __global__ __launch_bounds__(kThreads, 2) void frame_kernel(PrepArgs args) {
         const f16x8 aV = *reinterpret_cast<const f16x8*>(sBV + tile_off(16 * c + lr, grp));
 #pragma unroll
         for (int m = 0; m < NC; ++m) {
-          if (wave + 4 * m < RT) {
+          if (owns(m)) {
             Tt[m][c] = mfma_f16(aK, bBK[m], Tt[m][c]);
             Xt[m][c] = mfma_f16(aV, bK[m], Xt[m][c]);
           }
@@ -668,7 +670,7 @@ __global__ __launch_bounds__(kThreads, 2) void frame_kernel(PrepArgs args) {
     int mine = 0;  // own columns other than p
 #pragma unroll
     for (int m = 0; m < NC; ++m)
-      if (wave + 4 * m < RT && wave + 4 * m != p) mine |= 1 << m;
+      if (owns(m) && wave + 4 * m != p) mine |= 1 << m;
     if (q < RT && wave == owner1) {  // the next pivot's column first
       update(1 << mq);
       pivot_and_stage(q, mq);
@@ -687,7 +689,7 @@ __global__ __launch_bounds__(kThreads, 2) void frame_kernel(PrepArgs args) {
 #pragma unroll
   for (int m = 0; m < NC; ++m) {
     const int i = wave + 4 * m;
-    if (i >= RT) continue;
+    if (!owns(m)) continue;
 #pragma unroll
     for (int c = 0; c < RT; ++c) {
 #pragma unroll
@@ -711,7 +713,7 @@ __global__ __launch_bounds__(kThreads, 2) void frame_kernel(PrepArgs args) {
     lds_barrier();  // the previous readers of this memory are done
 #pragma unroll
     for (int m = 0; m < NC; ++m)
-      if (wave + 4 * m < RT) {
+      if (owns(m)) {
 #pragma unroll
         for (int rr = 0; rr < kRows; ++rr)
           bpk[(rr * RT + wave + 4 * m) * 64 + lane] = to_left_f16(Xt[m][r0 + rr], eye_hi, eye_lo);
@@ -720,7 +722,7 @@ __global__ __launch_bounds__(kThreads, 2) void frame_kernel(PrepArgs args) {
 #pragma unroll
     for (int m = 0; m < NC; ++m) {
       const int i = wave + 4 * m;
-      if (i >= RT) continue;
+      if (!owns(m)) continue;
       f32x4 acc[kRows];
 #pragma unroll
       for (int rr = 0; rr < kRows; ++rr) acc[rr] = f32x4{0, 0, 0, 0};
