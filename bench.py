@@ -119,14 +119,22 @@ KERNEL_SRC = {"frame_kernel": "vda_prepare.hip", "stats_kernel": "vda_prepare.hi
               "readout_gated": "vda_readout.hip"}
 
 
+def _code_only(text):
+    """C++ source without comments and blank lines, so that a change to
+    comments alone does not count as a change of the kernel."""
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(l.rstrip() for l in text.splitlines() if l.strip())
+
+
 def _src_hash(kernel):
-    """Hash of the sources a kernel is compiled from (its file and the
-    shared headers)."""
+    """Hash of the code a kernel is compiled from (its file and the shared
+    headers, comments left out)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "frame_wise_delta_amd", "csrc")
     for name in (KERNEL_SRC[kernel], "vda_common.h", "vda_kernels.h"):
-        with open(os.path.join(csrc, name), "rb") as f:
-            h.update(name.encode() + f.read())
+        with open(os.path.join(csrc, name), encoding="utf-8") as f:
+            h.update(name.encode() + _code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 

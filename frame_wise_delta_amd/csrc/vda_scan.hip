@@ -1,24 +1,28 @@
 // Forward / reverse VDA scan: the only sequential part of the path.
 //
-//   S_t = (S_{t-1} Diag(alpha_t) + B_t) N_t,   N_t = (I + A_t)^{-1}
+//   S_t = (S_{t-1} Diag(alpha_t) + B_t) N_t = (S_{t-1} Diag(alpha_t)) N_t + J_t,
+//   N_t = (I + A_t)^{-1},  J_t = B_t N_t
 //
 // ("Video DeltaNet: A Video-Native Hybrid Attention for Livestream Video
 // Generation", core-method section, paragraph 2: closed-form frame write;
 // method-steps section, step (4): both scans start from the text state.)
 //
-// The d_v rows of S evolve independently (row i: s_t = (s_{t-1} * alpha_t +
-// b_t) N_t), so one (head, direction) chain is split over d/32 workgroups of
+// The d_v rows of S evolve independently (row i: s_t = (s_{t-1} * alpha_t) N_t
+// + j_t), so one (head, direction) chain is split over d/32 workgroups of
 // 32 rows each (16 for d = 16); the row blocks of a head are mapped to one
 // XCD so that they share that XCD's L2 copy of N_t.  A workgroup keeps its
 // 32 x d slice of S in LDS in float32 and runs d/16 wavefronts, one per
 // 16-column output tile.
-// Per frame, the VALU forms X = S Diag(alpha) + B (float32) and splits it into
-// an f16 hi/lo pair in LDS; each wavefront computes its 16 x 16 tile of X N
-// on MFMA as X_hi N + X_lo N, N being stored by the prepare kernel as f16 in
-// MFMA fragment order and read as rows (N is symmetric).  Each workgroup
-// pulls N and its rows of B through its CU's vector-memory path once per
-// frame, and that is what bounds a step, so N and B are kept to 2 bytes per
-// entry (f16).
+// Per frame, the VALU forms X = S Diag(alpha) (float32) and splits it into an
+// f16 hi/lo pair in LDS; each wavefront computes its 16 x 16 tile of X N on
+// MFMA as X_hi N + X_lo N with the accumulators starting from its tile of
+// J_t, N and J_t being stored by the prepare kernel as f16 (N in MFMA
+// fragment order, read as rows since N is symmetric; J_t in this kernel's
+// accumulator order).  The comparators' slots hold B_t (the Newton
+// comparator) or B' (SANA-WM) instead of J_t, which the VALU adds into X
+// before the product.  Each workgroup pulls N and its rows of J_t through its
+// CU's vector-memory path once per frame, and that is what bounds a step, so
+// both are kept to 2 bytes per entry (f16).
 // The chain is bound by the latency of these per-frame operand loads, so
 // frames are prefetched three or four steps ahead into registers, their
 // loads issued part by part between the k-steps of the current step's

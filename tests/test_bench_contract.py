@@ -79,3 +79,14 @@ def test_h3_work_figures():
     assert kb["frame_kernel"] == kb["stats_kernel"] == 24 * (100 * frame_bytes + text_bytes) == 1_254_647_808
     assert kb["readout_kernel"] == 24 * (100 * (1008 * 128 * 2 + 128 * 4) + 102 * 1008 * 128 * 2)
     assert round(kb["readout_kernel"] / 1e9, 3) == 1.252
+
+
+def test_kernel_code_hash_ignores_comments_only():
+    """The traffic table is keyed by a hash of each kernel's code: comments
+    and blank lines do not change it, a change of code does."""
+    bm = _bench()
+    code = "int f(int a) {\n  return a + 1;  // one more\n}\n"
+    assert bm._code_only(code) == bm._code_only("/* a header\n   comment */\n" + code.replace("// one more", "// else"))
+    assert bm._code_only(code) == bm._code_only(code.replace("\n", "\n\n"))
+    assert bm._code_only(code) != bm._code_only(code.replace("a + 1", "a + 2"))
+    assert bm._code_only("x = 1; /* a */ y = 2;") == "x = 1;  y = 2;"
