@@ -13,8 +13,12 @@
 // one query block (a chunk's frames, or one anchor frame), eight wavefronts
 // of 32 queries, so that every key tile is fetched and staged once for 256
 // queries.  Keys stream through LDS in 64-key tiles, segment by segment
-// (window frames, anchor frames, text); the next two tiles' loads are in
-// flight, in two register sets, during the current tile's work.  The scores are formed transposed,
+// (window frames, anchor frames, text), rotating through three LDS buffers
+// with one barrier per tile; the next two tiles' loads are in flight, in two
+// register sets, during the current tile's work.  The second wavefront of
+// each SIMD runs one step behind the first (it accumulates the previous tile
+// before it scores the current one), so that one wavefront's exponentials
+// overlap the other's MFMAs.  The scores are formed transposed,
 // S^T = K Q^T (16x16x32 bf16 MFMA), so that a wavefront's accumulator lane
 // holds four consecutive keys of one query; two such tiles make the B
 // operand of a 16x16x32 MFMA.  The output is accumulated transposed as well,
@@ -51,6 +55,12 @@ __device__ __forceinline__ float rows4_max(float v) {
   return fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
 }
 
+// One key tile's P (f16) for a wavefront's two 16-query tiles: v[kp][qt]
+// holds keys 32 kp + 4g + e, then 32 kp + 16 + 4g + e (lane group g).
+struct PTile {
+  f16x8 v[2][2];
+};
+
 template <int OUT>
 __device__ __forceinline__ void store_out4(void* base, size_t idx, f32x4 v) {
   if constexpr (OUT == VDA_F32) {
@@ -78,8 +88,9 @@ __global__ __launch_bounds__(kAT, 1) void attn_kernel(AttnArgs a) {
   constexpr int CPR = D / 8;   // 16-byte chunks per key row
   constexpr int NCH = kKT * CPR;               // 16-byte chunks per tile (K and V each)
   constexpr int LPT = (NCH + kAT - 1) / kAT;   // chunks per thread per tile
-  __shared__ __attribute__((aligned(16))) u16 sK[kKT * KP];
-  __shared__ __attribute__((aligned(16))) _Float16 sV[kKT * KP];
+  // three tile buffers: tile j lives in buffer j % 3 (see the loop below)
+  __shared__ __attribute__((aligned(16))) u16 sK[3 * kKT * KP];
+  __shared__ __attribute__((aligned(16))) _Float16 sV[3 * kKT * KP];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int ln = lane & 15, lg = lane >> 4;
@@ -236,36 +247,12 @@ __global__ __launch_bounds__(kAT, 1) void attn_kernel(AttnArgs a) {
   // 16 dt + 4 (j & 3) .. +3
   const int vrow = 4 * lg + (ln >> 2), vcol = 4 * (ln & 3);
 
-  // tiles alternate between the two register sets: set j % 2 holds tile j
-  // until it is staged, then receives tile j + 2
-  int n_t[2] = {0, 0};
-  if (all_tiles > 0) n_t[0] = fetch(0, std::integral_constant<int, 0>{});
-  if (all_tiles > 1) n_t[1] = fetch(1, std::integral_constant<int, 1>{});
-  auto tile_step = [&](int j, auto set) {
-    constexpr int S = decltype(set)::value;
-    // ---- stage tile j: K as loaded, V converted to f16
-#pragma unroll
-    for (int i = 0; i < LPT; ++i) {
-      if (!chunk_live(i)) continue;
-      *reinterpret_cast<uint4*>(sK + loff[i]) = pk[S][i];
-      if constexpr (VF16) {
-        *reinterpret_cast<uint4*>(sV + loff[i]) = pv[S][i];
-      } else {  // bf16 V -> f16
-        const uint32_t u[4] = {pv[S][i].x, pv[S][i].y, pv[S][i].z, pv[S][i].w};
-        f16x8 hv;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          hv[2 * e] = (_Float16)__uint_as_float(u[e] << 16);
-          hv[2 * e + 1] = (_Float16)__uint_as_float(u[e] & 0xffff0000u);
-        }
-        *reinterpret_cast<f16x8*>(sV + loff[i]) = hv;
-      }
-    }
-    const int n_tile = n_t[S];
-    lds_barrier();
-    if (j + 2 < all_tiles) n_t[S] = fetch(j + 2, set);
-
-    // ---- S^T = K Q^T: 4 key sub-tiles x 2 query tiles
+  // S^T = K Q^T for tile buffer `buf`, masked past n_tile keys, then the
+  // online softmax: P (f16) into p, O and the row sums rescaled when a
+  // query's reference point moves
+  auto scores = [&](int buf, int n_tile) {
+    PTile p;
+    const u16* kb = sK + buf * (kKT * KP);
     f32x4 s[4][2];
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
@@ -273,13 +260,13 @@ __global__ __launch_bounds__(kAT, 1) void attn_kernel(AttnArgs a) {
       s[kt][1] = f32x4{0, 0, 0, 0};
 #pragma unroll
       for (int kk = 0; kk < KS; ++kk) {
-        const bf16x8 kf = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(sK + (16 * kt + ln) * KP + 32 * kk + 8 * lg));
+        const bf16x8 kf = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(kb + (16 * kt + ln) * KP + 32 * kk + 8 * lg));
         s[kt][0] = mfma_bf16(kf, qf[0][kk], s[kt][0]);
         s[kt][1] = mfma_bf16(kf, qf[1][kk], s[kt][1]);
       }
     }
-    // ---- online softmax; lane (n, g) holds keys 16 kt + 4g + e of query n.
-    // Scores stay unscaled; the running max is kept in scaled base-2 units.
+    // lane (n, g) holds keys 16 kt + 4g + e of query n.  Scores stay
+    // unscaled; the running max is kept in scaled base-2 units.
     if (n_tile < kKT) {  // last tile of a segment: keys past its end get no weight
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
@@ -287,7 +274,7 @@ __global__ __launch_bounds__(kAT, 1) void attn_kernel(AttnArgs a) {
         for (int e = 0; e < 4; ++e)
           if (16 * kt + 4 * lg + e >= n_tile) s[kt][0][e] = s[kt][1][e] = -INFINITY;
     }
-    f16x8 p[2][2];  // [key pair kp][query tile]: keys 32 kp + 4g + e, then 32 kp + 16 + 4g + e
+    // p[kp][qt]: keys 32 kp + 4g + e, then 32 kp + 16 + 4g + e
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt) {
       float mx = -INFINITY;
@@ -313,32 +300,92 @@ __global__ __launch_bounds__(kAT, 1) void attn_kernel(AttnArgs a) {
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          p[kt >> 1][qt][4 * (kt & 1) + e] = (_Float16)__builtin_amdgcn_exp2f(fmaf(s[kt][qt][e], sc, -m_new));
+          p.v[kt >> 1][qt][4 * (kt & 1) + e] = (_Float16)__builtin_amdgcn_exp2f(fmaf(s[kt][qt][e], sc, -m_new));
     }
-    // ---- O^T += V^T P^T on 16x16x32 MFMA: the k order of a 32-key pair is
-    // (16-key sub-tile 2kp, keys 4g .. 4g+3; sub-tile 2kp+1, keys 4g .. 4g+3)
-    // in lane group g, the same for the V^T operand (two transposing loads)
-    // and for P (two score accumulators)
+    return p;
+  };
+  // O^T += V^T P^T on 16x16x32 MFMA for tile buffer `buf`: the k order of a
+  // 32-key pair is (16-key sub-tile 2kp, keys 4g .. 4g+3; sub-tile 2kp+1,
+  // keys 4g .. 4g+3) in lane group g, the same for the V^T operand (two
+  // transposing loads) and for P (two score accumulators)
+  auto accumulate = [&](int buf, const PTile& p) {
+    const _Float16* vb = sV + buf * (kKT * KP);
 #pragma unroll
     for (int kp = 0; kp < 2; ++kp) {
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        const _Float16* src = sV + (32 * kp + vrow) * KP + 16 * dt + vcol;
+        const _Float16* src = vb + (32 * kp + vrow) * KP + 16 * dt + vcol;
         const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)src);
         const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(src + 16 * KP));
         const f16x8 vf = __builtin_bit_cast(f16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
-        o[0][dt] = mfma_f16(vf, p[kp][0], o[0][dt]);
-        o[1][dt] = mfma_f16(vf, p[kp][1], o[1][dt]);
+        o[0][dt] = mfma_f16(vf, p.v[kp][0], o[0][dt]);
+        o[1][dt] = mfma_f16(vf, p.v[kp][1], o[1][dt]);
       }
-      lsum[0] = mfma_f16(ones, p[kp][0], lsum[0]);
-      lsum[1] = mfma_f16(ones, p[kp][1], lsum[1]);
+      lsum[0] = mfma_f16(ones, p.v[kp][0], lsum[0]);
+      lsum[1] = mfma_f16(ones, p.v[kp][1], lsum[1]);
     }
-    lds_barrier();
   };
-  for (int j = 0; j < all_tiles; j += 2) {
-    tile_step(j, std::integral_constant<int, 0>{});
-    if (j + 1 < all_tiles) tile_step(j + 1, std::integral_constant<int, 1>{});
-  }
+
+  // Tiles alternate between the two register sets (set j % 2 holds tile j
+  // until it is staged, then receives tile j + 2) and rotate through three
+  // LDS buffers (tile j in buffer j % 3), with one barrier per tile.  The
+  // wavefronts 0-3 run each tile as scores, softmax, accumulate; the
+  // wavefronts 4-7 (the other wavefront on each SIMD) accumulate the
+  // previous tile first, then take this tile's scores and softmax, keeping
+  // its P for the next step.  So while one wavefront of a SIMD computes
+  // exponentials the other one issues MFMAs.  Buffer j % 3 is written at
+  // step j, read at steps j (both halves) and j + 1 (the second half), and
+  // written again only at step j + 3, after the barrier of step j + 2.
+  int n_t[2] = {0, 0};
+  if (all_tiles > 0) n_t[0] = fetch(0, std::integral_constant<int, 0>{});
+  if (all_tiles > 1) n_t[1] = fetch(1, std::integral_constant<int, 1>{});
+  auto tile_step = [&](int j, auto set, auto lag_c, PTile& p_prev) {
+    constexpr int S = decltype(set)::value;
+    constexpr bool lag = decltype(lag_c)::value;
+    const int buf = j % 3;
+    // ---- stage tile j: K as loaded, V converted to f16
+    u16* kdst = sK + buf * (kKT * KP);
+    _Float16* vdst = sV + buf * (kKT * KP);
+#pragma unroll
+    for (int i = 0; i < LPT; ++i) {
+      if (!chunk_live(i)) continue;
+      *reinterpret_cast<uint4*>(kdst + loff[i]) = pk[S][i];
+      if constexpr (VF16) {
+        *reinterpret_cast<uint4*>(vdst + loff[i]) = pv[S][i];
+      } else {  // bf16 V -> f16
+        const uint32_t u[4] = {pv[S][i].x, pv[S][i].y, pv[S][i].z, pv[S][i].w};
+        f16x8 hv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          hv[2 * e] = (_Float16)__uint_as_float(u[e] << 16);
+          hv[2 * e + 1] = (_Float16)__uint_as_float(u[e] & 0xffff0000u);
+        }
+        *reinterpret_cast<f16x8*>(vdst + loff[i]) = hv;
+      }
+    }
+    const int n_tile = n_t[S];
+    lds_barrier();
+    if (j + 2 < all_tiles) n_t[S] = fetch(j + 2, set);
+    if constexpr (!lag) {
+      accumulate(buf, scores(buf, n_tile));
+    } else {
+      if (j > 0) accumulate(buf == 0 ? 2 : buf - 1, p_prev);
+      p_prev = scores(buf, n_tile);
+    }
+  };
+  auto run = [&](auto lag_c) {
+    PTile p_prev;
+    for (int j = 0; j < all_tiles; j += 2) {
+      tile_step(j, std::integral_constant<int, 0>{}, lag_c, p_prev);
+      if (j + 1 < all_tiles) tile_step(j + 1, std::integral_constant<int, 1>{}, lag_c, p_prev);
+    }
+    if constexpr (decltype(lag_c)::value)
+      if (all_tiles > 0) accumulate((all_tiles - 1) % 3, p_prev);
+  };
+  if (__builtin_amdgcn_readfirstlane(wave) >= 4)
+    run(std::true_type{});
+  else
+    run(std::false_type{});
 
   // ---- O = O^T / l: lane (n, g) holds channels 16 dt + 4g + e of query n
   const size_t obase = (size_t)h * a.T * a.U * D;
