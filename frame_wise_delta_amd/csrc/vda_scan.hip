@@ -10,24 +10,29 @@
 // The d_v rows of S evolve independently (row i: s_t = (s_{t-1} * alpha_t) N_t
 // + j_t), so one (head, direction) chain is split over d/32 workgroups of
 // 32 rows each (16 for d = 16); the row blocks of a head are mapped to one
-// XCD so that they share that XCD's L2 copy of N_t.  A workgroup keeps its
-// 32 x d slice of S in LDS in float32 and runs d/16 wavefronts, one per
-// 16-column output tile.
-// Per frame, the VALU forms X = S Diag(alpha) (float32) and splits it into an
-// f16 hi/lo pair in LDS; each wavefront computes its 16 x 16 tile of X N on
-// MFMA as X_hi N + X_lo N with the accumulators starting from its tile of
-// J_t, N and J_t being stored by the prepare kernel as f16 (N in MFMA
-// fragment order, read as rows since N is symmetric; J_t in this kernel's
-// accumulator order).  The comparators' slots hold B_t (the Newton
-// comparator) or B' (SANA-WM) instead of J_t, which the VALU adds into X
-// before the product.  Each workgroup pulls N and its rows of J_t through its
-// CU's vector-memory path once per frame, and that is what bounds a step, so
-// both are kept to 2 bytes per entry (f16).
+// XCD so that they share that XCD's L2 copy of N_t.  A workgroup runs d/16
+// wavefronts, one per 16-column tile of its 32 x d slice of S, and keeps
+// the slice in the wavefronts' float32 accumulators, transposed: the
+// product is taken as S^T <- N X^T (N is symmetric), so that accumulator
+// lane (n, g) of column tile c holds S[n][16c + 4g .. 16c + 4g + 3] of one
+// row tile.  Per frame each wavefront forms its part of X = S Diag(alpha)
+// in registers (alpha is per column, so a lane needs four values), splits
+// it into an f16 hi/lo pair and writes it to LDS row-major; after one
+// barrier every wavefront reads the rows of X as the B operand (eight
+// consecutive columns per lane) and runs X_hi N + X_lo N on MFMA for its
+// column tile, the accumulators starting from J_t.  X is double-buffered
+// in LDS, so one barrier per frame orders both its writes and its reads.
+// N and J_t are stored by the prepare kernel as f16: N in MFMA fragment
+// order (a column tile's k-slices, which by symmetry are the rows the A
+// operand needs), J_t in the accumulator order of the untransposed product,
+// which an MFMA with the identity turns into this one.  The comparators'
+// slots hold B_t (the Newton comparator, added into X before the product)
+// or B' (SANA-WM, added after it) instead of J_t.
 // The chain is bound by the latency of these per-frame operand loads, so
-// frames are prefetched three or four steps ahead into registers, their
-// loads issued part by part between the k-steps of the current step's
-// MFMAs; the barriers wait for LDS traffic only, so the global loads stay in
-// flight across them.
+// frames are prefetched several steps ahead into registers, their loads
+// issued part by part between the k-steps of the current step's MFMAs; the
+// barrier waits for LDS traffic only, so the global loads stay in flight
+// across it.
 //
 // The same kernel also runs the scan at chunk level (method-steps section,
 // step (4): S_out = S_in M_chunk + J_chunk), in two launches:
@@ -54,6 +59,24 @@ namespace vda {
 
 namespace {
 
+// Two 16 x 16 f16 tiles held in accumulator order (lane (n, g): rows
+// 4g .. 4g+3 of column n), one in each half of an f16x8, are transposed
+// into float32 accumulator order exactly by one 16x16x32 MFMA each: the
+// pair as the A operand (tile 0 in k-slots 8g .. 8g+3, tile 1 in
+// 8g+4 .. 8g+7) times the identity placed in the slots of the wanted tile
+// (eye_k32).  It is the same MFMA shape as the products that then
+// accumulate onto the result, so every accumulator a product reads comes
+// from an MFMA of its own shape.
+__device__ __forceinline__ f16x8 eye_k32(int lr, int lg, int half) {
+  f16x8 e8;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) e8[e] = (_Float16)(e / 4 == half && 4 * lg + (e & 3) == lr ? 1.f : 0.f);
+  return e8;
+}
+__device__ __forceinline__ f32x4 transpose_tile(f16x8 pair, f16x8 eye_half) {
+  return mfma_f16(pair, eye_half, f32x4{0, 0, 0, 0});
+}
+
 template <int D>
 struct ScanShape {
   static constexpr int ROWS = D < 32 ? D : 32;          // state rows per workgroup
@@ -62,8 +85,7 @@ struct ScanShape {
   static constexpr int NT = 64 * NW;                    // threads
   static constexpr int KS = D >= 32 ? D / 32 : 1;       // MFMA k-steps (D = 16: one, zero padded)
   static constexpr int XP = D + 8;                      // LDS row pitch of X (halves)
-  static constexpr int NQ = ROWS / 16;                  // float4 X chunks per thread
-  static constexpr int TPR = D / 4;                     // threads per row in the elementwise phase
+  static constexpr int NQ = ROWS / 16;                  // J / B registers per lane (one per row tile)
   static constexpr int LG = D >= 32 ? 4 : D / 8;        // k-chunk groups per fragment-order block
   static constexpr int PD = D >= 128 ? 3 : (D >= 64 ? 4 : 2);  // frames prefetched ahead
 };
@@ -72,8 +94,10 @@ struct ScanShape {
 template <int D>
 struct FrameRegs {
   f16x8 nk[ScanShape<D>::KS];                          // N column tile (k-slices of this lane)
-  f16x4 b[ScanShape<D>::NQ];                           // B row segments (rows xrow + 16 q)
-  float4 al;                                           // alpha segment
+  f16x8 b;                                             // row tile 0 in the low half, 1 in the high half (zero for
+                                                       // d = 16): J_t / B' tiles in untransposed accumulator order,
+                                                       // or B_t row segments
+  float4 al;                                           // alpha of this lane's four columns
 };
 
 }  // namespace
@@ -90,10 +114,10 @@ __global__ __launch_bounds__(ScanShape<D>::NT) void scan_kernel(ScanPair p) {
   constexpr bool POST = MODE != kFrameScanB;
   using SS = ScanShape<D>;
   constexpr int ROWS = SS::ROWS, NQ = SS::NQ, PD = SS::PD;
-  static_assert(NQ == SS::RTS, "one B / J register per 16-row tile");
-  __shared__ __attribute__((aligned(16))) float sS[ROWS * D];
-  __shared__ __attribute__((aligned(16))) _Float16 sXh[ROWS * SS::XP];
-  __shared__ __attribute__((aligned(16))) _Float16 sXl[ROWS * SS::XP];
+  static_assert(NQ == SS::RTS && NQ <= 2, "one half of FrameRegs::b per 16-row tile");
+  // X = S Diag(alpha) as an f16 hi/lo pair, row-major, two buffers
+  __shared__ __attribute__((aligned(16))) _Float16 sXh[2][ROWS * SS::XP];
+  __shared__ __attribute__((aligned(16))) _Float16 sXl[2][ROWS * SS::XP];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, lg = lane >> 4;
@@ -106,9 +130,8 @@ __global__ __launch_bounds__(ScanShape<D>::NT) void scan_kernel(ScanPair p) {
   const ScanArgs& a = p.dir[dir];
   const int h = L / RB;
   const int r0 = ROWS * (L - h * RB);
-  // elementwise phase: thread owns columns xc0..xc0+3 of rows xrow + 16 q
-  const int xrow = tid / SS::TPR, xc0 = 4 * (tid - xrow * SS::TPR);
-  const int ct = wave;  // output column tile
+  const int ct = wave;       // column tile of S this wavefront holds
+  const int xc0 = 16 * ct + 4 * lg;  // this lane's four columns (of row r0 + 16 rt + lr)
 
   const size_t slot_floats = ws_slot_floats(D);
   const float* frames = a.frames + (size_t)h * a.n_eff * slot_floats;
@@ -144,13 +167,15 @@ __global__ __launch_bounds__(ScanShape<D>::NT) void scan_kernel(ScanPair p) {
       }
     }
     if (part == 2) {
+      f16x4 t[2] = {};
 #pragma unroll
       for (int q = 0; q < NQ; ++q) {
         if (form == 1)
-          fr.b[q] = *reinterpret_cast<const f16x4*>(bm + (size_t)(r0 + xrow + 16 * q) * D + xc0);
+          t[q] = *reinterpret_cast<const f16x4*>(bm + (size_t)(r0 + 16 * q + lr) * D + xc0);
         else
-          fr.b[q] = ba[((r0 / 16 + q) * SS::NW + ct) * 64 + lane];
+          t[q] = ba[((r0 / 16 + q) * SS::NW + ct) * 64 + lane];
       }
+      fr.b = __builtin_shufflevector(t[0], t[1], 0, 1, 2, 3, 4, 5, 6, 7);
     }
     if (part == 3)
       fr.al = alpha_row ? *reinterpret_cast<const float4*>(alpha_row + xc0) : make_float4(1.f, 1.f, 1.f, 1.f);
@@ -178,8 +203,10 @@ __global__ __launch_bounds__(ScanShape<D>::NT) void scan_kernel(ScanPair p) {
       }
     }
     if (part == 2) {
+      f16x4 t[2] = {};
 #pragma unroll
-      for (int rt = 0; rt < SS::RTS; ++rt) fr.b[rt] = jf[((r0 / 16 + rt) * SS::NW + ct) * 64 + lane];
+      for (int rt = 0; rt < SS::RTS; ++rt) t[rt] = jf[((r0 / 16 + rt) * SS::NW + ct) * 64 + lane];
+      fr.b = __builtin_shufflevector(t[0], t[1], 0, 1, 2, 3, 4, 5, 6, 7);
     }
     if (part == 3) fr.al = make_float4(1.f, 1.f, 1.f, 1.f);
   };
@@ -188,115 +215,119 @@ __global__ __launch_bounds__(ScanShape<D>::NT) void scan_kernel(ScanPair p) {
     for (int part = 0; part < 4; ++part) load_map_part(fr, c, part);
   };
 
-  // one frame write on the LDS state slice: S <- (S Diag(al) + B) N; a step
-  // with live == false leaves S unchanged (padding at the end of the chain);
-  // with logits the decay is sigmoid(al).  With post, B is added after the
-  // product, S <- S Diag(al) N + B, B in accumulator order: one chunk step
-  // S M_c + J_c (al = 1, fr from load_map) or one SANA-WM frame write.
+  // J_t, B' and J_c come in the untransposed accumulator order; transposed
+  // against this identity they start the accumulators
+  const f16x8 eye[2] = {eye_k32(lr, lg, 0), eye_k32(lr, lg, 1)};
+
+  // The state: st[rt] holds S[r0 + 16 rt + lr][xc0 .. xc0 + 3].
+  f32x4 st[SS::RTS];
+  int xb = 0;  // LDS buffer of X for the next step
+
+  // one frame write: S <- (S Diag(al) + B) N; a step with live == false
+  // leaves S unchanged (padding at the end of the chain); with logits the
+  // decay is sigmoid(al).  With post, B is added after the product,
+  // S <- S Diag(al) N + B, B in untransposed accumulator order: one chunk
+  // step S M_c + J_c (al = 1, fr from load_map), one frame step with J_t, or
+  // one SANA-WM frame write.
   // next(part) issues part `part` of a later frame's loads; it is called
   // after each k-step's MFMAs, so that those loads leave this wavefront
-  // while its MFMAs run instead of in one burst per step (eight wavefronts'
-  // bursts through one CU's vector-memory path otherwise hold up the last
-  // wavefront, and every barrier waits for it).
+  // while its MFMAs run instead of in one burst per step.
   auto step = [&](const FrameRegs<D>& fr, float* rec, bool live, bool logits, bool post, auto&& next) {
+    float4 al = fr.al;
+    if (logits) al = make_float4(sigmoid_gate(al.x), sigmoid_gate(al.y), sigmoid_gate(al.z), sigmoid_gate(al.w));
+    _Float16* xh_buf = sXh[xb];
+    _Float16* xl_buf = sXl[xb];
+    f16x4 hi[SS::RTS], lo[SS::RTS];
 #pragma unroll
-    for (int q = 0; q < NQ; ++q) {
-      const int row = xrow + 16 * q;
-      const float4 s = *reinterpret_cast<const float4*>(sS + row * D + xc0);
-      float4 al = fr.al;
-      if (logits) al = make_float4(sigmoid_gate(al.x), sigmoid_gate(al.y), sigmoid_gate(al.z), sigmoid_gate(al.w));
-      const f16x4 bb = fr.b[q];
-      float x[4] = {s.x * al.x, s.y * al.y, s.z * al.z, s.w * al.w};
+    for (int rt = 0; rt < SS::RTS; ++rt) {
+      float x[4] = {st[rt][0] * al.x, st[rt][1] * al.y, st[rt][2] * al.z, st[rt][3] * al.w};
       if (!post) {
-        x[0] = fmaf(s.x, al.x, (float)bb[0]);
-        x[1] = fmaf(s.y, al.y, (float)bb[1]);
-        x[2] = fmaf(s.z, al.z, (float)bb[2]);
-        x[3] = fmaf(s.w, al.w, (float)bb[3]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] += (float)fr.b[4 * rt + e];
       }
-      f16x4 hi, lo;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        hi[e] = (_Float16)x[e];
-        lo[e] = (_Float16)(x[e] - (float)hi[e]);
+        hi[rt][e] = (_Float16)x[e];
+        lo[rt][e] = (_Float16)(x[e] - (float)hi[rt][e]);
       }
-      *reinterpret_cast<f16x4*>(sXh + row * SS::XP + xc0) = hi;
-      *reinterpret_cast<f16x4*>(sXl + row * SS::XP + xc0) = lo;
+      *reinterpret_cast<f16x4*>(xh_buf + (16 * rt + lr) * SS::XP + xc0) = hi[rt];
+      *reinterpret_cast<f16x4*>(xl_buf + (16 * rt + lr) * SS::XP + xc0) = lo[rt];
     }
     lds_barrier();
     f32x4 acc[SS::RTS];
 #pragma unroll
     for (int rt = 0; rt < SS::RTS; ++rt) {
       if (post) {
-        acc[rt] = f32x4{(float)fr.b[rt][0], (float)fr.b[rt][1], (float)fr.b[rt][2], (float)fr.b[rt][3]};
+        acc[rt] = transpose_tile(fr.b, eye[rt]);
         if constexpr (MODE == kSanaScan) {  // the identity part: X (I - A') = X + X (-A')
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int at = (16 * rt + 4 * lg + e) * SS::XP + 16 * ct + lr;
-            acc[rt][e] += (float)sXh[at] + (float)sXl[at];
-          }
+          for (int e = 0; e < 4; ++e) acc[rt][e] += (float)hi[rt][e] + (float)lo[rt][e];
         }
       } else {
         acc[rt] = f32x4{0, 0, 0, 0};
       }
     }
+    // every X fragment of the step is read before the first product, so
+    // that the LDS latency is paid once per step, not once per k-step
+    f16x8 xh[SS::KS][SS::RTS], xl[SS::KS][SS::RTS];
 #pragma unroll
     for (int kk = 0; kk < SS::KS; ++kk) {
       const int k0 = 32 * kk + 8 * lg;
 #pragma unroll
       for (int rt = 0; rt < SS::RTS; ++rt) {
-        f16x8 xh, xl;
         if (k0 < D) {
-          xh = *reinterpret_cast<const f16x8*>(sXh + (16 * rt + lr) * SS::XP + k0);
-          xl = *reinterpret_cast<const f16x8*>(sXl + (16 * rt + lr) * SS::XP + k0);
+          xh[kk][rt] = *reinterpret_cast<const f16x8*>(xh_buf + (16 * rt + lr) * SS::XP + k0);
+          xl[kk][rt] = *reinterpret_cast<const f16x8*>(xl_buf + (16 * rt + lr) * SS::XP + k0);
         } else {
 #pragma unroll
-          for (int e = 0; e < 8; ++e) xh[e] = xl[e] = (_Float16)0.f;
+          for (int e = 0; e < 8; ++e) xh[kk][rt][e] = xl[kk][rt][e] = (_Float16)0.f;
         }
-        acc[rt] = mfma_f16(xh, fr.nk[kk], acc[rt]);
-        acc[rt] = mfma_f16(xl, fr.nk[kk], acc[rt]);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the products
+#pragma unroll
+    for (int kk = 0; kk < SS::KS; ++kk) {
+#pragma unroll
+      for (int rt = 0; rt < SS::RTS; ++rt) {
+        acc[rt] = mfma_f16(fr.nk[kk], xh[kk][rt], acc[rt]);
+        acc[rt] = mfma_f16(fr.nk[kk], xl[kk][rt], acc[rt]);
       }
       if (kk < 4) next(kk);
     }
 #pragma unroll
     for (int part = SS::KS; part < 4; ++part) next(part);
+    xb ^= 1;
 #pragma unroll
     for (int rt = 0; rt < SS::RTS; ++rt) {
-      if (live) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) sS[(16 * rt + 4 * lg + e) * D + 16 * ct + lr] = acc[rt][e];
-      }
+      if (live) st[rt] = acc[rt];
       if (rec) {
         bool fin = true;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          rec[(size_t)(r0 + 16 * rt + 4 * lg + e) * D + 16 * ct + lr] = acc[rt][e];
-          fin = fin && __builtin_isfinite(acc[rt][e]);
-        }
+        for (int e = 0; e < 4; ++e) fin = fin && __builtin_isfinite(acc[rt][e]);
+        *reinterpret_cast<f32x4*>(rec + (size_t)(r0 + 16 * rt + lr) * D + xc0) = acc[rt];
         if (!fin) atomicOr(a.status, VDA_DEV_NONFINITE);
       }
     }
-    lds_barrier();
   };
 
   // ---- initial state
-  if (a.s_init) {
-    const float* si = a.s_init + (size_t)h * D * D + (size_t)r0 * D;
-    for (int i = tid; i < ROWS * D; i += SS::NT) sS[i] = si[i];
-  } else {
-    for (int i = tid; i < ROWS * D; i += SS::NT) sS[i] = 0.f;
+#pragma unroll
+  for (int rt = 0; rt < SS::RTS; ++rt) {
+    if (a.s_init)
+      st[rt] = *reinterpret_cast<const f32x4*>(a.s_init + (size_t)h * D * D + (size_t)(r0 + 16 * rt + lr) * D + xc0);
+    else
+      st[rt] = f32x4{0, 0, 0, 0};
   }
-  lds_barrier();
   if (!a.s_init && a.use_text) {
     FrameRegs<D> fr;
     load(fr, a.n, nullptr);
     step(fr, nullptr, true, false, form != 1, [](int) {});  // S^T = 0 N_T + J_T (or (0 + B_T) N_T, or 0 T_T + B'_T)
   }
-  for (int i = tid; i < ROWS * D; i += SS::NT) {
-    const float s0 = a.scale * sS[i];
-    sS[i] = s0;
-    states_h[(size_t)r0 * D + i] = s0;
+#pragma unroll
+  for (int rt = 0; rt < SS::RTS; ++rt) {
+    st[rt] *= a.scale;
+    *reinterpret_cast<f32x4*>(states_h + (size_t)(r0 + 16 * rt + lr) * D + xc0) = st[rt];
   }
-  lds_barrier();
 
   if constexpr (MODE == kChunkScan) {
     // ---- C chunk steps S <- S M_c + J_c, maps prefetched PD chunks ahead;
@@ -417,10 +448,21 @@ __global__ __launch_bounds__(ComposeShape<D>::NTH, 1) void compose_kernel(ScanPa
 
   f16x8 nreg[CS::CPT];
   float areg = 0.f;
-  f16x4 breg[NTW][MT];
-  f16x4 eye4;  // the 16 x 16 identity as a B operand: lane (n, g) holds rows 4g .. 4g+3 of column n
+  // per row tile nt, column tiles 2c and 2c + 1 in the two halves of
+  // breg[nt][c] (the high half zero when MT is odd)
+  constexpr int MP = (MT + 1) / 2;
+  f16x8 breg[NTW][MP];
 #pragma unroll
-  for (int e = 0; e < 4; ++e) eye4[e] = (_Float16)(4 * lg + e == lr ? 1.f : 0.f);
+  for (int nt = 0; nt < NTW; ++nt)
+#pragma unroll
+    for (int c = 0; c < MP; ++c)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) breg[nt][c][e] = (_Float16)0.f;
+  const f16x8 eye[2] = {eye_k32(lr, lg, 0), eye_k32(lr, lg, 1)};
+  auto put_b = [&](int nt, int mt, f16x4 v) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) breg[nt][mt / 2][4 * (mt & 1) + e] = v[e];
+  };
   auto fetch = [&](int i) {
     const float* base = frames + (size_t)slot_of(i) * slot_floats;
     const f16x8* src = reinterpret_cast<const f16x8*>(base);
@@ -436,7 +478,7 @@ __global__ __launch_bounds__(ComposeShape<D>::NTH, 1) void compose_kernel(ScanPa
       for (int nt = 0; nt < NTW; ++nt)
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
-          breg[nt][mt] = *reinterpret_cast<const f16x4*>(bm + (size_t)(n0 + 16 * nt + lr) * D + 16 * mt + 4 * lg);
+          put_b(nt, mt, *reinterpret_cast<const f16x4*>(bm + (size_t)(n0 + 16 * nt + lr) * D + 16 * mt + 4 * lg));
     } else if (jpart) {
       // J_t in the accumulator order at byte 2 d^2: this lane's f16x4 of
       // tile (R, mt), i.e. J[16R + 4 lg + e][16 mt + lr], loaded whole; it is
@@ -446,7 +488,7 @@ __global__ __launch_bounds__(ComposeShape<D>::NTH, 1) void compose_kernel(ScanPa
 #pragma unroll
       for (int nt = 0; nt < NTW; ++nt)
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) breg[nt][mt] = jm[(size_t)(((n0 + 16 * nt) / 16) * MT + mt) * 64 + lane];
+        for (int mt = 0; mt < MT; ++mt) put_b(nt, mt, jm[(size_t)(((n0 + 16 * nt) / 16) * MT + mt) * 64 + lane]);
     }
   };
   auto stage = [&](int buf) {
@@ -491,7 +533,7 @@ __global__ __launch_bounds__(ComposeShape<D>::NTH, 1) void compose_kernel(ScanPa
             for (int nt = 0; nt < NTW; ++nt)
 #pragma unroll
               for (int e = 0; e < 4; ++e) {
-                const float x = (JP && BFORM) ? fmaf(acc[mt][nt][e], alv[e], (float)breg[nt][mt][e])
+                const float x = (JP && BFORM) ? fmaf(acc[mt][nt][e], alv[e], (float)breg[nt][mt / 2][4 * (mt & 1) + e])
                                               : acc[mt][nt][e] * alv[e];
                 const _Float16 hi = (_Float16)x;
                 xh[nt][kk][4 * half + e] = hi;
@@ -512,7 +554,7 @@ __global__ __launch_bounds__(ComposeShape<D>::NTH, 1) void compose_kernel(ScanPa
 #pragma unroll
         for (int nt = 0; nt < NTW; ++nt) {
           if constexpr (JP && !BFORM)
-            acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x16f16(breg[nt][mt], eye4, f32x4{0, 0, 0, 0}, 0, 0, 0);
+            acc[mt][nt] = transpose_tile(breg[nt][mt / 2], eye[mt & 1]);
           else
             acc[mt][nt] = f32x4{0, 0, 0, 0};
         }
