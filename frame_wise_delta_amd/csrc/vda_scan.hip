@@ -23,16 +23,17 @@
 // column tile, the accumulators starting from J_t.  X is double-buffered
 // in LDS, so one barrier per frame orders both its writes and its reads.
 // N and J_t are stored by the prepare kernel as f16: N in MFMA fragment
-// order (a column tile's k-slices, which by symmetry are the rows the A
-// operand needs), J_t in the accumulator order of the untransposed product,
-// which an MFMA with the identity turns into this one.  The comparators'
+// order (16-byte pieces of eight consecutive entries of a row, by 16-row
+// tile and k-slice: what the A operand of N X^T takes directly), J_t in the
+// accumulator order of the untransposed product, which an MFMA with the
+// identity turns into this one.  The comparators'
 // slots hold B_t (the Newton comparator, added into X before the product)
 // or B' (SANA-WM, added after it) instead of J_t.
-// The chain is bound by the latency of these per-frame operand loads, so
-// frames are prefetched several steps ahead into registers, their loads
-// issued part by part between the k-steps of the current step's MFMAs; the
-// barrier waits for LDS traffic only, so the global loads stay in flight
-// across it.
+// Frames are prefetched several steps ahead into registers, their loads
+// issued part by part between the k-steps of the current step's MFMAs, and
+// the barrier waits for LDS traffic only, so the global loads stay in
+// flight across it; a step is then bound by its own chain (X through LDS,
+// the barrier, the products of the two wavefronts sharing each SIMD).
 //
 // The same kernel also runs the scan at chunk level (method-steps section,
 // step (4): S_out = S_in M_chunk + J_chunk), in two launches:
@@ -47,7 +48,8 @@
 //    accumulator order: the f16x4 at index (R * d/16 + ct) * 64 + l holds
 //    J_c[16R + 4(l/16) + e][16ct + l%16].
 //  * chunk scan: C steps of S <- S M_c + J_c, the product on the same MFMA
-//    path as a frame step (S as an f16 hi/lo pair, M_c as the B operand) with
+//    path as a frame step (S^T <- M_c^T X^T: M_c's stored columns are the
+//    rows of M_c^T the A operand needs, X = S as an f16 hi/lo pair) with
 //    the accumulators starting from J_c; the state is recorded after every
 //    chunk, which is where the windowed readout needs it.
 #include <type_traits>
