@@ -460,7 +460,7 @@ __global__ __launch_bounds__(kThreads, 2) void frame_kernel(PrepArgs args) {
   constexpr int kTile = D * kRound;       // halves per LDS token tile
   constexpr int kTP = 20;                 // LDS pitch (floats) of a staged 16 x 16 tile
   constexpr int kStageT = RT * 16 * kTP;  // floats per sweep buffer (column p of T)
-  constexpr int kSweepB = 2 * kStageT * 4 + RT * 64 * 16;  // two column buffers, RT operand tiles
+  constexpr int kSweepB = 2 * kStageT * 4 + 2 * RT * 64 * 16;  // two column buffers, two sets of RT operand tiles
   constexpr int kJB = (RT < 4 ? RT : 4) * RT * 64 * 16;     // B operand tiles of four row tiles
   constexpr int kStageB = kSweepB > kJB ? kSweepB : kJB;
   constexpr int kBytes = 3 * kTile * 2 > kStageB ? 3 * kTile * 2 : kStageB;
@@ -602,11 +602,13 @@ __global__ __launch_bounds__(kThreads, 2) void frame_kernel(PrepArgs args) {
   //      tile is inverted.  The step's left factors -T[j][p] Ei^T (j != p) are
   //      formed once per workgroup, spread over the wavefronts, and staged as
   //      ready f16 hi/lo A operands; after a second barrier every wavefront
-  //      updates its columns from them, the owner of column p + 1 that
-  //      column first, after which it inverts the next pivot and stages the
-  //      next column, so that the inversion overlaps the other updates.
-  float* raw = reinterpret_cast<float*>(smem);                // 2 x RT float32 tiles
-  f16x8* packs = reinterpret_cast<f16x8*>(raw + 2 * kStageT);  // RT operand tiles, 64 lanes each
+  //      updates its columns from them.  The owner of column p + 1 updates
+  //      the next pivot tile first and the rest of that column while it
+  //      inverts the pivot, stages the column, and leaves its other column
+  //      to the next step (the left factors are double-buffered for it), so
+  //      that the next step's barrier waits for the inversion alone.
+  float* raw = reinterpret_cast<float*>(smem);                     // 2 x RT float32 tiles
+  f16x8* packs_base = reinterpret_cast<f16x8*>(raw + 2 * kStageT);  // 2 x RT operand tiles, 64 lanes each
   const f16x8 eye_hi = eye_f16(lr, lg, 0, 1.f), eye_lo = eye_f16(lr, lg, 1, 1.f);
   const f16x8 neye = eye_f16(lr, lg, -1, -1.f);  // [-I | -I]
   auto put_tile = [&](float* buf, int slot, f32x4 v) {  // tile -> row-major 16 x 16 at pitch kTP
@@ -624,6 +626,27 @@ __global__ __launch_bounds__(kThreads, 2) void frame_kernel(PrepArgs args) {
 #pragma unroll
     for (int j = 0; j < RT; ++j) put_tile(buf, j, Tt[mq][j]);  // slot q holds Ei^T
   };
+  // T[j][i] += L_j T[p][i] for the own columns in `cols` (bit m: column
+  // wave + 4m) and every row tile j != pp, then T[pp][i] = -Ei^T T[pp][i],
+  // with the left factors L_j of step pp in pk
+  auto update_cols = [&](int pp, const f16x8* pk, f16x8 neit, int cols) {
+    RightF16 tpi[NC];
+#pragma unroll
+    for (int m = 0; m < NC; ++m)
+      if ((cols >> m) & 1) tpi[m] = right_f16(Tt[m][pp]);
+#pragma unroll
+    for (int j = 0; j < RT; ++j) {
+      if (j == pp) continue;
+      const f16x8 l = pk[j * 64 + lane];
+#pragma unroll
+      for (int m = 0; m < NC; ++m)
+        if ((cols >> m) & 1) Tt[m][j] = mul_f16(l, tpi[m], Tt[m][j]);
+    }
+#pragma unroll
+    for (int m = 0; m < NC; ++m)
+      if ((cols >> m) & 1) Tt[m][pp] = mul_f16(neit, tpi[m], f32x4{0, 0, 0, 0});
+  };
+  f16x8 neit_keep;  // -Ei^T of the step whose update the pivot owner left over
   if (wave == 0) pivot_and_stage(0, 0);
 #pragma unroll
   for (int p = 0; p < RT; ++p) {
@@ -631,6 +654,7 @@ __global__ __launch_bounds__(kThreads, 2) void frame_kernel(PrepArgs args) {
     const int q = p + 1, owner1 = q % 4, mq = q / 4;
     lds_barrier();
     const float* buf = raw + (p & 1) * kStageT;
+    f16x8* packs = packs_base + (p & 1) * (RT * 64);
     // left factors: -T[j][p] Ei^T = -(Ei (T[j][p])^T)^T for j = wave (mod 4);
     // the accumulator registers of Ei (T[j][p])^T are the A operand
     {
@@ -650,33 +674,32 @@ __global__ __launch_bounds__(kThreads, 2) void frame_kernel(PrepArgs args) {
       for (int j = 0; j < RT; ++j)
         if (j != p) Tt[mo][j] = mfma_f16(packs[j * 64 + lane], neye, f32x4{0, 0, 0, 0});
     }
-    auto update = [&](int cols) {  // own columns i = wave + 4m != p, set bit m
-      RightF16 tpi[NC];
+    // the owner of column p inverted this step's pivot at step p - 1 and
+    // left its other columns' update of that step until now
+    if (p > 0 && wave == owner) {
+      int late = 0;
 #pragma unroll
       for (int m = 0; m < NC; ++m)
-        if ((cols >> m) & 1) tpi[m] = right_f16(Tt[m][p]);
-#pragma unroll
-      for (int j = 0; j < RT; ++j) {
-        if (j == p) continue;
-        const f16x8 l = packs[j * 64 + lane];
-#pragma unroll
-        for (int m = 0; m < NC; ++m)
-          if ((cols >> m) & 1) Tt[m][j] = mul_f16(l, tpi[m], Tt[m][j]);
-      }
-#pragma unroll
-      for (int m = 0; m < NC; ++m)
-        if ((cols >> m) & 1) Tt[m][p] = mul_f16(neit_l, tpi[m], f32x4{0, 0, 0, 0});  // -Ei^T T[p][i]
-    };
+        if (owns(m) && wave + 4 * m != p - 1 && wave + 4 * m != p) late |= 1 << m;
+      if (late) update_cols(p - 1, packs_base + ((p - 1) & 1) * (RT * 64), neit_keep, late);
+    }
     int mine = 0;  // own columns other than p
 #pragma unroll
     for (int m = 0; m < NC; ++m)
       if (owns(m) && wave + 4 * m != p) mine |= 1 << m;
-    if (q < RT && wave == owner1) {  // the next pivot's column first
-      update(1 << mq);
+    if (q < RT && wave == owner1) {
+      // column q: the pivot tile first, then the rest of the column, whose
+      // products run while the pivot is inverted; the column is then staged
+      const RightF16 tq = right_f16(Tt[mq][p]);
+      Tt[mq][q] = mul_f16(packs[q * 64 + lane], tq, Tt[mq][q]);
+#pragma unroll
+      for (int j = 0; j < RT; ++j)
+        if (j != p && j != q) Tt[mq][j] = mul_f16(packs[j * 64 + lane], tq, Tt[mq][j]);
+      Tt[mq][p] = mul_f16(neit_l, tq, f32x4{0, 0, 0, 0});
       pivot_and_stage(q, mq);
-      update(mine & ~(1 << mq));
+      neit_keep = neit_l;  // the other columns: next step
     } else {
-      update(mine);
+      update_cols(p, packs, neit_l, mine);
     }
   }
 
