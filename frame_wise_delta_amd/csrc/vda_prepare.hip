@@ -446,8 +446,9 @@ __device__ __forceinline__ f16x8 to_left_f16(f32x4 z, f16x8 eye_hi, f16x8 eye_lo
 // the left factors, and updates its own columns, the next pivot's column
 // first.
 //
-// Injection.  J = B N as a product: the B tiles of four row tiles at a time
-// are staged through LDS by the owners of their columns, and each wavefront
+// Injection.  J = B N as a product: the B tiles of every row tile are
+// staged through LDS at once by the owners of their columns (4 d^2 bytes:
+// 64 KB at d = 128, where two workgroups per CU still fit), and each wavefront
 // forms its columns of J from them and its own columns of N.
 //
 // All products of the inverse and of J use f16 hi/lo pairs (2^-22).  A pivot
@@ -461,7 +462,7 @@ __global__ __launch_bounds__(kThreads, 2) void frame_kernel(PrepArgs args) {
   constexpr int kTP = 20;                 // LDS pitch (floats) of a staged 16 x 16 tile
   constexpr int kStageT = RT * 16 * kTP;  // floats per sweep buffer (column p of T)
   constexpr int kSweepB = 2 * kStageT * 4 + 2 * RT * 64 * 16;  // two column buffers, two sets of RT operand tiles
-  constexpr int kJB = (RT < 4 ? RT : 4) * RT * 64 * 16;     // B operand tiles of four row tiles
+  constexpr int kJB = RT * RT * 64 * 16;                     // B operand tiles of every row tile
   constexpr int kStageB = kSweepB > kJB ? kSweepB : kJB;
   constexpr int kBytes = 3 * kTile * 2 > kStageB ? 3 * kTile * 2 : kStageB;
   __shared__ __attribute__((aligned(16))) char smem[kBytes];
@@ -723,44 +724,42 @@ __global__ __launch_bounds__(kThreads, 2) void frame_kernel(PrepArgs args) {
     }
   }
 
-  // ---- J = B N (f16, the scan's accumulator order: the f16x4 at
-  //      (r RT + i) 64 + lane holds tile (r, i)), four row tiles at a time:
-  //      the owners of the columns k stage the tiles B[r][k] of those rows as
-  //      ready A operands, then every wavefront forms
+  // ---- J = B N (f16, the untransposed accumulator order: the f16x4 at
+  //      (r RT + i) 64 + lane holds tile (r, i)), every row tile in one
+  //      round: the owners of the columns k stage the tiles B[r][k] as ready
+  //      A operands, then every wavefront forms
   //      J[r][i] = sum_k B[r][k] N[k][i] for its columns i (N[k][i] is its own
   //      tile T[k][i]).
   f16x8* bpk = reinterpret_cast<f16x8*>(smem);
-#pragma unroll
-  for (int r0 = 0; r0 < RT; r0 += 4) {
-    constexpr int kRows = RT < 4 ? RT : 4;
+  {
     lds_barrier();  // the previous readers of this memory are done
 #pragma unroll
     for (int m = 0; m < NC; ++m)
       if (owns(m)) {
 #pragma unroll
-        for (int rr = 0; rr < kRows; ++rr)
-          bpk[(rr * RT + wave + 4 * m) * 64 + lane] = to_left_f16(Xt[m][r0 + rr], eye_hi, eye_lo);
+        for (int rr = 0; rr < RT; ++rr)
+          bpk[(rr * RT + wave + 4 * m) * 64 + lane] = to_left_f16(Xt[m][rr], eye_hi, eye_lo);
       }
     lds_barrier();
 #pragma unroll
     for (int m = 0; m < NC; ++m) {
       const int i = wave + 4 * m;
       if (!owns(m)) continue;
-      f32x4 acc[kRows];
+      f32x4 acc[RT];
 #pragma unroll
-      for (int rr = 0; rr < kRows; ++rr) acc[rr] = f32x4{0, 0, 0, 0};
+      for (int rr = 0; rr < RT; ++rr) acc[rr] = f32x4{0, 0, 0, 0};
 #pragma unroll
       for (int k = 0; k < RT; ++k) {
         const RightF16 nki = right_f16(Tt[m][k]);
 #pragma unroll
-        for (int rr = 0; rr < kRows; ++rr) acc[rr] = mul_f16(bpk[(rr * RT + k) * 64 + lane], nki, acc[rr]);
+        for (int rr = 0; rr < RT; ++rr) acc[rr] = mul_f16(bpk[(rr * RT + k) * 64 + lane], nki, acc[rr]);
       }
 #pragma unroll
-      for (int rr = 0; rr < kRows; ++rr) {
+      for (int rr = 0; rr < RT; ++rr) {
 #pragma unroll
         for (int e = 0; e < 4; ++e)
           if (!__builtin_isfinite(acc[rr][e])) bad |= VDA_DEV_NONFINITE;
-        jf[((r0 + rr) * RT + i) * 64 + lane] = __builtin_convertvector(acc[rr], f16x4);
+        jf[(rr * RT + i) * 64 + lane] = __builtin_convertvector(acc[rr], f16x4);
       }
     }
   }
