@@ -469,18 +469,22 @@ def main():
         torch.cuda.synchronize()
         cold.append(e0.elapsed_time(e1))
     del flush
-    # the read bandwidth of a plain streaming kernel on this device (2 GiB, 2048 workgroups)
-    src = torch.ones(2 * 1024 * 1024 * 1024 // 4, dtype=torch.float32, device="cuda")
-    sink = torch.empty(2048, dtype=torch.int32, device="cuda")
-    vda.vda_stream_read(src, sink, 2048)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(main_s)
-    for _ in range(5):
-        vda.vda_stream_read(src, sink, 2048)
-    e1.record(main_s)
-    torch.cuda.synchronize()
-    stream_gbs = 5 * src.numel() * 4 / (e0.elapsed_time(e1) / 1e3) / 1e9
-    del src, sink
+    # the read bandwidth of a plain streaming kernel on this device: 4 GiB,
+    # the best of four grid sizes (2 to 128 workgroups of 256 threads per CU)
+    src = torch.ones(4 * 1024 * 1024 * 1024 // 4, dtype=torch.float32, device="cuda")
+    stream_gbs = 0.0
+    for blocks in (512, 2048, 8192, 32768):
+        sink = torch.empty(blocks, dtype=torch.int32, device="cuda")
+        vda.vda_stream_read(src, sink, blocks)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(main_s)
+        for _ in range(5):
+            vda.vda_stream_read(src, sink, blocks)
+        e1.record(main_s)
+        torch.cuda.synchronize()
+        stream_gbs = max(stream_gbs, 5 * src.numel() * 4 / (e0.elapsed_time(e1) / 1e3) / 1e9)
+        del sink
+    del src
     print(f"[bench] cold steps median {np.median(cold):.3f} ms; stream read {stream_gbs:.0f} GB/s", file=sys.stderr,
           flush=True)
 
