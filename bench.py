@@ -14,8 +14,8 @@ the stream it runs on, for the per-call times and the roofline of the
 dominant HBM-bound kernel (the events add ~30 us per step, so that pass is
 not the step time); a third pass times each step with the caches flushed
 first (a 512 MiB buffer written between steps, outside the events); and a
-plain streaming read of a 2 GiB buffer gives the read bandwidth the device
-reaches without any arithmetic.  Prints one JSON line: latent frames/s,
+plain streaming read of a 4 GiB buffer (the best of four grid sizes) gives
+the read bandwidth the device reaches without any arithmetic.  Prints one JSON line: latent frames/s,
 algorithmic TFLOP/s, the roofline entry, and the float64 oracle timed on
 this host's cores.
 
