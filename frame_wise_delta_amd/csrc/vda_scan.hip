@@ -17,7 +17,8 @@
 // lane (n, g) of column tile c holds S[n][16c + 4g .. 16c + 4g + 3] of one
 // row tile.  Per frame each wavefront forms its part of X = S Diag(alpha)
 // in registers (alpha is per column, so a lane needs four values), splits
-// it into an f16 hi/lo pair and writes it to LDS row-major; after one
+// it into an f16 hi/lo pair and writes it to LDS (row-major, 16-byte pieces
+// swizzled by row so that the operand reads are free of bank conflicts); after one
 // barrier every wavefront reads the rows of X as the B operand (eight
 // consecutive columns per lane) and runs X_hi N + X_lo N on MFMA for its
 // column tile, the accumulators starting from J_t.  X is double-buffered
@@ -86,11 +87,21 @@ struct ScanShape {
   static constexpr int NW = D / 16;                     // wavefronts = 16-column tiles
   static constexpr int NT = 64 * NW;                    // threads
   static constexpr int KS = D >= 32 ? D / 32 : 1;       // MFMA k-steps (D = 16: one, zero padded)
-  static constexpr int XP = D + 8;                      // LDS row pitch of X (halves)
+  static constexpr int XP = D;                          // LDS row pitch of X (halves), see x_off
   static constexpr int NQ = ROWS / 16;                  // J / B registers per lane (one per row tile)
   static constexpr int LG = D >= 32 ? 4 : D / 8;        // k-chunk groups per fragment-order block
   static constexpr int PD = D >= 128 ? 3 : (D >= 64 ? 4 : 2);  // frames prefetched ahead
 };
+
+// Offset (halves) of X[row][col] in an LDS buffer of X: unpadded rows whose
+// 16-byte pieces (eight columns) are XOR-swizzled by the row.  A step's
+// 16-byte operand reads (rows 16 rt + 0..15, one piece per lane) then fall
+// on distinct banks, and its 8-byte writes (four columns of one row per
+// lane) need two passes per sixteen lanes, the least any layout allows.
+template <int D>
+__device__ __forceinline__ int x_off(int row, int col) {
+  return row * D + (((col >> 3) ^ (row & (D / 8 - 1))) << 3) + (col & 7);
+}
 
 // Operands of one frame held by one thread.
 template <int D>
@@ -252,8 +263,8 @@ __global__ __launch_bounds__(ScanShape<D>::NT) void scan_kernel(ScanPair p) {
         hi[rt][e] = (_Float16)x[e];
         lo[rt][e] = (_Float16)(x[e] - (float)hi[rt][e]);
       }
-      *reinterpret_cast<f16x4*>(xh_buf + (16 * rt + lr) * SS::XP + xc0) = hi[rt];
-      *reinterpret_cast<f16x4*>(xl_buf + (16 * rt + lr) * SS::XP + xc0) = lo[rt];
+      *reinterpret_cast<f16x4*>(xh_buf + x_off<D>(16 * rt + lr, xc0)) = hi[rt];
+      *reinterpret_cast<f16x4*>(xl_buf + x_off<D>(16 * rt + lr, xc0)) = lo[rt];
     }
     lds_barrier();
     f32x4 acc[SS::RTS];
@@ -278,8 +289,8 @@ __global__ __launch_bounds__(ScanShape<D>::NT) void scan_kernel(ScanPair p) {
 #pragma unroll
       for (int rt = 0; rt < SS::RTS; ++rt) {
         if (k0 < D) {
-          xh[kk][rt] = *reinterpret_cast<const f16x8*>(xh_buf + (16 * rt + lr) * SS::XP + k0);
-          xl[kk][rt] = *reinterpret_cast<const f16x8*>(xl_buf + (16 * rt + lr) * SS::XP + k0);
+          xh[kk][rt] = *reinterpret_cast<const f16x8*>(xh_buf + x_off<D>(16 * rt + lr, k0));
+          xl[kk][rt] = *reinterpret_cast<const f16x8*>(xl_buf + x_off<D>(16 * rt + lr, k0));
         } else {
 #pragma unroll
           for (int e = 0; e < 8; ++e) xh[kk][rt][e] = xl[kk][rt][e] = (_Float16)0.f;
