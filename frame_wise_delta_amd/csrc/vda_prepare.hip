@@ -30,8 +30,11 @@ namespace {
 constexpr int kRound = 64;  // tokens per LDS round (two MFMA k-steps of 32)
 
 // Offset (in halves) of the 16-byte group `grp` (8 tokens) of LDS row `row`.
+// The swizzle spreads both access patterns over distinct banks: the
+// transposing writes (eight lanes per pass, rows 8 apart, one group) and the
+// operand reads (32 lanes per pass, 16 consecutive rows, two groups).
 __device__ __forceinline__ int tile_off(int row, int grp) {
-  const int swz = (row & 7) ^ ((row >> 3) & 7);
+  const int swz = ((row >> 1) ^ (row >> 3)) & 7;
   return row * kRound + ((grp ^ swz) << 3);
 }
 
